@@ -1,0 +1,21 @@
+"""MI355X-native sparse-embedding + dot-interaction core of a DLRM-style recommender.
+
+The compute lives in ``libembcore.so`` (HIP kernels for gfx950 behind the C ABI in
+``include/embcore.h``); ``embcore`` is its Python binding and ``synth`` makes seeded
+synthetic inputs shaped like the workloads of the page "DLRM For PyTorch".
+"""
+from .embcore import (  # noqa: F401
+    Bags,
+    EmbcoreError,
+    Tables,
+    alloc_workspace,
+    dot_interact_bwd,
+    dot_interact_fwd,
+    el_last_error,
+    el_validate_bags,
+    el_version,
+    emb_bag_fwd,
+    emb_grad_reduce_update,
+    emb_grad_sort,
+    emb_grad_workspace_bytes,
+)

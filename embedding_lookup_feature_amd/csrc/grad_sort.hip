@@ -1,0 +1,317 @@
+// grad_sort.hip -- keys of the embedding-gradient lookups, stable LSD radix sort,
+// run-length segments, and the exclusive scan they use (gfx950).
+//
+// Every lookup k of bag g = t*B + b contributes demb[b][t] to row row_offset[t] + idx[k]
+// of the joint table (plain SGD, page "DLRM For PyTorch", §Command-line options --lr).
+// Sorting the (row, bag) pairs by row puts all contributions to one row next to each
+// other, so that the reduction needs no atomics.
+//
+// Radix sort: 8-bit digits, least significant first, as many passes as the largest row
+// number needs.  One pass = tile histogram -> exclusive scan of the digit-major
+// histogram -> stable scatter.  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes,
+// each wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same
+// digit are found with 8 ballots; the lowest of them adds the group's size to its
+// wavefront's private LDS counter, so every LDS counter has one writer per step and no
+// atomic is needed.  Ranks are taken in key order (wave, step, lane), which makes every
+// pass stable and the whole sort deterministic.
+#include "el_internal.hpp"
+
+namespace el {
+namespace {
+
+__device__ inline uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+// Lanes of this wavefront whose (valid) digit equals this lane's digit.
+__device__ inline uint64_t match_digit(uint32_t d, bool valid) {
+  uint64_t m = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < kRadixBits; ++bit) {
+    const bool x = (d >> bit) & 1u;
+    const uint64_t bb = __ballot(x);
+    m &= x ? bb : ~bb;
+  }
+  return m;
+}
+
+// key = global row of the joint table, val = bag id; one thread per bag.
+__global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ row_off,
+                                                    const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ off, int32_t B,
+                                                    int32_t nbags, uint32_t hash,
+                                                    uint32_t* __restrict__ keys,
+                                                    uint32_t* __restrict__ vals) {
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= nbags) return;
+  const int t = g / B;
+  const int64_t base = row_off[t];
+  const int32_t n = hash ? static_cast<int32_t>(row_off[t + 1] - base) : 1;
+  const int s = ld_stream(off + g), e = ld_stream(off + g + 1);
+  for (int k = s; k < e; ++k) {
+    int32_t r = ld_stream(idx + k);
+    if (hash) r = floor_mod(r, n);
+    keys[k] = static_cast<uint32_t>(base + r);
+    vals[k] = static_cast<uint32_t>(g);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
+                                                    int shift, uint32_t* __restrict__ hist,
+                                                    int nblocks) {
+  __shared__ uint32_t cnt[4][kRadix];
+  for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * 1024;
+#pragma unroll 4
+  for (int st = 0; st < 16; ++st) {
+    const int64_t pos = base + st * 64 + lane;
+    const bool valid = pos < n;
+    const uint32_t d = valid ? (keys[pos] >> shift) & (kRadix - 1) : 0u;
+    const uint64_t m = match_digit(d, valid);
+    if (valid && (m & lanemask_lt(lane)) == 0) cnt[w][d] += static_cast<uint32_t>(__popcll(m));
+  }
+  __syncthreads();
+  for (int dg = threadIdx.x; dg < kRadix; dg += 256)
+    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[0][dg] + cnt[1][dg] + cnt[2][dg] + cnt[3][dg];
+}
+
+__global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restrict__ keys_in,
+                                                       const uint32_t* __restrict__ vals_in,
+                                                       int64_t n, int shift,
+                                                       const uint32_t* __restrict__ hist_scan,
+                                                       uint32_t* __restrict__ keys_out,
+                                                       uint32_t* __restrict__ vals_out, int nblocks) {
+  __shared__ uint32_t cnt[4][kRadix];
+  for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * 1024;
+  uint32_t kk[16], vv[16], rk[16];
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const int64_t pos = base + st * 64 + lane;
+    const bool valid = pos < n;
+    kk[st] = valid ? keys_in[pos] : 0u;
+    vv[st] = valid ? vals_in[pos] : 0u;
+  }
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    const bool valid = base + st * 64 + lane < n;
+    const uint32_t d = (kk[st] >> shift) & (kRadix - 1);
+    const uint64_t m = match_digit(d, valid);
+    const uint32_t before = static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
+    const uint32_t pre = cnt[w][d];  // every lane reads before the group leader writes
+    rk[st] = pre + before;
+    if (valid && before == 0) cnt[w][d] = pre + static_cast<uint32_t>(__popcll(m));
+  }
+  __syncthreads();
+  for (int dg = threadIdx.x; dg < kRadix; dg += 256) {
+    uint32_t run = hist_scan[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const uint32_t c = cnt[ww][dg];
+      cnt[ww][dg] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int st = 0; st < 16; ++st) {
+    if (base + st * 64 + lane < n) {
+      const uint32_t d = (kk[st] >> shift) & (kRadix - 1);
+      const uint32_t dst = cnt[w][d] + rk[st];
+      keys_out[dst] = kk[st];
+      vals_out[dst] = vv[st];
+    }
+  }
+}
+
+// Exclusive scan of one tile of 4096 values (256 threads x 16 consecutive values).
+__global__ __launch_bounds__(256) void k_scan_tile(const uint32_t* __restrict__ in,
+                                                   uint32_t* __restrict__ out, int64_t n,
+                                                   uint32_t* __restrict__ tile_sums) {
+  __shared__ uint32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kScanTile + tid * 16;
+  uint32_t v[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = base + i < n ? in[base + i] : 0u;
+    sum += v[i];
+  }
+  // inclusive scan of the thread sums inside the wavefront
+  uint32_t inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint32_t wpre = 0;
+  for (int i = 0; i < w; ++i) wpre += wsum[i];
+  uint32_t run = wpre + inc - sum;  // exclusive prefix of this thread
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (base + i < n) out[base + i] = run;
+    run += v[i];
+  }
+  if (tid == 255) tile_sums[blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+__global__ __launch_bounds__(256) void k_scan_add(uint32_t* __restrict__ out, int64_t n,
+                                                  const uint32_t* __restrict__ tile_pre) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) out[i] += tile_pre[i / kScanTile];
+}
+
+__global__ __launch_bounds__(256) void k_seg_flags(const uint32_t* __restrict__ keys, int64_t n,
+                                                   uint32_t* __restrict__ flags) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q < n) flags[q] = (q == 0 || keys[q] != keys[q - 1]) ? 1u : 0u;
+}
+
+__global__ __launch_bounds__(256) void k_seg_emit(const uint32_t* __restrict__ keys,
+                                                  const uint32_t* __restrict__ flags,
+                                                  const uint32_t* __restrict__ flags_scan, int64_t n,
+                                                  uint32_t* __restrict__ unique_rows,
+                                                  uint32_t* __restrict__ seg_offsets,
+                                                  uint32_t* __restrict__ num_unique) {
+  const int64_t q = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= n) return;
+  if (flags[q]) {
+    const uint32_t u = flags_scan[q];
+    unique_rows[u] = keys[q];
+    seg_offsets[u] = static_cast<uint32_t>(q);
+  }
+  if (q == n - 1) {
+    const uint32_t U = flags_scan[q] + flags[q];
+    num_unique[0] = U;
+    seg_offsets[U] = static_cast<uint32_t>(n);
+  }
+}
+
+__global__ void k_seg_empty(uint32_t* seg_offsets, uint32_t* num_unique) {
+  if (threadIdx.x == 0) {
+    seg_offsets[0] = 0;
+    num_unique[0] = 0;
+  }
+}
+
+int blocks_for(int64_t n, int per) { return static_cast<int>((n + per - 1) / per); }
+
+int key_bits(int64_t total_rows) {
+  int bits = 0;
+  const uint64_t maxkey = total_rows > 0 ? static_cast<uint64_t>(total_rows - 1) : 0;
+  while (bits < 32 && (maxkey >> bits) != 0) ++bits;
+  return bits;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* base) {
+  GradWorkspace ws;
+  ws.n = n;
+  if (n <= 0) return ws;
+  ws.passes = (key_bits(total_rows) + kRadixBits - 1) / kRadixBits;
+  ws.nblocks = (n + kSortTile - 1) / kSortTile;
+  ws.nchunks = (n + kChunk - 1) / kChunk;
+  const int64_t m_hist = ws.nblocks * kRadix;
+  const int64_t scan_len = m_hist > n ? m_hist : n;
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  ws.keys0 = static_cast<uint32_t*>(take(4 * n));
+  ws.vals0 = static_cast<uint32_t*>(take(4 * n));
+  ws.keys1 = static_cast<uint32_t*>(take(4 * n));
+  ws.vals1 = static_cast<uint32_t*>(take(4 * n));
+  ws.hist = static_cast<uint32_t*>(take(4 * m_hist));
+  ws.hist_scan = static_cast<uint32_t*>(take(4 * m_hist));
+  ws.flags = static_cast<uint32_t*>(take(4 * n));
+  ws.flags_scan = static_cast<uint32_t*>(take(4 * n));
+  int64_t len = scan_len;
+  for (int l = 0; l < 4; ++l) {
+    len = (len + kScanTile - 1) / kScanTile;
+    ws.scan_level[l][0] = static_cast<uint32_t*>(take(4 * len));
+    ws.scan_level[l][1] = static_cast<uint32_t*>(take(4 * len));
+    if (len <= 1) break;
+  }
+  ws.head = static_cast<float*>(take(sizeof(float) * ws.nchunks * D));
+  ws.tail = static_cast<float*>(take(sizeof(float) * ws.nchunks * D));
+  ws.through = static_cast<uint32_t*>(take(4 * ws.nchunks));
+  ws.owner = static_cast<uint32_t*>(take(4 * ws.nchunks));
+  ws.bytes = off;
+  return ws;
+}
+
+el_status launch_exclusive_scan(const uint32_t* in, uint32_t* out, int64_t n,
+                                uint32_t* const level[4][2], hipStream_t stream) {
+  if (n <= 0) return EL_OK;
+  const int tiles = blocks_for(n, kScanTile);
+  hipLaunchKernelGGL(k_scan_tile, dim3(tiles), dim3(256), 0, stream, in, out, n, level[0][0]);
+  el_status st = check_launch("scan");
+  if (st != EL_OK || tiles == 1) return st;
+  st = launch_exclusive_scan(level[0][0], level[0][1], tiles, level + 1, stream);
+  if (st != EL_OK) return st;
+  hipLaunchKernelGGL(k_scan_add, dim3(blocks_for(n, 256)), dim3(256), 0, stream, out, n,
+                     static_cast<const uint32_t*>(level[0][1]));
+  return check_launch("scan");
+}
+
+el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                                GradWorkspace& ws, uint32_t** sorted_keys, uint32_t** sorted_vals,
+                                hipStream_t stream) {
+  const int64_t nbags = static_cast<int64_t>(tab.num_tables) * bags.batch;
+  hipLaunchKernelGGL(k_build_keys, dim3(blocks_for(nbags, 256)), dim3(256), 0, stream,
+                     tab.row_offset, bags.indices, bags.offsets, bags.batch,
+                     static_cast<int32_t>(nbags), (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
+                     ws.keys0, ws.vals0);
+  el_status st = check_launch("build_keys");
+  if (st != EL_OK) return st;
+  uint32_t *kin = ws.keys0, *vin = ws.vals0, *kout = ws.keys1, *vout = ws.vals1;
+  const int nb = static_cast<int>(ws.nblocks);
+  for (int pass = 0; pass < ws.passes; ++pass) {
+    const int shift = pass * kRadixBits;
+    hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(256), 0, stream, kin, ws.n, shift, ws.hist, nb);
+    if ((st = check_launch("radix_hist")) != EL_OK) return st;
+    if ((st = launch_exclusive_scan(ws.hist, ws.hist_scan, ws.nblocks * kRadix, ws.scan_level,
+                                    stream)) != EL_OK)
+      return st;
+    hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(256), 0, stream, kin, vin, ws.n, shift,
+                       ws.hist_scan, kout, vout, nb);
+    if ((st = check_launch("radix_scatter")) != EL_OK) return st;
+    std::swap(kin, kout);
+    std::swap(vin, vout);
+  }
+  *sorted_keys = kin;
+  *sorted_vals = vin;
+  return EL_OK;
+}
+
+el_status launch_segments(const GradWorkspace& ws, const uint32_t* sorted_keys,
+                          uint32_t* unique_rows, uint32_t* seg_offsets, uint32_t* num_unique,
+                          hipStream_t stream) {
+  if (ws.n <= 0) {
+    hipLaunchKernelGGL(k_seg_empty, dim3(1), dim3(64), 0, stream, seg_offsets, num_unique);
+    return check_launch("segments");
+  }
+  const int nb = blocks_for(ws.n, 256);
+  hipLaunchKernelGGL(k_seg_flags, dim3(nb), dim3(256), 0, stream, sorted_keys, ws.n, ws.flags);
+  el_status st = check_launch("segments");
+  if (st != EL_OK) return st;
+  if ((st = launch_exclusive_scan(ws.flags, ws.flags_scan, ws.n, ws.scan_level, stream)) != EL_OK)
+    return st;
+  hipLaunchKernelGGL(k_seg_emit, dim3(nb), dim3(256), 0, stream, sorted_keys,
+                     static_cast<const uint32_t*>(ws.flags), static_cast<const uint32_t*>(ws.flags_scan),
+                     ws.n, unique_rows, seg_offsets, num_unique);
+  return check_launch("segments");
+}
+
+}  // namespace el

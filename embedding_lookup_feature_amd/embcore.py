@@ -1,0 +1,211 @@
+"""Python binding of libembcore (the C ABI in ``include/embcore.h``).
+
+Argument marshalling only: torch tensors are passed as raw device pointers plus sizes,
+on torch's current HIP stream unless a stream is given.  Every step of the computation
+runs in the library's HIP kernels; if the library is missing this module raises at load.
+Function names and argument order follow the C ABI.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libembcore.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "embcore.h")
+
+EL_OK, EL_ERR_INVALID_ARG, EL_ERR_UNSUPPORTED, EL_ERR_WORKSPACE, EL_ERR_HIP = range(5)
+EL_F32, EL_F16, EL_BF16 = 0, 1, 2
+EL_FLAG_HASH_INDICES = 1
+
+_DTYPE = {torch.float32: EL_F32, torch.float16: EL_F16, torch.bfloat16: EL_BF16}
+
+
+class EmbcoreError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class ElTables(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("row_offset", ctypes.c_void_p),
+                ("total_rows", ctypes.c_int64), ("num_tables", ctypes.c_int32),
+                ("dim", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class ElBags(ctypes.Structure):
+    _fields_ = [("indices", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("nnz", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with embedding_lookup_feature_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+        T, Bg = ctypes.POINTER(ElTables), ctypes.POINTER(ElBags)
+        L.emb_bag_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp]
+        L.dot_interact_fwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32, vp]
+        L.dot_interact_bwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32,
+                                       vp, vp, ctypes.c_int, vp]
+        L.emb_grad_workspace_bytes.argtypes = [T, Bg]
+        L.emb_grad_workspace_bytes.restype = ctypes.c_size_t
+        L.emb_grad_reduce_update.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
+        L.emb_grad_sort.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp]
+        L.el_validate_bags.argtypes = [T, Bg, u32, vp, vp]
+        L.el_last_error.restype = ctypes.c_char_p
+        L.el_version.restype = ctypes.c_int
+        for name in ("emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd",
+                     "emb_grad_reduce_update", "emb_grad_sort", "el_validate_bags"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions():
+    """Names of the functions `include/embcore.h` declares."""
+    text = open(HEADER).read()
+    return re.findall(r"EL_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def _check(status: int):
+    if status != EL_OK:
+        raise EmbcoreError(status, el_last_error())
+
+
+def el_last_error() -> str:
+    return lib().el_last_error().decode()
+
+
+def el_version() -> int:
+    return lib().el_version()
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DTYPE:
+        raise ValueError(f"{name}: unsupported dtype {t.dtype}")
+    return _DTYPE[t.dtype]
+
+
+class Tables:
+    """F embedding tables in one joint [total_rows, D] buffer; table t owns rows
+    row_offset[t] .. row_offset[t+1]-1."""
+
+    def __init__(self, weight: torch.Tensor, row_offset: torch.Tensor, total_rows: int = None):
+        if weight.dim() != 2 or row_offset.dtype != torch.int64 or row_offset.dim() != 1:
+            raise ValueError("weight must be [total_rows, D]; row_offset int64 [F+1]")
+        self.weight = weight
+        self.row_offset = row_offset
+        self.total_rows = int(weight.shape[0] if total_rows is None else total_rows)
+        self.c = ElTables(_dev(weight, "weight"), _dev(row_offset, "row_offset"), self.total_rows,
+                          row_offset.numel() - 1, weight.shape[1], _dtype(weight, "weight"))
+
+    @property
+    def num_tables(self):
+        return self.c.num_tables
+
+    @property
+    def dim(self):
+        return self.c.dim
+
+
+class Bags:
+    """CSR lookups over F*B table-major bags (bag t*B + b)."""
+
+    def __init__(self, indices: torch.Tensor, offsets: torch.Tensor, batch: int, nnz: int = None):
+        if indices.dtype != torch.int32 or offsets.dtype != torch.int32:
+            raise ValueError("indices and offsets must be int32")
+        self.indices = indices
+        self.offsets = offsets
+        self.batch = int(batch)
+        self.nnz = int(indices.numel() if nnz is None else nnz)
+        ip = _dev(indices, "indices") if indices.numel() else 0
+        self.c = ElBags(ip, _dev(offsets, "offsets"), self.batch, self.nnz)
+
+
+def emb_bag_fwd(tables: Tables, bags: Bags, emb_out: torch.Tensor, hash_indices=False, stream=None):
+    """emb_out[b][t] = sum of the rows of bag (t, b); emb_out is [B, F, D]."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_bag_fwd(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                             _dev(emb_out, "emb_out"), _dtype(emb_out, "emb_out"), _stream(stream)))
+    return emb_out
+
+
+def dot_interact_fwd(x0: torch.Tensor, emb: torch.Tensor, out: torch.Tensor, stream=None):
+    """out[b] = [x0[b] | strict-lower pair dot products | 0 pad]; out is [B, out_stride]."""
+    B, F, D = emb.shape
+    _check(lib().dot_interact_fwd(_dev(x0, "x0"), _dev(emb, "emb"), _dtype(emb, "emb"), B, F, D,
+                                  _dev(out, "out"), _dtype(out, "out"), out.shape[1], _stream(stream)))
+    return out
+
+
+def dot_interact_bwd(x0, emb, dout, dx0, demb, stream=None):
+    """Interaction gradients for upstream gradient dout [B, out_stride]."""
+    B, F, D = emb.shape
+    _check(lib().dot_interact_bwd(_dev(x0, "x0"), _dev(emb, "emb"), _dtype(emb, "emb"), B, F, D,
+                                  _dev(dout, "dout"), _dtype(dout, "dout"), dout.shape[1],
+                                  _dev(dx0, "dx0"), _dev(demb, "demb"), _dtype(demb, "demb"),
+                                  _stream(stream)))
+    return dx0, demb
+
+
+def emb_grad_workspace_bytes(tables: Tables, bags: Bags) -> int:
+    return int(lib().emb_grad_workspace_bytes(ctypes.byref(tables.c), ctypes.byref(bags.c)))
+
+
+def alloc_workspace(tables: Tables, bags: Bags, device=None) -> torch.Tensor:
+    """A byte tensor large enough for the gradient path (torch allocations are 256-aligned)."""
+    n = max(emb_grad_workspace_bytes(tables, bags), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device or tables.weight.device)
+
+
+def emb_grad_reduce_update(tables: Tables, bags: Bags, demb: torch.Tensor, lr: float,
+                           workspace: torch.Tensor, hash_indices=False, stream=None):
+    """Sparse SGD: every looked-up row r gets W[r] -= lr * (sum of its lookups' gradients)."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_grad_reduce_update(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                                        _dev(demb, "demb"), _dtype(demb, "demb"), float(lr),
+                                        _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def emb_grad_sort(tables: Tables, bags: Bags, workspace: torch.Tensor, sorted_rows, bag_ids,
+                  unique_rows, seg_offsets, num_unique, hash_indices=False, stream=None):
+    """The sort / segment stage of the gradient path (int32 tensors hold uint32 values)."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_grad_sort(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                               _dev(workspace, "workspace"), workspace.numel(),
+                               _dev(sorted_rows, "sorted_rows"), _dev(bag_ids, "bag_ids"),
+                               _dev(unique_rows, "unique_rows"), _dev(seg_offsets, "seg_offsets"),
+                               _dev(num_unique, "num_unique"), _stream(stream)))
+
+
+def el_validate_bags(tables: Tables, bags: Bags, bad_count: torch.Tensor, hash_indices=False,
+                     stream=None):
+    """bad_count (int64 [1]) := number of CSR defects / out-of-range indices."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().el_validate_bags(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                                  _dev(bad_count, "bad_count"), _stream(stream)))
+    return bad_count

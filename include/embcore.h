@@ -1,0 +1,166 @@
+/*
+ * embcore.h -- C ABI of the MI355X (gfx950) sparse-embedding + dot-interaction core.
+ *
+ * The calls follow the model statement of the page "DLRM For PyTorch" (§Model
+ * architecture): dense features go through a bottom MLP, every categorical feature has its
+ * own embedding table, the bottom-MLP output and the embedding vectors meet in a "dot
+ * interaction" whose output is concatenated with the bottom-MLP output and fed to the top
+ * MLP.  This library holds the part between the MLPs: the embedding-bag gather, the
+ * interaction forward and backward, and the sparse SGD update of the embedding rows.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all memory; the
+ *     library allocates nothing and keeps no state between calls.
+ *   - Work is enqueued on `stream` and runs asynchronously; no call synchronises.
+ *   - Arguments are validated on the host before anything is enqueued.  A call that
+ *     returns a status other than EL_OK has enqueued nothing, except EL_ERR_HIP, which
+ *     reports a launch failure (text from el_last_error()).
+ *   - Outputs must not alias inputs.  Only emb_grad_reduce_update writes to the tables.
+ *   - Every call with the same inputs produces bitwise identical outputs (no atomics).
+ *   - Float conversions round to nearest even; denormals are kept; NaN stays NaN.
+ */
+#ifndef EMBCORE_H
+#define EMBCORE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__)
+#define EL_API __attribute__((visibility("default")))
+#else
+#define EL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  EL_OK = 0,
+  EL_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, inconsistent shape */
+  EL_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. row size) */
+  EL_ERR_WORKSPACE = 3,   /* workspace smaller than emb_grad_workspace_bytes() */
+  EL_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} el_status;
+
+typedef enum { EL_F32 = 0, EL_F16 = 1, EL_BF16 = 2 } el_dtype;
+
+/* --hash_indices (page "DLRM For PyTorch", §Command-line options): replace every index by
+ * index mod table size, with the floor-modulo sign convention (a negative index maps into
+ * the table).  Without the flag an index outside [0, rows of its table) is undefined
+ * behaviour in the gather/update calls; el_validate_bags counts such indices. */
+enum { EL_FLAG_HASH_INDICES = 1u };
+
+/* All F embedding tables in one "joint" buffer (--embedding_type joint, same page):
+ * table t occupies rows [row_offset[t], row_offset[t+1]) of a row-major
+ * [total_rows][dim] array of `dtype`. */
+typedef struct {
+  void* base;                /* [total_rows][dim], 16-byte aligned; dim * sizeof(dtype) % 16 == 0 */
+  const int64_t* row_offset; /* [F+1] device; row_offset[0] = 0, non-decreasing */
+  int64_t total_rows;        /* [host] == row_offset[F]; < 2^32 */
+  int32_t num_tables;        /* F >= 1 */
+  int32_t dim;               /* D >= 1 */
+  el_dtype dtype;
+} el_tables;
+
+/* Lookups in CSR form over F*B bags, table-major: bag (t, b) has number g = t*B + b and
+ * holds indices[offsets[g] .. offsets[g+1]) (row numbers local to table t).  A bag may be
+ * empty and may repeat a row. */
+typedef struct {
+  const int32_t* indices; /* [nnz], 4-byte aligned */
+  const int32_t* offsets; /* [F*B+1], offsets[0] = 0, non-decreasing, offsets[F*B] = nnz */
+  int32_t batch;          /* B >= 0 */
+  int64_t nnz;            /* [host] == offsets[F*B]; < 2^31 */
+} el_bags;
+
+/*
+ * Embedding bag with sum pooling (same page, §Model architecture: one table per
+ * categorical feature; the pooling over a CSR bag is the multi-hot generalisation):
+ *   emb_out[b][t][:] = sum_{k in bag (t,b), ascending} W_t[indices[k]][:]
+ * accumulated in fp32 and rounded once to out_dtype.  An empty bag gives +0.
+ * emb_out: [B][F][D] of out_dtype, 16-byte aligned.
+ * flags: 0 or EL_FLAG_HASH_INDICES.
+ */
+EL_API el_status emb_bag_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags, void* emb_out,
+                      el_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Dot interaction forward (same page, §Model architecture; --interaction_op dot).  With
+ * V = F+1 vectors per sample (vector 0 = x0[b], vector 1+t = emb[b][t]) and
+ * P = V(V-1)/2 pairs:
+ *   out[b][0:D)        = x0[b]                                  (copy)
+ *   out[b][D + p(i,j)] = <V_i, V_j>, i > j, p(i,j) = i(i-1)/2 + j (row-major strict lower)
+ *   out[b][D+P : out_stride) = +0
+ * x0: [B][D], emb: [B][F][D] of in_dtype; out: [B][out_stride] of out_dtype,
+ * out_stride >= D + P.  bf16/fp16 inputs use MFMA with fp32 accumulation; fp32 inputs
+ * use fp32 FMA.  All base pointers 16-byte aligned.
+ */
+EL_API el_status dot_interact_fwd(const void* x0, const void* emb, el_dtype in_dtype, int32_t B,
+                           int32_t F, int32_t D, void* out, el_dtype out_dtype,
+                           int32_t out_stride, hipStream_t stream);
+
+/*
+ * Dot interaction backward.  With G = dout[b] and the symmetric V x V matrix S,
+ * S_ij = S_ji = G[D + p(i,j)] (i > j), S_ii = 0:
+ *   dV = S V;   dx0[b] = G[0:D) + dV_0;   demb[b][t] = dV_{1+t}
+ * Columns [D+P, out_stride) of dout are ignored.  dout: [B][out_stride] of dout_dtype;
+ * dx0: [B][D], demb: [B][F][D] of grad_dtype.  fp32 accumulation, one rounding.
+ */
+EL_API el_status dot_interact_bwd(const void* x0, const void* emb, el_dtype in_dtype, int32_t B,
+                           int32_t F, int32_t D, const void* dout, el_dtype dout_dtype,
+                           int32_t out_stride, void* dx0, void* demb, el_dtype grad_dtype,
+                           hipStream_t stream);
+
+/* [host, pure] Bytes of device workspace that emb_grad_reduce_update and emb_grad_sort
+ * need for these tables and bags (0 when nnz == 0).  Returns 0 for invalid arguments. */
+EL_API size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags);
+
+/*
+ * Sparse SGD update of the embedding rows (same page, §Command-line options, --lr: plain
+ * SGD).  For every distinct row r looked up by the batch:
+ *   W[r] <- round( W[r] - lr * sum_{lookups k of row r, in lookup order} demb[b_k][t_k] )
+ * Rows that are not looked up are not written.  The lookups are sorted by global row with
+ * a stable, deterministic LSD radix sort; equal rows form segments that are reduced in
+ * fixed-size chunks (fp32) with an ordered fix-up for segments spanning chunks.  No
+ * atomics: the result is bitwise reproducible.
+ * demb: [B][F][D] of grad_dtype, 16-byte aligned.  workspace: >= emb_grad_workspace_bytes,
+ * 256-byte aligned, contents on entry irrelevant.
+ */
+EL_API el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                                 const void* demb, el_dtype grad_dtype, float lr,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The sort and segment stage of emb_grad_reduce_update, exposed for inspection:
+ *   sorted_rows[q], bag_ids[q] (q < nnz): global row (row_offset[t] + index) and bag id
+ *     g = t*B + b of every lookup, sorted by row, equal rows in lookup order;
+ *   unique_rows[u] (u < U): the distinct rows ascending; seg_offsets[u]: first sorted
+ *     position of unique row u, seg_offsets[U] = nnz; num_unique[0] = U.
+ * Arrays: sorted_rows, bag_ids, unique_rows [nnz]; seg_offsets [nnz+1]; num_unique [1].
+ */
+EL_API el_status emb_grad_sort(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                        void* workspace, size_t workspace_bytes, uint32_t* sorted_rows,
+                        uint32_t* bag_ids, uint32_t* unique_rows, uint32_t* seg_offsets,
+                        uint32_t* num_unique, hipStream_t stream);
+
+/*
+ * Count defects of a CSR batch: offsets that decrease, offsets[0] != 0,
+ * offsets[F*B] != nnz, and (without EL_FLAG_HASH_INDICES) indices outside their table.
+ * bad_count: [1] int64 device, overwritten with the total.
+ */
+EL_API el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                           int64_t* bad_count, hipStream_t stream);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+EL_API const char* el_last_error(void);
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+EL_API int el_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMBCORE_H */

@@ -1,0 +1,321 @@
+"""Parity of every HIP call with the CPU oracle on seeded synthetic inputs (GPU).
+
+Sizes are small enough for the oracle to finish in seconds but span several tiles of
+every kernel and end in a ragged tail.  Both sides always receive the same input bytes,
+drawn by ``synth`` (never produced by the HIP path).  Bars: hotness-1 gathers, sorted
+rows, bag ids and segments bit for bit; fp32 results within 1e-5 and 16-bit results
+within 2e-2 relative error (max |g - r| / max(|r|, rms r)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import embedding_lookup_feature_amd as elf
+from embedding_lookup_feature_amd import synth
+from oracle import oracle as orc
+from tests.helpers import NAME, assert_bits, assert_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def base_wl(**kw):
+    return synth.WORKLOADS["train_step"].scaled(name="parity", **kw)
+
+
+def make_problem(wl, hash_spread=False):
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    if hash_spread:
+        # indices far outside [0, n) on both sides; --hash_indices folds them back
+        g = torch.Generator(device=DEV)
+        g.manual_seed(synth.seed_for(wl.name, "spread"))
+        k = torch.randint(-3, 4, idx.shape, generator=g, device=DEV, dtype=torch.int64)
+        rows = torch.tensor(wl.rows, device=DEV, dtype=torch.int64)
+        lens = off[1:].long() - off[:-1].long()
+        t_of = torch.repeat_interleave(torch.arange(wl.num_tables, device=DEV).repeat_interleave(wl.batch), lens)
+        idx = (idx.long() + k * rows[t_of]).to(torch.int32)
+    return W, ro, idx, off
+
+
+EMB_CASES = [
+    # label, rows, D, table dtype, out dtype, bag, index dist, hash, B
+    ("f32-d16-hot1", (1000,) * 8, 16, "f32", "f32", ("one",), "uniform", False, 777),
+    ("f32-bf16-d128-zipf", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 700),
+    ("f16-d128-zipf-ragged-tables", (3, 70000, 1234), 128, "f16", "f16", ("one",), "zipf", False, 1500),
+    ("bf16-d64-multihot", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300),
+    ("bf16-f32-d64-empty-bags", (500,) * 5, 64, "bf16", "f32", ("poisson", 3.0, 0, 10), "uniform", False, 333),
+    ("f32-d512-nvl2", (300,) * 3, 512, "f32", "f32", ("poisson", 2.0, 0, 5), "uniform", False, 100),
+    ("f32-bf16-d1024-nvl4", (64,) * 2, 1024, "f32", "bf16", ("poisson", 3.0, 0, 6), "uniform", False, 50),
+    ("bf16-d8-one-lane", (100,) * 4, 8, "bf16", "bf16", ("one",), "uniform", False, 65),
+    ("f32-hash-hot1", (999, 7, 5000), 32, "f32", "f32", ("one",), "uniform", True, 400),
+    ("bf16-hash-multihot", (999, 7, 5000), 64, "bf16", "bf16", ("poisson", 4.0, 0, 9), "zipf", True, 200),
+]
+
+
+@pytest.mark.parametrize("case", EMB_CASES, ids=[c[0] for c in EMB_CASES])
+def test_emb_bag_fwd_matches_oracle(case):
+    label, rows, D, tdt, odt, bag, dist, hsh, B = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=odt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag)
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    out = torch.full((B, wl.num_tables, D), float("nan"), dtype=synth.torch_dtype(odt), device=DEV)
+    elf.emb_bag_fwd(elf.Tables(W, ro), elf.Bags(idx, off, B), out, hash_indices=hsh)
+    torch.cuda.synchronize()
+    ref = orc.emb_bag_fwd(to_np(W), tdt, to_np(ro), to_np(idx), to_np(off), B, D, odt, hash_indices=hsh)
+    if bag == ("one",):
+        assert_bits(out, ref, label)
+    else:
+        assert_close(out, ref, odt, label)
+    # determinism: a second call gives the same bits
+    out2 = torch.empty_like(out)
+    elf.emb_bag_fwd(elf.Tables(W, ro), elf.Bags(idx, off, B), out2, hash_indices=hsh)
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+
+
+DOT_CASES = [
+    # label, F, D, in dtype, out dtype, out_stride (None = padded to 16 bytes), B
+    ("f32-tiny", 8, 16, "f32", "f32", None, 300),
+    ("bf16-27x128", 26, 128, "bf16", "bf16", None, 1000),
+    ("f16-27x128", 26, 128, "f16", "f16", None, 513),
+    ("bf16-101x64", 100, 64, "bf16", "bf16", None, 100),
+    ("bf16-101x64-odd-stride", 100, 64, "bf16", "bf16", 5114 + 3, 37),
+    ("bf16-two-vectors", 1, 16, "bf16", "bf16", None, 64),
+    ("bf16-32-vectors", 31, 32, "bf16", "f32", None, 99),
+    ("bf16-33-vectors", 32, 32, "bf16", "bf16", None, 99),
+    ("bf16-128-vectors", 127, 32, "bf16", "bf16", None, 10),
+    ("bf16-d24-fma-path", 5, 24, "bf16", "bf16", None, 50),
+    ("f32-27x128", 26, 128, "f32", "bf16", None, 200),
+]
+
+
+def dot_inputs(F, D, idt, B, stride):
+    wl = base_wl(batch=B, rows=(10,) * F, dim=D, act_dtype=idt, bottom_mlp=(13, 64, D))
+    x0 = synth.make_x0(wl, DEV)
+    emb = synth.make_emb(wl, DEV)
+    stride = stride or wl.out_stride
+    return wl, x0, emb, stride
+
+
+@pytest.mark.parametrize("case", DOT_CASES, ids=[c[0] for c in DOT_CASES])
+def test_dot_interact_fwd_matches_oracle(case):
+    label, F, D, idt, odt, stride, B = case
+    wl, x0, emb, stride = dot_inputs(F, D, idt, B, stride)
+    out = torch.full((B, stride), float("nan"), dtype=synth.torch_dtype(odt), device=DEV)
+    elf.dot_interact_fwd(x0, emb, out)
+    torch.cuda.synchronize()
+    ref = orc.dot_interact_fwd(to_np(x0), to_np(emb), idt, odt, stride)
+    P = (F + 1) * F // 2
+    assert_bits(out[:, :D], ref[:, :D], label + " x0 copy")
+    assert_close(out[:, D:D + P], ref[:, D:D + P], odt, label + " pairs")
+    assert_bits(out[:, D + P:], ref[:, D + P:], label + " padding")
+    out2 = torch.empty_like(out)
+    elf.dot_interact_fwd(x0, emb, out2)
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+
+
+BWD_CASES = [
+    # label, F, D, in dtype, dout dtype, grad dtype, stride, B
+    ("f32-tiny", 8, 16, "f32", "f32", "f32", None, 300),
+    ("bf16-27x128", 26, 128, "bf16", "bf16", "bf16", None, 1000),
+    ("f16-27x128", 26, 128, "f16", "f16", "f16", None, 300),
+    ("bf16-101x64", 100, 64, "bf16", "bf16", "bf16", None, 60),
+    ("bf16-101x64-odd-stride", 100, 64, "bf16", "bf16", "bf16", 5114 + 1, 20),
+    ("bf16-two-vectors-d32", 1, 32, "bf16", "bf16", "f32", None, 64),
+    ("bf16-33-vectors", 32, 32, "bf16", "bf16", "bf16", None, 99),
+    ("bf16-128-vectors", 127, 32, "bf16", "bf16", "bf16", None, 8),
+    ("bf16-f32-dout-fma-path", 26, 128, "bf16", "f32", "bf16", None, 50),
+    ("bf16-d16-fma-path", 8, 16, "bf16", "bf16", "bf16", None, 70),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_dot_interact_bwd_matches_oracle(case):
+    label, F, D, idt, ddt, gdt, stride, B = case
+    wl, x0, emb, stride = dot_inputs(F, D, idt, B, stride)
+    wlg = wl.scaled(act_dtype=ddt)
+    dout = torch.zeros((B, stride), dtype=synth.torch_dtype(ddt), device=DEV)
+    dout[:, :wl.out_width] = synth.make_dout(wlg, DEV)[:, :wl.out_width]
+    dout[:, wl.out_width:] = 1e3  # padding columns must be ignored
+    gt = synth.torch_dtype(gdt)
+    dx0 = torch.full((B, D), float("nan"), dtype=gt, device=DEV)
+    demb = torch.full((B, F, D), float("nan"), dtype=gt, device=DEV)
+    elf.dot_interact_bwd(x0, emb, dout, dx0, demb)
+    torch.cuda.synchronize()
+    rdx0, rdemb = orc.dot_interact_bwd(to_np(x0), to_np(emb), idt, to_np(dout), ddt, gdt)
+    assert_close(dx0, rdx0, gdt, label + " dx0")
+    assert_close(demb, rdemb, gdt, label + " demb")
+    dx0b, dembb = torch.empty_like(dx0), torch.empty_like(demb)
+    elf.dot_interact_bwd(x0, emb, dout, dx0b, dembb)
+    assert torch.equal(dx0.view(torch.uint8), dx0b.view(torch.uint8))
+    assert torch.equal(demb.view(torch.uint8), dembb.view(torch.uint8))
+
+
+SORT_CASES = [
+    # label, rows, D, table dtype, grad dtype, bag, dist, hash, B
+    ("hot1-zipf-26x5000", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 777),
+    ("multihot-bf16", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300),
+    ("f16-table-f32-grad", (3000, 17, 40000), 32, "f16", "f32", ("poisson", 5.0, 0, 12), "zipf", False, 500),
+    ("hash-negative", (999, 7, 5000), 64, "bf16", "f32", ("poisson", 4.0, 0, 9), "uniform", True, 250),
+    ("tiny-f32", (1000,) * 8, 16, "f32", "f32", ("one",), "uniform", False, 256),
+    ("four-radix-passes", (20_000_000, 5), 4, "f32", "f32", ("poisson", 3.0, 0, 8), "uniform", False, 3000),
+]
+
+
+def grad_problem(case):
+    label, rows, D, tdt, gdt, bag, dist, hsh, B = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=gdt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag)
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    return wl, W, ro, idx, off
+
+
+def run_sort(W, ro, idx, off, B, hsh):
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    ws = elf.alloc_workspace(tab, bags)
+    n = idx.numel()
+    outs = [torch.full((max(n, 1),), -1, dtype=torch.int32, device=DEV) for _ in range(3)]
+    seg = torch.full((n + 1,), -1, dtype=torch.int32, device=DEV)
+    nu = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    elf.emb_grad_sort(tab, bags, ws, outs[0], outs[1], outs[2], seg, nu, hash_indices=hsh)
+    torch.cuda.synchronize()
+    return outs, seg, nu
+
+
+@pytest.mark.parametrize("case", SORT_CASES, ids=[c[0] for c in SORT_CASES])
+def test_emb_grad_sort_bit_exact(case):
+    wl, W, ro, idx, off = grad_problem(case)
+    hsh = case[7]
+    (srt, bag_ids, uniq), seg, nu = run_sort(W, ro, idx, off, wl.batch, hsh)
+    ref = orc.grad_sort(to_np(ro), to_np(idx), to_np(off), wl.batch, hash_indices=hsh)
+    U = ref["num_unique"]
+    assert int(nu.item()) == U
+    assert_bits(srt.view(torch.int32)[:idx.numel()], ref["sorted_rows"].view(np.int32), "sorted_rows")
+    assert_bits(bag_ids[:idx.numel()], ref["bag_ids"].view(np.int32), "bag_ids")
+    assert_bits(uniq[:U], ref["unique_rows"].view(np.int32), "unique_rows")
+    assert_bits(seg[:U + 1], ref["seg_offsets"].view(np.int32), "seg_offsets")
+
+
+def test_emb_grad_sort_degenerate():
+    # every lookup hits one row (one segment across many chunks and radix tiles)
+    wl = base_wl(batch=5000, rows=(50, 50, 50), dim=16, table_dtype="f32", act_dtype="f32",
+                 index_dist="uniform")
+    W, ro = synth.make_tables(wl, DEV)
+    off = torch.arange(3 * 5000 + 1, dtype=torch.int32, device=DEV)
+    idx = torch.full((15000,), 7, dtype=torch.int32, device=DEV)
+    (srt, bag_ids, uniq), seg, nu = run_sort(W, ro, idx, off, 5000, False)
+    assert int(nu.item()) == 3
+    assert to_np(uniq[:3]).tolist() == [7, 57, 107]
+    assert to_np(seg[:4]).tolist() == [0, 5000, 10000, 15000]
+    assert np.array_equal(to_np(bag_ids), np.arange(15000, dtype=np.int32))
+    # no lookups at all
+    off0 = torch.zeros(3 * 10 + 1, dtype=torch.int32, device=DEV)
+    idx0 = torch.zeros(0, dtype=torch.int32, device=DEV)
+    (_, _, _), seg0, nu0 = run_sort(W, ro, idx0, off0, 10, False)
+    assert int(nu0.item()) == 0 and int(seg0[0].item()) == 0
+    # a single-row table: keys need no radix pass
+    W1 = torch.zeros((1, 16), dtype=torch.float32, device=DEV)
+    ro1 = torch.tensor([0, 1], dtype=torch.int64, device=DEV)
+    off1 = torch.arange(101, dtype=torch.int32, device=DEV)
+    idx1 = torch.zeros(100, dtype=torch.int32, device=DEV)
+    (srt1, bag1, _), seg1, nu1 = run_sort(W1, ro1, idx1, off1, 100, False)
+    assert int(nu1.item()) == 1 and np.array_equal(to_np(bag1), np.arange(100, dtype=np.int32))
+
+
+UPDATE_CASES = SORT_CASES + [
+    ("one-row-per-table", (50, 50, 50), 16, "f32", "f32", ("one",), "uniform", False, 5000),
+]
+
+
+@pytest.mark.parametrize("case", UPDATE_CASES, ids=[c[0] for c in UPDATE_CASES])
+def test_emb_grad_reduce_update_matches_oracle(case):
+    label = case[0]
+    wl, W, ro, idx, off = grad_problem(case)
+    hsh = case[7]
+    if label == "one-row-per-table":
+        idx = torch.full_like(idx, 7)
+    B, tdt, gdt = wl.batch, wl.table_dtype, wl.act_dtype
+    demb = synth.make_demb(wl, DEV, dtype=gdt)
+    W0 = to_np(W)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    ws = elf.alloc_workspace(tab, bags)
+    ws.fill_(0xAB)  # contents on entry must not matter
+    elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws, hash_indices=hsh)
+    torch.cuda.synchronize()
+    ref = orc.grad_reduce_update(W0, tdt, to_np(ro), to_np(idx), to_np(off), B, to_np(demb), gdt,
+                                 wl.lr, hash_indices=hsh)
+    got = to_np(W)
+    keys = orc.grad_sort(to_np(ro), to_np(idx), to_np(off), B, hash_indices=hsh)["unique_rows"]
+    touched = np.zeros(W0.shape[0], bool)
+    touched[keys.astype(np.int64)] = True
+    # untouched rows bitwise unchanged, touched rows within tolerance
+    assert_bits(W[torch.from_numpy(~touched).to(DEV)], W0[~touched], label + " untouched rows")
+    assert_close(W[torch.from_numpy(touched).to(DEV)], ref[touched], tdt, label + " updated rows")
+
+
+def test_emb_grad_reduce_update_is_deterministic_and_lr0_is_identity():
+    case = SORT_CASES[0]
+    wl, W, ro, idx, off = grad_problem(case)
+    demb = synth.make_demb(wl, DEV, dtype="bf16")
+    tab_w = [W.clone(), W.clone(), W.clone()]
+    for i, Wi in enumerate(tab_w):
+        tab, bags = elf.Tables(Wi, ro), elf.Bags(idx, off, wl.batch)
+        ws = elf.alloc_workspace(tab, bags)
+        elf.emb_grad_reduce_update(tab, bags, demb, 0.0 if i == 2 else 0.01, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(tab_w[0].view(torch.int32), tab_w[1].view(torch.int32))
+    assert torch.equal(tab_w[2].view(torch.int32), W.view(torch.int32))
+
+
+def test_validate_bags_counts_defects():
+    wl = base_wl(batch=100, rows=(10, 20), dim=16, table_dtype="f32", index_dist="uniform",
+                 bag=("poisson", 3.0, 0, 6))
+    W, ro, idx, off = make_problem(wl)
+    tab = elf.Tables(W, ro)
+    cnt = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    elf.el_validate_bags(tab, elf.Bags(idx, off, 100), cnt)
+    assert int(cnt.item()) == 0
+    bad_idx = idx.clone()
+    n0 = int(off[100].item())  # lookups of table 0
+    bad_idx[0] = -1
+    bad_idx[n0 - 1] = 10       # table 0 has 10 rows
+    bad_idx[n0] = 20           # table 1 has 20 rows
+    elf.el_validate_bags(tab, elf.Bags(bad_idx, off, 100), cnt)
+    assert int(cnt.item()) == 3
+    elf.el_validate_bags(tab, elf.Bags(bad_idx, off, 100), cnt, hash_indices=True)
+    assert int(cnt.item()) == 0
+    bad_off = off.clone()
+    bad_off[5] = bad_off[6] + 1  # decreasing pair
+    elf.el_validate_bags(tab, elf.Bags(idx, bad_off, 100), cnt)
+    assert int(cnt.item()) >= 1
+
+
+def test_tiny_training_step_chain_matches_oracle_chain():
+    """The whole path on the tiny fp32 workload: each side runs its own chain."""
+    wl = synth.WORKLOADS["tiny"]
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    G = synth.make_dout(wl, DEV)
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W0 = to_np(W)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    emb = torch.empty((B, F, D), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, wl.out_stride), dtype=torch.float32, device=DEV)
+    dx0 = torch.empty((B, D), dtype=torch.float32, device=DEV)
+    demb = torch.empty((B, F, D), dtype=torch.float32, device=DEV)
+    ws = elf.alloc_workspace(tab, bags)
+    elf.emb_bag_fwd(tab, bags, emb)
+    elf.dot_interact_fwd(x0, emb, out)
+    elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+    elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
+    torch.cuda.synchronize()
+    r_emb = orc.emb_bag_fwd(W0, "f32", to_np(ro), to_np(idx), to_np(off), B, D, "f32")
+    r_out = orc.dot_interact_fwd(to_np(x0), r_emb, "f32", "f32", wl.out_stride)
+    r_dx0, r_demb = orc.dot_interact_bwd(to_np(x0), r_emb, "f32", to_np(G), "f32", "f32")
+    r_W = orc.grad_reduce_update(W0, "f32", to_np(ro), to_np(idx), to_np(off), B, r_demb, "f32", wl.lr)
+    assert_bits(emb, r_emb, "emb")
+    assert_close(out, r_out, "f32", "interaction output")
+    assert_close(dx0, r_dx0, "f32", "dx0")
+    assert_close(demb, r_demb, "f32", "demb")
+    assert_close(W, r_W, "f32", "updated tables")
