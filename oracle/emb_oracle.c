@@ -184,7 +184,10 @@ static int check_offsets(const int32_t* offsets, int64_t nbags) {
  * emb[b][t][:] = sum over the lookups k of bag (t, b), in ascending k, of the table row
  * W_t[idx[k]].  Bags are table-major: bag (t, b) is number g = t*B + b and holds the
  * lookups offsets[g] .. offsets[g+1]-1.  The joint table stores table t at rows
- * row_offset[t] .. row_offset[t+1]-1 of a [total_rows][D] array.  An empty bag gives +0.
+ * row_offset[t] .. row_offset[t+1]-1 of a [total_rows][D] array.
+ * The sum of a non-empty bag is x_1 + x_2 + ... + x_n, starting from its first row, so a
+ * one-row bag returns that row exactly (sign of zero included: the hotness-1 gather is an
+ * index select).  An empty bag gives +0.
  */
 int oracle_emb_bag_fwd(const void* W, int w_dtype, const int64_t* row_offset, int F, int D,
                        const int32_t* indices, const int32_t* offsets, int B, int hash,
@@ -203,7 +206,10 @@ int oracle_emb_bag_fwd(const void* W, int w_dtype, const int64_t* row_offset, in
       for (int64_t k = offsets[g]; k < offsets[g + 1]; ++k) {
         int64_t row = resolve_row(row_offset, t, indices[k], hash);
         if (row < 0) { free(acc); return OR_BAD_INDEX; }
-        for (int d = 0; d < D; ++d) acc[d] += load_elem(W, w_dtype, (size_t)row * D + d);
+        for (int d = 0; d < D; ++d) {
+          double w = load_elem(W, w_dtype, (size_t)row * D + d);
+          acc[d] = (k == offsets[g]) ? w : acc[d] + w;
+        }
       }
       for (int d = 0; d < D; ++d)
         store_elem(out, out_dtype, ((size_t)b * F + t) * D + d, acc[d]);

@@ -16,7 +16,8 @@ from oracle import oracle as orc
 from tests import test_oracle_pins as pins
 
 MUTANTS = [
-    ("pooling sign", "acc[d] += load_elem(W, w_dtype", "acc[d] -= load_elem(W, w_dtype"),
+    ("pooling sign", "acc[d] = (k == offsets[g]) ? w : acc[d] + w;", "acc[d] = (k == offsets[g]) ? w : acc[d] - w;"),
+    ("pooling starts from +0", "acc[d] = (k == offsets[g]) ? w : acc[d] + w;", "acc[d] = acc[d] + w;"),
     ("pooled output transposed", "store_elem(out, out_dtype, ((size_t)b * F + t) * D + d, acc[d]);",
      "store_elem(out, out_dtype, ((size_t)t * B + b) * D + d, acc[d]);"),
     ("C remainder instead of floor modulo", "return r < 0 ? r + n : r;", "return r;"),
@@ -53,6 +54,7 @@ def battery():
         lambda: pins.test_emb_bag_equals_dense_count_matrix("bf16"),
         pins.test_emb_bag_hotness1_is_index_select_bit_exact,
         pins.test_emb_bag_empty_bags_give_positive_zero,
+        pins.test_emb_bag_hotness1_keeps_signed_zeros_and_subnormals,
         pins.test_emb_bag_hash_is_floor_modulo,
         pins.test_emb_bag_rounding_is_single_rne,
         lambda: pins.test_dot_fwd_equals_masked_gram(8, 16),

@@ -232,6 +232,21 @@ def test_emb_bag_hotness1_is_index_select_bit_exact():
         assert np.array_equal(out16[:, t, :], f32_to_bf16_bits_torch(sel))
 
 
+def test_emb_bag_hotness1_keeps_signed_zeros_and_subnormals():
+    # a one-row bag is an index select: -0.0 and fp16 subnormal rows come back bit for bit
+    F, B, D = 1, 4, 8
+    row_offset = np.array([0, 4], np.int64)
+    offsets = np.arange(B + 1, dtype=np.int32)
+    indices = np.array([0, 1, 2, 3], np.int32)
+    bits = np.array([[0x8000] * 8, [0x0001] * 8, [0x8001] * 8, [0x03FF] * 8], np.uint16)
+    W = bits.view(np.float16)
+    out = orc.emb_bag_fwd(W, "f16", row_offset, indices, offsets, B, D, "f16")
+    assert np.array_equal(out.view(np.uint16).reshape(B, D), bits)
+    out32 = orc.emb_bag_fwd(W, "f16", row_offset, indices, offsets, B, D, "f32")
+    assert np.array_equal(out32.reshape(B, D), W.astype(np.float32))
+    assert np.signbit(out32[0, 0, 0])
+
+
 def test_emb_bag_empty_bags_give_positive_zero():
     F, B, D = 2, 3, 4
     row_offset = np.array([0, 5, 10], np.int64)
