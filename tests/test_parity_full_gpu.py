@@ -1,0 +1,184 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times (GPU).
+
+The GPU runs every call over the whole batch; the oracle checks either everything (when
+it finishes in seconds) or sampled samples / the touched rows, restricted with
+``tests.helpers.sub_batch`` / ``compact_tables`` (row-order-preserving renumbering, so
+sums and sort order are unchanged).  Chained checks give each side its own chain: the
+oracle's interaction input is the oracle's own pooled output, the GPU's is the GPU's.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import embedding_lookup_feature_amd as elf
+from embedding_lookup_feature_amd import synth
+from oracle import oracle as orc
+from tests.helpers import assert_bits, assert_close, compact_tables, sub_batch, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SAMPLES = 384
+
+
+def sample_ids(B, k=SAMPLES, seed=7):
+    rng = np.random.default_rng(seed)
+    s = np.unique(np.concatenate([[0, B - 1], rng.choice(B, size=k, replace=False)]))
+    return s
+
+
+@pytest.fixture(autouse=True)
+def _free_memory():
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_train_step_full_size():
+    """B = 65536, 26 x 100,000 x 128 fp32 tables, bf16 activations, Zipf(1.05) hotness 1:
+    every stage of the step over the whole batch."""
+    wl = synth.WORKLOADS["train_step"]
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    G = synth.make_dout(wl, DEV)
+    W0, ro_h, idx_h, off_h = to_np(W), to_np(ro), to_np(idx), to_np(off)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+
+    # gather: every output, bit for bit
+    emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb)
+    r_emb = orc.emb_bag_fwd(W0, "f32", ro_h, idx_h, off_h, B, D, "bf16")
+    assert_bits(emb, r_emb, "train_step emb_bag_fwd")
+
+    # interaction forward / backward on sampled samples (each side's own pooled input)
+    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    elf.dot_interact_fwd(x0, emb, out)
+    dx0 = torch.empty((B, D), dtype=torch.bfloat16, device=DEV)
+    demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :D].view(torch.int16), x0.view(torch.int16))  # copy part, all rows
+    assert torch.count_nonzero(out[:, wl.out_width:].float()) == 0          # padding, all rows
+    s = sample_ids(B)
+    r_out = orc.dot_interact_fwd(to_np(x0)[s], r_emb[s], "bf16", "bf16", wl.out_stride)
+    assert_close(out[torch.from_numpy(s).to(DEV)], r_out, "bf16", "train_step dot fwd")
+    r_dx0, r_demb = orc.dot_interact_bwd(to_np(x0)[s], r_emb[s], "bf16", to_np(G)[s], "bf16", "bf16")
+    sel = torch.from_numpy(s).to(DEV)
+    assert_close(dx0[sel], r_dx0, "bf16", "train_step dx0")
+    assert_close(demb[sel], r_demb, "bf16", "train_step demb")
+
+    # sort + segments: everything, bit for bit
+    ws = elf.alloc_workspace(tab, bags)
+    n = idx.numel()
+    srt, bag_ids, uniq = (torch.empty(n, dtype=torch.int32, device=DEV) for _ in range(3))
+    seg = torch.empty(n + 1, dtype=torch.int32, device=DEV)
+    nu = torch.empty(1, dtype=torch.int32, device=DEV)
+    elf.emb_grad_sort(tab, bags, ws, srt, bag_ids, uniq, seg, nu)
+    ref = orc.grad_sort(ro_h, idx_h, off_h, B)
+    U = ref["num_unique"]
+    assert int(nu.item()) == U
+    assert_bits(srt, ref["sorted_rows"].view(np.int32), "sorted_rows")
+    assert_bits(bag_ids, ref["bag_ids"].view(np.int32), "bag_ids")
+    assert_bits(uniq[:U], ref["unique_rows"].view(np.int32), "unique_rows")
+    assert_bits(seg[:U + 1], ref["seg_offsets"].view(np.int32), "seg_offsets")
+
+    # reduce + SGD on a synthetic gradient (same input on both sides), whole table
+    dsyn = synth.make_demb(wl, DEV)
+    elf.emb_grad_reduce_update(tab, bags, dsyn, wl.lr, ws)
+    torch.cuda.synchronize()
+    r_W = orc.grad_reduce_update(W0, "f32", ro_h, idx_h, off_h, B, to_np(dsyn), "bf16", wl.lr)
+    touched = np.zeros(W0.shape[0], bool)
+    touched[ref["unique_rows"].astype(np.int64)] = True
+    got = to_np(W)
+    assert np.array_equal(got[~touched].view(np.uint32), W0[~touched].view(np.uint32)), "untouched rows changed"
+    assert_close(W[torch.from_numpy(touched).to(DEV)], r_W[touched], "f32", "train_step SGD rows")
+
+
+def test_large_table_full_size_sampled():
+    """B = 262144, 26 fp16 tables of 4 .. 40M rows (200M rows, 51.2 GB), Zipf(1.1):
+    full-batch gather and interaction, checked on sampled samples."""
+    wl = synth.WORKLOADS["large_table"]
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    emb = torch.empty((B, F, D), dtype=torch.float16, device=DEV)
+    elf.emb_bag_fwd(elf.Tables(W, ro), elf.Bags(idx, off, B), emb)
+    out = torch.empty((B, wl.out_stride), dtype=torch.float16, device=DEV)
+    elf.dot_interact_fwd(x0, emb, out)
+    torch.cuda.synchronize()
+    s = sample_ids(B)
+    si, so, nb = sub_batch(to_np(idx), to_np(off), F, B, s)
+    Wc, roc, sic, _ = compact_tables(W, to_np(ro), si, so, F, nb)
+    r_emb = orc.emb_bag_fwd(Wc, "f16", roc, sic, so, nb, D, "f16")
+    sel = torch.from_numpy(s).to(DEV)
+    assert_bits(emb[sel], r_emb, "large_table emb_bag_fwd")
+    r_out = orc.dot_interact_fwd(to_np(x0)[s], r_emb, "f16", "f16", wl.out_stride)
+    assert_close(out[sel], r_out, "f16", "large_table dot fwd")
+    assert torch.equal(out[:, :D].view(torch.int16), x0.view(torch.int16))
+
+
+def test_multi_hot_full_size():
+    """B = 16384, 100 bf16 tables x 1M x 64, Poisson(20) bags, 101 vectors: full-batch
+    forward / backward / update; gather and interaction checked on sampled samples, the
+    sort bit for bit over all 32.8M lookups, the update on every touched row."""
+    wl = synth.WORKLOADS["multi_hot"]
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    G = synth.make_dout(wl, DEV)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb)
+    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    elf.dot_interact_fwd(x0, emb, out)
+    dx0 = torch.empty((B, D), dtype=torch.bfloat16, device=DEV)
+    demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+    torch.cuda.synchronize()
+    idx_h, off_h, ro_h = to_np(idx), to_np(off), to_np(ro)
+
+    s = sample_ids(B, k=128)
+    sel = torch.from_numpy(s).to(DEV)
+    si, so, nb = sub_batch(idx_h, off_h, F, B, s)
+    Wc, roc, sic, _ = compact_tables(W, ro_h, si, so, F, nb)
+    r_emb = orc.emb_bag_fwd(Wc, "bf16", roc, sic, so, nb, D, "bf16")
+    assert_close(emb[sel], r_emb, "bf16", "multi_hot emb_bag_fwd")
+    r_out = orc.dot_interact_fwd(to_np(x0)[s], r_emb, "bf16", "bf16", wl.out_stride)
+    assert_close(out[sel], r_out, "bf16", "multi_hot dot fwd")
+    r_dx0, r_demb = orc.dot_interact_bwd(to_np(x0)[s], r_emb, "bf16", to_np(G)[s], "bf16", "bf16")
+    assert_close(dx0[sel], r_dx0, "bf16", "multi_hot dx0")
+    assert_close(demb[sel], r_demb, "bf16", "multi_hot demb")
+    del emb, out, dx0, demb
+
+    ws = elf.alloc_workspace(tab, bags)
+    n = idx.numel()
+    srt, bag_ids, uniq = (torch.empty(n, dtype=torch.int32, device=DEV) for _ in range(3))
+    seg = torch.empty(n + 1, dtype=torch.int32, device=DEV)
+    nu = torch.empty(1, dtype=torch.int32, device=DEV)
+    elf.emb_grad_sort(tab, bags, ws, srt, bag_ids, uniq, seg, nu)
+    ref = orc.grad_sort(ro_h, idx_h, off_h, B)
+    U = ref["num_unique"]
+    assert int(nu.item()) == U
+    assert_bits(srt, ref["sorted_rows"].view(np.int32), "multi_hot sorted_rows")
+    assert_bits(bag_ids, ref["bag_ids"].view(np.int32), "multi_hot bag_ids")
+    assert_bits(seg[:U + 1], ref["seg_offsets"].view(np.int32), "multi_hot seg_offsets")
+    del srt, bag_ids, uniq, seg, ref
+
+    # update on every touched row: the problem restricted to its touched rows is exact
+    Wc, roc, ic, rows = compact_tables(W, ro_h, idx_h, off_h, F, B)
+    dsyn = synth.make_demb(wl, DEV)
+    elf.emb_grad_reduce_update(tab, bags, dsyn, wl.lr, ws)
+    torch.cuda.synchronize()
+    r_Wc = orc.grad_reduce_update(Wc, "bf16", roc, ic, off_h, B, to_np(dsyn), "bf16", wl.lr)
+    got = W.index_select(0, torch.from_numpy(rows).to(DEV))
+    assert_close(got, r_Wc, "bf16", "multi_hot SGD rows")
+    # rows outside the batch are untouched: compare a sample of them with a regenerated copy
+    W_fresh, _ = synth.make_tables(wl, DEV)
+    mask = torch.ones(wl.total_rows, dtype=torch.bool, device=DEV)
+    mask[torch.from_numpy(rows).to(DEV)] = False
+    assert torch.equal(W[mask].view(torch.int16), W_fresh[mask].view(torch.int16))
