@@ -52,6 +52,9 @@ def main():
     ap.add_argument("--batches", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel "
+                         "of known size, to scale HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -93,6 +96,15 @@ def main():
         if ev: ev[3].record()
         elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
         if ev: ev[4].record()
+
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for i in range(args.warmup):
         step(i)
