@@ -17,6 +17,9 @@
 // result does not depend on how the hardware orders K inside one instruction.
 // fp32 inputs (and shapes the MFMA path does not cover) use an fp32 FMA kernel.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "el_internal.hpp"
 
@@ -102,7 +105,7 @@ __device__ inline u32x4 lds16_or_zero(const char* lds, int off, bool ok) {
 // Forward, MFMA path.
 // LDS: V x D tile (pitch 2D+16) | one output row (16-byte rounded) | 16-byte scratch slot.
 // ---------------------------------------------------------------------------------------
-template <class IT, class OT, int NQ>
+template <class IT, class OT, int NQ, int SPL>
 __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict__ x0,
                                                      const uint16_t* __restrict__ emb, int B, int F,
                                                      int D, typename OT::S* __restrict__ out,
@@ -155,9 +158,17 @@ __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict_
     }
     __syncthreads();
     OS* orow = out + static_cast<int64_t>(b) * out_stride;
-    if (vec_out) {
-      for (int q = lane; q < obytes / 16; q += 64)
+    if (SPL > 0 && vec_out) {
+      // a fixed number of 16-byte stores per lane (lanes past the end repeat the last chunk
+      // with the same bytes), so that waiting for the next sample's loads never has to wait
+      // for these stores as well
+      const int nchunk = obytes / 16;
+#pragma unroll
+      for (int k = 0; k < SPL; ++k) {
+        int q = k * 64 + lane;
+        q = q < nchunk ? q : nchunk - 1;
         reinterpret_cast<u32x4*>(orow)[q] = reinterpret_cast<const u32x4*>(ostage)[q];
+      }
     } else {
       for (int c = lane; c < out_stride; c += 64) orow[c] = ostage[c];
     }
@@ -165,95 +176,173 @@ __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------
-// Backward, MFMA path.  dout has the input's 16-bit type (so that S is exact) and a row
-// stride that is a multiple of 8 elements (16-byte chunks of the D + P used columns stay
-// inside the row).
-// LDS: V x D tile | gradient row | (32*NT) x D output block (pitch D*sizeof+16) | scratch.
+// Backward, MFMA path, computed transposed: dV^T = V^T S (S is symmetric), so that
+//   A = V^T  (lane: one dimension d, 8 consecutive vectors)  -> one 16-byte LDS read,
+//   B = S    (lane: one vector v, 8 consecutive vectors)     -> rebuilt from the gradient row,
+//   C = dV^T (lane: one vector v, runs of 4 consecutive d)   -> 8-byte LDS writes.
+// A workgroup of 4 wavefronts works on one sample at a time (grid-strided over samples,
+// the next sample's loads issued before the current one is computed).  Loading: every
+// thread takes pairs of rows of one 8-element column block (2 x 16-byte loads), interleaves
+// them into 8 two-vector words and writes those into V^T.  Compute: the 32 x 32 output
+// tiles (vector tile, dimension tile) are dealt round-robin to the 4 wavefronts.  Store:
+// all threads write the V x D block with 16-byte stores; dx0 = G[0:D) + dV_0 is formed
+// there from an fp32 copy of dV_0.  dout has the input's 16-bit type (S is then exact).
+// LDS: V^T [D][VP] | gradient row | VP x D output block | dV_0 in fp32 | scratch slot.
+// UPT: row pairs per thread; GPT: gradient-row chunks per thread held in registers
+// (0: loaded straight into LDS when the sample starts); KSM: K steps (>= KS).
 // ---------------------------------------------------------------------------------------
-template <class IT, class GT, int NQ, int KSM>
-__global__ __launch_bounds__(64) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
-                                                     const uint16_t* __restrict__ emb, int B, int F,
-                                                     int D, const uint16_t* __restrict__ dout,
-                                                     int out_stride, typename GT::S* __restrict__ dx0,
-                                                     typename GT::S* __restrict__ demb) {
+template <class IT, class GT, int UPT, int GPT, int KSM>
+__global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
+                                                      const uint16_t* __restrict__ emb, int B, int F,
+                                                      int D, const uint16_t* __restrict__ dout,
+                                                      int out_stride, typename GT::S* __restrict__ dx0,
+                                                      typename GT::S* __restrict__ demb) {
   extern __shared__ uint4 smem[];
   char* lds = reinterpret_cast<char*>(smem);
   using GS = typename GT::S;
+  constexpr int GSZ = static_cast<int>(sizeof(GS));
   const int V = F + 1;
   const int P = V * (V - 1) / 2;
-  const int pitch = D * 2 + 16;
-  const int gchunks = (D + P + 7) / 8;
-  const int goff = V * pitch;
-  const uint16_t* G = reinterpret_cast<const uint16_t*>(lds + goff);
   const int NT = (V + 31) / 32;
-  const int opitch = D * static_cast<int>(sizeof(GS)) + 16;
+  const int VP = NT * 32;
+  const int DT = D / 32;
+  const int tpitch = VP * 2 + 16;
+  const int goff = D * tpitch;
+  const int gchunks = (D + P + 7) / 8;
+  const uint16_t* G = reinterpret_cast<const uint16_t*>(lds + goff);
+  const int opitch = D * GSZ + 16;
   const int ooff = goff + gchunks * 16;
-  const int trash = ooff + NT * 32 * opitch;
+  const int r0off = ooff + VP * opitch;  // dV_0, fp32
+  const int trash = r0off + D * 4;
   const int KS = (V + 15) / 16;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
-  const int tile = V * (D / 8);
-  const int total = tile + gchunks;
+  const int npairs = VP / 2;
+  const int units = npairs * (D / 8);  // (row pair, column block); row pair fastest
 
-  u32x4 r[NQ];
-  int b = blockIdx.x;
-  if (b < B) fetch_sample<NQ, true>(x0, emb, dout, out_stride, b, F, D, tile, total, r);
-  for (; b < B; b += gridDim.x) {
-    put_sample<NQ>(lds, pitch, goff, trash, D, tile, total, r);
-    if (b + static_cast<int>(gridDim.x) < B)
-      fetch_sample<NQ, true>(x0, emb, dout, out_stride, b + gridDim.x, F, D, tile, total, r);
-    __syncthreads();
-    for (int I = 0; I < NT; ++I) {
-      const int i = I * 32 + col;
-      u32x4 A[KSM];  // rows of S for the K steps of 16 vectors
+  u32x4 t[UPT][2];
+  u32x4 g[GPT > 0 ? GPT : 1];
+  auto fetch = [&](int bb) {
+    const int64_t xb = static_cast<int64_t>(bb) * D;
+    const int64_t eb = static_cast<int64_t>(bb) * F * D - D;  // row v >= 1 at eb + v * D
 #pragma unroll
-      for (int ks = 0; ks < KSM; ++ks) {
-        uint32_t w[4] = {0, 0, 0, 0};
+    for (int uu = 0; uu < UPT; ++uu) {
+      int u = uu * 256 + tid;
+      u = u < units ? u : units - 1;
+      const int c = u / npairs, rp = u - c * npairs;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = ks * 16 + half * 8 + e;
-          const bool ok = i < V && k < V && i != k;
-          const int hi = i > k ? i : k, lo = i > k ? k : i;
-          const uint32_t sv = G[ok ? D + hi * (hi - 1) / 2 + lo : 0];
-          w[e >> 1] |= (ok ? sv : 0u) << ((e & 1) * 16);
-        }
-        A[ks] = u32x4{w[0], w[1], w[2], w[3]};
+      for (int m = 0; m < 2; ++m) {
+        const int v = rp * 2 + m;
+        const int vc = v < V ? v : 0;
+        const uint16_t* src = (vc == 0 ? x0 + xb : emb + eb + static_cast<int64_t>(vc) * D) + c * 8;
+        t[uu][m] = *reinterpret_cast<const u32x4*>(src);  // rows >= V are masked in put()
       }
-      for (int N = 0; N < D / 32; ++N) {
-        f32x16 acc = {};
-        const int n = N * 32 + col;
+    }
+    if constexpr (GPT > 0) {
+      const int64_t gb = static_cast<int64_t>(bb) * out_stride;
+#pragma unroll
+      for (int gg = 0; gg < GPT; ++gg) {
+        int q = gg * 256 + tid;
+        q = q < gchunks ? q : gchunks - 1;
+        g[gg] = *reinterpret_cast<const u32x4*>(dout + gb + q * 8);
+      }
+    }
+  };
+  auto put = [&](int bb) {
+#pragma unroll
+    for (int uu = 0; uu < UPT; ++uu) {
+      const int u = uu * 256 + tid;
+      const int c = u / npairs, rp = u - c * npairs;
+      const u32x4 r0 = rp * 2 < V ? t[uu][0] : u32x4{0, 0, 0, 0};
+      const u32x4 r1 = rp * 2 + 1 < V ? t[uu][1] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // value e of both rows, row 2rp in the low half: V^T[c*8 + e][2rp .. 2rp+1]
+        const uint32_t a = r0[e >> 1], w = r1[e >> 1];
+        const uint32_t word = (e & 1) ? __builtin_amdgcn_perm(w, a, 0x07060302u)
+                                      : __builtin_amdgcn_perm(w, a, 0x05040100u);
+        const int off = u < units ? (c * 8 + e) * tpitch + rp * 4 : trash;
+        *reinterpret_cast<uint32_t*>(lds + off) = word;
+      }
+    }
+    if constexpr (GPT > 0) {
+#pragma unroll
+      for (int gg = 0; gg < GPT; ++gg) {
+        const int q = gg * 256 + tid;
+        *reinterpret_cast<u32x4*>(lds + (q < gchunks ? goff + q * 16 : trash)) = g[gg];
+      }
+    } else {
+      const uint16_t* grow = dout + static_cast<int64_t>(bb) * out_stride;
+      for (int q = tid; q < gchunks; q += 256)
+        *reinterpret_cast<u32x4*>(lds + goff + q * 16) = *reinterpret_cast<const u32x4*>(grow + q * 8);
+    }
+  };
+
+  int b = blockIdx.x;
+  if (b < B) fetch(b);
+  for (; b < B; b += gridDim.x) {
+    put(b);
+    if (b + static_cast<int>(gridDim.x) < B) fetch(b + gridDim.x);
+    __syncthreads();
+    int cur_vt = -1;
+    u32x4 Sop[KSM];  // S[v][k], k = 16 ks + 8 half + e
+    for (int tile = wave; tile < NT * DT; tile += 4) {
+      const int vt = tile / DT, dt = tile - vt * DT;
+      const int v = vt * 32 + col;
+      if (vt != cur_vt) {  // wave-uniform
+        cur_vt = vt;
 #pragma unroll
         for (int ks = 0; ks < KSM; ++ks) {
-          if (ks < KS) {
-            uint32_t w[4] = {0, 0, 0, 0};
+          uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int k = ks * 16 + half * 8 + e;
-              const uint32_t v = *reinterpret_cast<const uint16_t*>(lds + (k < V ? k : 0) * pitch + n * 2);
-              w[e >> 1] |= (k < V ? v : 0u) << ((e & 1) * 16);
-            }
-            acc = mfma32<IT>(A[ks], u32x4{w[0], w[1], w[2], w[3]}, acc);
+          for (int e = 0; e < 8; ++e) {
+            const int k = ks * 16 + half * 8 + e;
+            const bool ok = v < V && k < V && v != k;
+            const int hi = v > k ? v : k, lo = v > k ? k : v;
+            const uint32_t sv = G[ok ? D + hi * (hi - 1) / 2 + lo : 0];
+            w[e >> 1] |= (ok ? sv : 0u) << ((e & 1) * 16);
           }
+          Sop[ks] = u32x4{w[0], w[1], w[2], w[3]};
         }
-        const float g0 = IT::to_f(G[n]);
+      }
+      f32x16 acc = {};
+      const char* arow = lds + (dt * 32 + col) * tpitch + half * 16;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int vi = I * 32 + acc_row(rr, lane);  // rows >= V land in unused output rows
-          const float v = vi == 0 ? g0 + acc[rr] : acc[rr];
-          *reinterpret_cast<GS*>(lds + ooff + vi * opitch + n * static_cast<int>(sizeof(GS))) = GT::from_f(v);
-        }
+      for (int ks = 0; ks < KSM; ++ks)
+        if (ks < KS) acc = mfma32<IT>(*reinterpret_cast<const u32x4*>(arow + ks * 32), Sop[ks], acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = dt * 32 + q * 8 + half * 4;
+        float f[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        store_n<GT, 4>(reinterpret_cast<GS*>(lds + ooff + v * opitch + d0 * GSZ), f);
+        if (v == 0) store_n<F32T, 4>(reinterpret_cast<float*>(lds + r0off + d0 * 4), f);
       }
     }
     __syncthreads();
-    // row 0 -> dx0[b], rows 1.. -> demb[b] (contiguous), 16-byte stores
-    const int nv = D * static_cast<int>(sizeof(GS)) / 16;
-    char* dxrow = reinterpret_cast<char*>(dx0 + static_cast<int64_t>(b) * D);
-    char* derow = reinterpret_cast<char*>(demb + static_cast<int64_t>(b) * F * D) - nv * 16;
-    for (int q = lane; q < V * nv; q += 64) {
-      const int row = q / nv, c = q - row * nv;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + ooff + row * opitch + c * 16);
-      char* dst = row == 0 ? dxrow + c * 16 : derow + static_cast<int64_t>(q) * 16;
-      *reinterpret_cast<u32x4*>(dst) = v;
+    // rows 1.. -> demb[b] (contiguous), row 0 -> dx0[b] = G[0:D) + dV_0; 16-byte stores.
+    // Every thread issues a fixed number of stores (threads past the end repeat the last
+    // chunk with the same bytes), so that waiting for the next sample's loads never has to
+    // wait for these stores as well.
+    const int nv = D * GSZ / 16;
+    const int nchunk = (V - 1) * nv;
+    char* derow = reinterpret_cast<char*>(demb + static_cast<int64_t>(b) * F * D);
+#pragma unroll
+    for (int k = 0; k < UPT * GSZ; ++k) {
+      int q = k * 256 + tid;
+      q = q < nchunk ? q : nchunk - 1;
+      const int row = q / nv + 1, c = q - (row - 1) * nv;
+      *reinterpret_cast<uint4*>(derow + static_cast<int64_t>(q) * 16) =
+          *reinterpret_cast<const uint4*>(lds + ooff + row * opitch + c * 16);
+    }
+    constexpr int EPC = 16 / GSZ;  // elements per 16-byte chunk of the gradient
+    {
+      const int q = tid < nv ? tid : nv - 1;
+      float f[EPC];
+#pragma unroll
+      for (int x = 0; x < EPC; ++x)
+        f[x] = reinterpret_cast<const float*>(lds + r0off)[q * EPC + x] + IT::to_f(G[q * EPC + x]);
+      store_n<GT, EPC>(dx0 + static_cast<int64_t>(b) * D + q * EPC, f);
     }
   }
 }
@@ -347,14 +436,58 @@ int grid_for(int B, size_t lds_bytes) {
   return B < g ? B : g;
 }
 
-template <class IT, class OT, int NQ>
+// One-wavefront workgroups that loop over samples: launch as many as can be resident at
+// once (occupancy from the kernel's registers and LDS), never more than there are samples.
+int resident_grid(const void* kernel, int B, size_t lds_bytes, int block = 64) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({kernel, lds_bytes});
+    if (it != cache.end()) {
+      per_cu = it->second;
+    } else {
+      int n = 0, cus = 0, dev = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds_bytes) != hipSuccess) n = 4;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+      per_cu = (n > 0 ? n : 1) * (cus > 0 ? cus : 256);
+      cache[{kernel, lds_bytes}] = per_cu;
+    }
+  }
+  return B < per_cu ? B : per_cu;
+}
+
+template <class IT, class OT, int NQ, int SPL>
+el_status launch_fwd_t(const void* x0, const void* emb, int B, int F, int D, void* out,
+                       int out_stride, size_t lds, hipStream_t stream) {
+  const int vec_out = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S)) % 16 == 0;
+  auto kern = k_dot_fwd_mfma<IT, OT, NQ, SPL>;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds)), dim3(64),
+                     lds, stream, static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B,
+                     F, D, static_cast<typename OT::S*>(out), out_stride, vec_out);
+  return check_launch("dot_interact_fwd");
+}
+
+// Shape classes of the MFMA forward: input chunks per lane (NQ) and output-row chunks per
+// lane (SPL; 0 = a loop of run-time length).
+template <class IT, class OT>
 el_status launch_fwd_mfma(const void* x0, const void* emb, int B, int F, int D, void* out,
                           int out_stride, size_t lds, hipStream_t stream) {
-  const int vec_out = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S)) % 16 == 0;
-  hipLaunchKernelGGL((k_dot_fwd_mfma<IT, OT, NQ>), dim3(grid_for(B, lds)), dim3(64), lds, stream,
-                     static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B, F, D,
-                     static_cast<typename OT::S*>(out), out_stride, vec_out);
-  return check_launch("dot_interact_fwd");
+  const int chunks = (F + 1) * (D / 8);
+  const int64_t ochunks = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S) + 15) / 16;
+  if (chunks <= 8 * 64) {
+    if (ochunks <= 64) return launch_fwd_t<IT, OT, 8, 1>(x0, emb, B, F, D, out, out_stride, lds, stream);
+    if (ochunks <= 4 * 64) return launch_fwd_t<IT, OT, 8, 4>(x0, emb, B, F, D, out, out_stride, lds, stream);
+    return launch_fwd_t<IT, OT, 8, 0>(x0, emb, B, F, D, out, out_stride, lds, stream);
+  }
+  if (chunks <= 16 * 64) {
+    if (ochunks <= 16 * 64) return launch_fwd_t<IT, OT, 16, 16>(x0, emb, B, F, D, out, out_stride, lds, stream);
+    return launch_fwd_t<IT, OT, 16, 0>(x0, emb, B, F, D, out, out_stride, lds, stream);
+  }
+  return launch_fwd_t<IT, OT, 32, 0>(x0, emb, B, F, D, out, out_stride, lds, stream);
 }
 
 template <class IT, class OT>
@@ -366,9 +499,7 @@ el_status fwd_typed(const void* x0, const void* emb, int B, int F, int D, void* 
     const size_t lds = static_cast<size_t>(V) * (D * 2 + 16) + ost + 16;
     const int chunks = V * (D / 8);
     if (D % 16 == 0 && V <= 128 && lds <= kMaxLds && chunks <= 32 * 64) {
-      if (chunks <= 8 * 64) return launch_fwd_mfma<IT, OT, 8>(x0, emb, B, F, D, out, out_stride, lds, stream);
-      if (chunks <= 16 * 64) return launch_fwd_mfma<IT, OT, 16>(x0, emb, B, F, D, out, out_stride, lds, stream);
-      return launch_fwd_mfma<IT, OT, 32>(x0, emb, B, F, D, out, out_stride, lds, stream);
+      return launch_fwd_mfma<IT, OT>(x0, emb, B, F, D, out, out_stride, lds, stream);
     }
   }
   const size_t lds = static_cast<size_t>(V) * D * 4;
@@ -380,24 +511,39 @@ el_status fwd_typed(const void* x0, const void* emb, int B, int F, int D, void* 
   return check_launch("dot_interact_fwd");
 }
 
-template <class IT, class GT, int NQ, int KSM>
-el_status launch_bwd_ks(const void* x0, const void* emb, int B, int F, int D, const void* dout,
-                        int out_stride, void* dx0, void* demb, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((k_dot_bwd_mfma<IT, GT, NQ, KSM>), dim3(grid_for(B, lds)), dim3(64), lds, stream,
-                     static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B, F, D,
-                     static_cast<const uint16_t*>(dout), out_stride,
-                     static_cast<typename GT::S*>(dx0), static_cast<typename GT::S*>(demb));
+template <class IT, class GT, int UPT, int GPT, int KSM>
+el_status launch_bwd_t(const void* x0, const void* emb, int B, int F, int D, const void* dout,
+                       int out_stride, void* dx0, void* demb, size_t lds, hipStream_t stream) {
+  auto kern = k_dot_bwd_mfma<IT, GT, UPT, GPT, KSM>;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 256)),
+                     dim3(256), lds, stream, static_cast<const uint16_t*>(x0),
+                     static_cast<const uint16_t*>(emb), B, F, D, static_cast<const uint16_t*>(dout),
+                     out_stride, static_cast<typename GT::S*>(dx0), static_cast<typename GT::S*>(demb));
   return check_launch("dot_interact_bwd");
 }
 
-// K steps of the S V product: one per 16 vectors
-template <class IT, class GT, int NQ>
+// Shape classes of the MFMA backward: K steps (vectors per sample), row pairs per thread,
+// gradient-row chunks per thread.  EL_ERR_UNSUPPORTED for shapes outside them.
+template <class IT, class GT>
 el_status launch_bwd_mfma(const void* x0, const void* emb, int B, int F, int D, const void* dout,
                           int out_stride, void* dx0, void* demb, size_t lds, hipStream_t stream) {
   const int V = F + 1;
-  if (V <= 32) return launch_bwd_ks<IT, GT, NQ, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-  if (V <= 64) return launch_bwd_ks<IT, GT, NQ, 4>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-  return launch_bwd_ks<IT, GT, NQ, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+  const int VP = (V + 31) / 32 * 32;
+  const int units = VP / 2 * (D / 8);
+  const int gchunks = (D + V * (V - 1) / 2 + 7) / 8;
+  if (V <= 32) {
+    if (units <= 256 && gchunks <= 256)
+      return launch_bwd_t<IT, GT, 1, 1, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 512 && gchunks <= 512)
+      return launch_bwd_t<IT, GT, 2, 2, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+  } else if (V <= 64) {
+    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 4>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 4>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+  } else if (V <= 128) {
+    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+  }
+  return EL_ERR_UNSUPPORTED;
 }
 
 template <class IT, class DT, class GT>
@@ -407,16 +553,13 @@ el_status bwd_typed(const void* x0, const void* emb, int B, int F, int D, const 
   const int64_t P = static_cast<int64_t>(V) * (V - 1) / 2;
   if constexpr (sizeof(typename IT::S) == 2 && IT::code == DT::code) {
     const int64_t gchunks = (D + P + 7) / 8;
-    const size_t lds = static_cast<size_t>(V) * (D * 2 + 16) + gchunks * 16 +
-                       static_cast<size_t>((V + 31) / 32 * 32) * (D * sizeof(typename GT::S) + 16) + 16;
-    const int64_t chunks = static_cast<int64_t>(V) * (D / 8) + gchunks;
+    const size_t VP = static_cast<size_t>((V + 31) / 32 * 32);
+    const size_t lds = static_cast<size_t>(D) * (VP * 2 + 16) + gchunks * 16 +
+                       VP * (D * sizeof(typename GT::S) + 16) + static_cast<size_t>(D) * 4 + 16;
     // 16-byte chunks of the gradient row must stay inside the row: stride multiple of 8
-    if (D % 32 == 0 && V <= 128 && lds <= kMaxLds && out_stride % 8 == 0 && chunks <= 32 * 64) {
-      if (chunks <= 8 * 64)
-        return launch_bwd_mfma<IT, GT, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-      if (chunks <= 16 * 64)
-        return launch_bwd_mfma<IT, GT, 16>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-      return launch_bwd_mfma<IT, GT, 32>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (D % 32 == 0 && V <= 128 && lds <= kMaxLds && out_stride % 8 == 0) {
+      const el_status st = launch_bwd_mfma<IT, GT>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+      if (st != EL_ERR_UNSUPPORTED) return st;
     }
   }
   const size_t lds = (static_cast<size_t>(V) * D + D + P) * 4;
