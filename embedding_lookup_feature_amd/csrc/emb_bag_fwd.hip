@@ -4,19 +4,31 @@
 // feature; the embedding vector of a sample for a table is here the sum of the rows its
 // bag names (hotness 1 = one row).  Bags are table-major (bag g = t*B + b).
 //
-// Mapping.  A wavefront owns a batch of 64 consecutive bags.  Lane i first streams in the
-// CSR bounds of bag i and its first index with non-temporal loads (coalesced, read once).
-// The wave is cut into groups of L lanes; a group covers one table row with 16-byte
-// loads (L = row bytes / 16, rounded up to a power of two).  The groups then walk the 64
-// bags in rounds; U rounds are issued back to back so that U independent row loads per
-// lane are in flight before the first is consumed (for hotness-1 bags this is the whole
-// gather).  Further entries of a bag follow in ascending CSR order, 4 loads in flight.
-// Sums are fp32 in CSR order and rounded once to the output type, so a hotness-1 gather
-// returns the row itself (bit-exact copy up to the output rounding).
+// Mapping.  A wavefront gathers NB = NG * U consecutive bags in one pass and exits: the
+// wave is cut into NG groups of L lanes (L = row bytes / 16, rounded up to a power of two;
+// a group covers one row with 16-byte loads) and every group pools U bags.
+//   1. lane i < NB streams in the CSR bounds of bag i and the first row of its table
+//      (independent loads, one round trip), then the bag's first index;
+//   2. every group issues the first-row loads of its U bags back to back, so U row loads
+//      per lane are in flight (for hotness-1 bags this is the whole gather); later entries
+//      of multi-hot bags follow in ascending CSR order, 4 loads in flight;
+//   3. all NB pooled rows are stored at the end.
+// A wave never waits for its own stores (on this architecture loads and stores share one
+// completion counter), and a new wave takes its slot as soon as it is done.  Sums are fp32
+// in CSR order and rounded once to the output type, so a hotness-1 gather returns the row
+// itself (bit-exact up to the output rounding).
 #include "el_internal.hpp"
 
 namespace el {
 namespace {
+
+template <int L, int NVL>
+constexpr int bags_per_group() {
+  constexpr int NG = 64 / L;
+  constexpr int byreg = 16 / NVL;  // keep U * NVL 16-byte vectors <= 16 per lane
+  constexpr int u = 64 / NG < 8 ? 64 / NG : 8;
+  return u < byreg ? u : byreg;
+}
 
 template <class TT, class OT, int L, int NVL>
 __global__ __launch_bounds__(256) void k_emb_bag_fwd(
@@ -24,91 +36,107 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ off, int32_t B, int32_t F,
     int32_t D, int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int32_t nbags) {
   constexpr int E = epv<TT>();
-  constexpr int NG = 64 / L;  // bag groups per wave
-  constexpr int R = 64 / NG;  // rounds to cover the wave's 64 bags
-  constexpr int U0 = 8 / NVL;
-  constexpr int U = R < U0 ? R : U0;  // rounds issued together
+  constexpr int NG = 64 / L;                  // bag groups per wave
+  constexpr int U = bags_per_group<L, NVL>();  // bags per group
+  constexpr int NB = NG * U;                  // bags per wave
 
   const int lane = threadIdx.x & 63;
   const int grp = lane / L;
   const int gl = lane % L;
   const int blk = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t g0l = (static_cast<int64_t>(blk) * 4 + (threadIdx.x >> 6)) * 64;
+  const int64_t g0l = (static_cast<int64_t>(blk) * 4 + (threadIdx.x >> 6)) * NB;
   if (g0l >= nbags) return;
   const int g0 = static_cast<int>(g0l);  // < nbags < 2^31
 
-  int s = 0, e = 0, r0 = 0;
-  if (g0l + lane < nbags) {
-    s = ld_stream(off + g0 + lane);
-    e = ld_stream(off + g0 + lane + 1);
-    if (e > s) r0 = ld_stream(idx + s);
+  // 1. per-lane bag metadata (lanes < NB): bounds, table, table base; then the first index
+  int s = 0, e = 0, r0 = 0, t = -1, b = 0, nt = 1;
+  int64_t base = 0;
+  if (lane < NB && g0l + lane < nbags) {
+    const int g = g0 + lane;
+    t = g / B;
+    b = g - t * B;
+    s = ld_stream(off + g);
+    e = ld_stream(off + g + 1);
+    base = row_off[t];
+    if (hash) nt = static_cast<int32_t>(row_off[t + 1] - base);
+  }
+  if (e > s) {
+    r0 = ld_stream(idx + s);
+    if (hash) r0 = floor_mod(r0, nt);
   }
 
-  for (int j0 = 0; j0 < R; j0 += U) {
-    uint4 v[U][NVL];
-    int bs[U], be[U], tt[U], bb[U], nt[U];
-    int64_t base[U];
+  // 2. first rows of the group's U bags, all in flight together
+  uint4 v[U][NVL];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bi = (j0 + u) * NG + grp;
-      bs[u] = __shfl(s, bi);
-      be[u] = __shfl(e, bi);
-      int r = __shfl(r0, bi);
-      const bool ok = g0l + bi < nbags;
-      const int g = ok ? g0 + bi : 0;
-      const int t = ok ? g / B : 0;
-      tt[u] = ok ? t : -1;
-      bb[u] = g - t * B;
-      base[u] = ok ? row_off[t] : 0;
-      nt[u] = (ok && hash) ? static_cast<int32_t>(row_off[t + 1] - base[u]) : 1;
-      const bool has = ok && be[u] > bs[u];
-      if (hash) r = floor_mod(r, nt[u]);
-      const typename TT::S* row = W + (base[u] + r) * D;
+  for (int u = 0; u < U; ++u) {
+    const int bi = u * NG + grp;
+    const int bs = __shfl(s, bi), be = __shfl(e, bi), r = __shfl(r0, bi);
+    const int64_t bse = __shfl(base, bi);
+    const typename TT::S* row = W + (bse + r) * D;
 #pragma unroll
-      for (int m = 0; m < NVL; ++m) {
-        const int c = gl + m * L;
-        v[u][m] = (has && c < nvec) ? load16<TT>(row + c * E) : uint4{0, 0, 0, 0};
+    for (int m = 0; m < NVL; ++m) {
+      v[u][m] = uint4{0, 0, 0, 0};
+      const int c = gl + m * L;
+      if (be > bs && c < nvec) v[u][m] = load16<TT>(row + c * E);
+    }
+  }
+  float acc[U][NVL][E];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int m = 0; m < NVL; ++m) unpack16<TT>(v[u][m], acc[u][m]);
+
+  //    further entries of multi-hot bags, in CSR order
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int bi = u * NG + grp;
+    const int bs = __shfl(s, bi), be = __shfl(e, bi), ntb = __shfl(nt, bi);
+    const int64_t bse = __shfl(base, bi);
+    for (int k = bs + 1; k < be; k += 4) {
+      // indices and rows of the next 4 entries, all loads issued before any is used
+      // (entries past the bag end re-read its last entry and are not added)
+      int r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        r[q] = idx[k + q < be ? k + q : be - 1];
+        if (hash) r[q] = floor_mod(r[q], ntb);
+      }
+      uint4 w[4][NVL];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const typename TT::S* row = W + (bse + r[q]) * D;
+#pragma unroll
+        for (int m = 0; m < NVL; ++m) {
+          const int c = gl + m * L;
+          w[q][m] = load16<TT>(row + (c < nvec ? c : nvec - 1) * E);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (k + q < be) {
+#pragma unroll
+          for (int m = 0; m < NVL; ++m) {
+            float f[E];
+            unpack16<TT>(w[q][m], f);
+#pragma unroll
+            for (int x = 0; x < E; ++x) acc[u][m][x] += f[x];
+          }
+        }
       }
     }
+  }
+
+  // 3. store every pooled row
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (tt[u] < 0) continue;
-      float acc[NVL][E];
-#pragma unroll
-      for (int m = 0; m < NVL; ++m) unpack16<TT>(v[u][m], acc[m]);
-      for (int k = bs[u] + 1; k < be[u]; k += 4) {
-        uint4 w[4][NVL];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (k + q < be[u]) {
-            int r = idx[k + q];
-            if (hash) r = floor_mod(r, nt[u]);
-            const typename TT::S* row = W + (base[u] + r) * D;
-#pragma unroll
-            for (int m = 0; m < NVL; ++m) {
-              const int c = gl + m * L;
-              w[q][m] = c < nvec ? load16<TT>(row + c * E) : uint4{0, 0, 0, 0};
-            }
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if (k + q < be[u]) {
-#pragma unroll
-            for (int m = 0; m < NVL; ++m) {
-              float f[E];
-              unpack16<TT>(w[q][m], f);
-#pragma unroll
-              for (int x = 0; x < E; ++x) acc[m][x] += f[x];
-            }
-          }
-        }
-      }
-      typename OT::S* dst = out + (static_cast<int64_t>(bb[u]) * F + tt[u]) * D;
+  for (int u = 0; u < U; ++u) {
+    const int bi = u * NG + grp;
+    const int tb = __shfl(t, bi), bb = __shfl(b, bi);
+    if (tb >= 0) {
+      typename OT::S* dst = out + (static_cast<int64_t>(bb) * F + tb) * D;
 #pragma unroll
       for (int m = 0; m < NVL; ++m) {
         const int c = gl + m * L;
-        if (c < nvec) store_n<OT, E>(dst + c * E, acc[m]);
+        if (c < nvec) store_n<OT, E>(dst + c * E, acc[u][m]);
       }
     }
   }
@@ -117,8 +145,9 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
 template <class TT, class OT, int L, int NVL>
 el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
                    int nvec, hipStream_t stream) {
+  constexpr int NB = (64 / L) * bags_per_group<L, NVL>();
   const int64_t nbags = static_cast<int64_t>(tab.num_tables) * bags.batch;
-  const int64_t waves = (nbags + 63) / 64;
+  const int64_t waves = (nbags + NB - 1) / NB;
   const int blocks = round_up8((waves + 3) / 4);
   hipLaunchKernelGGL((k_emb_bag_fwd<TT, OT, L, NVL>), dim3(blocks), dim3(256), 0, stream,
                      static_cast<const typename TT::S*>(tab.base), tab.row_offset, bags.indices,
