@@ -139,13 +139,17 @@ struct GradWorkspace {
   uint32_t* scan_level[4][2] = {};  // per scan level: tile sums, scanned tile sums
   float *head = nullptr, *tail = nullptr;
   uint32_t *through = nullptr, *owner = nullptr;
+  int64_t nblk = 0;             // blocks of kBlockChunks chunks
+  float* bsum = nullptr;        // per block: sum of its chunks' head partials (fully "through" blocks)
+  uint32_t* bthrough = nullptr;  // per block: 1 if every chunk of the block is "through"
 };
 
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
-constexpr int kChunk = 64;       // lookups per reduce chunk
+constexpr int kChunk = 16;       // lookups per reduce chunk
+constexpr int kBlockChunks = 64;  // chunks per fix-up block
 
 // Lay out the workspace in `base` (nullptr: only compute the size).
 GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* base);

@@ -247,6 +247,9 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
   ws.tail = static_cast<float*>(take(sizeof(float) * ws.nchunks * D));
   ws.through = static_cast<uint32_t*>(take(4 * ws.nchunks));
   ws.owner = static_cast<uint32_t*>(take(4 * ws.nchunks));
+  ws.nblk = (ws.nchunks + kBlockChunks - 1) / kBlockChunks;
+  ws.bsum = static_cast<float*>(take(sizeof(float) * ws.nblk * D));
+  ws.bthrough = static_cast<uint32_t*>(take(4 * ws.nblk));
   ws.bytes = off;
   return ws;
 }
