@@ -19,10 +19,11 @@
 //                 (loads and stores share one completion counter on this architecture).
 //   k_seg_blocksum : for every block of 64 chunks that one run covers entirely ("through"
 //                 chunks only), the sum of their head partials.
-//   k_seg_fixup : one wavefront per owning chunk finds where its run ends (first chunk after
-//                 it that is not "through", skipping whole "through" blocks), adds tail +
-//                 head partials + block sums in a fixed order with 32 loads in flight, and
-//                 updates the row.
+//   k_seg_fixup : one wavefront per 64 chunks.  An owning chunk's run ends at the first
+//                 chunk after it that is not "through"; runs ending within a few chunks are
+//                 finished by small lane groups side by side (tail + head partials in chunk
+//                 order), longer ones by the whole wavefront, skipping whole "through"
+//                 blocks via their block sums.
 // Every sum has a fixed association, so results are bitwise reproducible; nothing uses
 // atomics and every row is written by exactly one lane group.
 #include <type_traits>
@@ -284,22 +285,17 @@ __device__ inline int64_t first_zero(const uint32_t* __restrict__ flag, int64_t 
   }
 }
 
-// One wavefront per chunk that owns a run crossing its end: total = tail partial + head
+// Row update of a long run owned by chunk c (whole wavefront): total = tail partial + head
 // partials of the chunks up to the one where the run ends, taking whole "through" blocks
-// from their block sums.  Then the row update.
+// from their block sums.
 template <class WT, int LF, int NV>
-__global__ __launch_bounds__(256) void k_seg_fixup(
-    const uint32_t* __restrict__ keys, int64_t n, int64_t nchunks, int32_t D, int32_t nv4,
-    typename WT::S* __restrict__ W, float lr, const float* __restrict__ head,
-    const float* __restrict__ tail, const uint32_t* __restrict__ through,
-    const uint32_t* __restrict__ owner, const float* __restrict__ bsum,
-    const uint32_t* __restrict__ bthrough, int64_t nblk) {
+__device__ inline void fix_long(int64_t c, uint32_t key, int64_t nchunks, int32_t D, int32_t nv4,
+                                typename WT::S* __restrict__ W, float lr,
+                                const float* __restrict__ head, const float* __restrict__ tail,
+                                const uint32_t* __restrict__ through, const float* __restrict__ bsum,
+                                const uint32_t* __restrict__ bthrough, int64_t nblk) {
   const int lane = threadIdx.x & 63;
   const int gl = lane % LF;
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (c >= nchunks || owner[c] == 0) return;  // wave-uniform
-  const int64_t last = (c + 1) * CH < n ? (c + 1) * CH : n;
-  const uint32_t key = keys[last - 1];
   typename Raw4<WT>::type wold[NV];
 #pragma unroll
   for (int m = 0; m < NV; ++m) {
@@ -312,7 +308,6 @@ __global__ __launch_bounds__(256) void k_seg_fixup(
     const int v = gl + m * LF;
     unpack16<F32T>(*reinterpret_cast<const uint4*>(tail + c * D + (v < nv4 ? v : nv4 - 1) * 4), tot[m]);
   }
-
   // where does the run end?  first a window of 64 chunks, then whole blocks
   const int64_t cw = first_zero(through, c + 1, c + 65 < nchunks ? c + 65 : nchunks);
   if (cw < c + 65 && cw < nchunks && through[cw] == 0) {
@@ -336,6 +331,94 @@ __global__ __launch_bounds__(256) void k_seg_fixup(
   }
 }
 
+// One wavefront per 64 consecutive chunks.  Ballots give the "owner" and "through" flags of
+// its chunks (and of the 64 after them), so every owning chunk sees at once where its run
+// ends.  Runs ending at most S chunks after their owner ("short", the common case) are
+// finished by lane groups of LG lanes, 64/LG owners side by side: the group loads the tail
+// partial, the S head partials (clamped to the end chunk) and the table row together, adds
+// them in chunk order and updates the row.  Longer runs are then finished one after the
+// other by the whole wavefront (fix_long).
+template <class WT, int LG, int NVG, int S, int LF, int NV>
+__global__ __launch_bounds__(256) void k_seg_fixup(
+    const uint32_t* __restrict__ keys, int64_t n, int64_t nchunks, int32_t D, int32_t nv4,
+    typename WT::S* __restrict__ W, float lr, const float* __restrict__ head,
+    const float* __restrict__ tail, const uint32_t* __restrict__ through,
+    const uint32_t* __restrict__ owner, const float* __restrict__ bsum,
+    const uint32_t* __restrict__ bthrough, int64_t nblk) {
+  constexpr int NGW = 64 / LG;  // owner groups per wavefront
+  const int lane = threadIdx.x & 63;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 64;
+  if (c0 >= nchunks) return;  // wave-uniform
+  const int64_t cl = c0 + lane, ch = c0 + 64 + lane;
+  const bool own = cl < nchunks && owner[cl] != 0;
+  const uint64_t tm0 = __ballot(cl < nchunks && through[cl] != 0);
+  const uint64_t tm1 = __ballot(ch < nchunks && through[ch] != 0);
+  // row of this lane's chunk (the last key of the chunk: the run it owns)
+  const int64_t lastpos = (cl + 1) * CH < n ? (cl + 1) * CH : n;
+  const uint32_t keyl = cl < nchunks ? keys[lastpos - 1] : 0u;
+  // end chunk (relative to c0) of the run owned by chunk cl: first non-"through" chunk after it
+  int e = 128;
+  {
+    const uint64_t z0 = lane < 63 ? (~tm0 & (~0ull << (lane + 1))) : 0ull;
+    if (z0) e = __ffsll(static_cast<unsigned long long>(z0)) - 1;
+    else if (~tm1) e = 64 + __ffsll(static_cast<unsigned long long>(~tm1)) - 1;
+  }
+  const bool is_short = own && e - lane <= S;
+  const uint64_t ms = __ballot(is_short);
+  uint64_t ml = __ballot(own && !is_short);
+  const int ns = __popcll(ms);
+  // ranks: short owners first in chunk order, then every other lane (a permutation of lanes)
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int rank = is_short ? __popcll(ms & lt) : ns + __popcll(~ms & lt);
+  // lane r receives the lane index of the owner of rank r
+  const int who = __builtin_amdgcn_ds_permute(rank * 4, lane);
+  const int grp = lane / LG, gl = lane % LG;
+  for (int r0 = 0; r0 < ns; r0 += NGW) {  // wave-uniform trip count
+    const int R = r0 + grp;
+    const int i = __shfl(who, R < ns ? R : 0);
+    const int ei = __shfl(e, i);
+    const uint32_t key = static_cast<uint32_t>(__shfl(static_cast<int>(keyl), i));
+    if (R < ns) {  // group-uniform
+      const int64_t c = c0 + i, ce = c0 + ei;  // c < ce <= c + S
+      typename Raw4<WT>::type wold[NVG];
+      uint4 tl[NVG], hd[S][NVG];
+#pragma unroll
+      for (int m = 0; m < NVG; ++m) {
+        const int v = gl + m * LG;
+        const int vo = (v < nv4 ? v : nv4 - 1) * 4;
+        wold[m] = load4_raw<WT>(W + static_cast<int64_t>(key) * D + vo);
+        tl[m] = *reinterpret_cast<const uint4*>(tail + c * D + vo);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          const int64_t cc = c + 1 + j <= ce ? c + 1 + j : ce;
+          hd[j][m] = *reinterpret_cast<const uint4*>(head + cc * D + vo);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < NVG; ++m) {
+        const int v = gl + m * LG;
+        float tot[4], f[4];
+        unpack16<F32T>(tl[m], tot);
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+          if (c + 1 + j <= ce) {
+            unpack16<F32T>(hd[j][m], f);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) tot[x] += f[x];
+          }
+        }
+        if (v < nv4) sgd4<WT>(W + static_cast<int64_t>(key) * D + v * 4, wold[m], tot, lr);
+      }
+    }
+  }
+  while (ml) {  // wave-uniform
+    const int i = __ffsll(static_cast<unsigned long long>(ml)) - 1;
+    ml &= ml - 1;
+    const uint32_t key = static_cast<uint32_t>(__shfl(static_cast<int>(keyl), i));
+    fix_long<WT, LF, NV>(c0 + i, key, nchunks, D, nv4, W, lr, head, tail, through, bsum, bthrough, nblk);
+  }
+}
+
 int blocks_for(int64_t n, int per) { return static_cast<int>((n + per - 1) / per); }
 
 template <class GT, class WT, int L, int NV>
@@ -349,7 +432,7 @@ el_status chunk_t(const el_tables& tab, const el_bags& bags, const GradWorkspace
   return check_launch("segment_reduce");
 }
 
-template <class WT, int LF, int NV>
+template <class WT, int LG, int NVG, int S, int LF, int NV>
 el_status fixup_t(const el_tables& tab, const GradWorkspace& ws, const uint32_t* keys, float lr,
                   int nv4, hipStream_t stream) {
   hipLaunchKernelGGL((k_seg_blocksum<LF, NV>), dim3(blocks_for(ws.nblk, 4)), dim3(256), 0, stream,
@@ -357,7 +440,8 @@ el_status fixup_t(const el_tables& tab, const GradWorkspace& ws, const uint32_t*
                      ws.nchunks, ws.nblk, tab.dim, nv4, ws.bsum, ws.bthrough);
   el_status st = check_launch("segment_blocksum");
   if (st != EL_OK) return st;
-  hipLaunchKernelGGL((k_seg_fixup<WT, LF, NV>), dim3(blocks_for(ws.nchunks, 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL((k_seg_fixup<WT, LG, NVG, S, LF, NV>), dim3(blocks_for(ws.nchunks, 256)), dim3(256),
+                     0, stream,
                      keys, ws.n, ws.nchunks, tab.dim, nv4, static_cast<typename WT::S*>(tab.base), lr,
                      static_cast<const float*>(ws.head), static_cast<const float*>(ws.tail),
                      static_cast<const uint32_t*>(ws.through), static_cast<const uint32_t*>(ws.owner),
@@ -380,14 +464,16 @@ el_status reduce_typed(const el_tables& tab, const el_bags& bags, const GradWork
   else if (nv4 <= 128) st = chunk_t<GT, WT, 64, 2>(tab, bags, ws, keys, vals, demb, lr, nv4, stream);
   else return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim > 512 is not supported");
   if (st != EL_OK) return st;
-  if (nv4 <= 1) return fixup_t<WT, 1, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 2) return fixup_t<WT, 2, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 4) return fixup_t<WT, 4, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 8) return fixup_t<WT, 8, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 16) return fixup_t<WT, 16, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 32) return fixup_t<WT, 32, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 64) return fixup_t<WT, 64, 1>(tab, ws, keys, lr, nv4, stream);
-  return fixup_t<WT, 64, 2>(tab, ws, keys, lr, nv4, stream);
+  // fix-up: short runs by groups of LG lanes (NVG vectors each, S head partials in flight),
+  // long runs by the wavefront (LF lanes per row, NV vectors each)
+  if (nv4 <= 1) return fixup_t<WT, 1, 1, 8, 1, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 2) return fixup_t<WT, 2, 1, 8, 2, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 4) return fixup_t<WT, 4, 1, 8, 4, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 8) return fixup_t<WT, 8, 1, 8, 8, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 16) return fixup_t<WT, 16, 1, 8, 16, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 32) return fixup_t<WT, 16, 2, 8, 32, 1>(tab, ws, keys, lr, nv4, stream);
+  if (nv4 <= 64) return fixup_t<WT, 16, 4, 4, 64, 1>(tab, ws, keys, lr, nv4, stream);
+  return fixup_t<WT, 32, 4, 4, 64, 2>(tab, ws, keys, lr, nv4, stream);
 }
 
 template <class GT>
