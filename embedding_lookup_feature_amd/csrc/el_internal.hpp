@@ -130,11 +130,13 @@ el_status launch_dot_bwd(const void* x0, const void* emb, el_dtype in_dtype, int
 struct GradWorkspace {
   int64_t n = 0;        // lookups
   int passes = 0;       // radix passes
+  int rbits = 0;        // digit width of every pass
   int64_t nblocks = 0;  // radix tiles
   int64_t nchunks = 0;  // reduce chunks
   size_t bytes = 0;
   uint32_t *keys0 = nullptr, *vals0 = nullptr, *keys1 = nullptr, *vals1 = nullptr;
-  uint32_t *hist = nullptr, *hist_scan = nullptr;
+  uint32_t *hist = nullptr, *hist_scan = nullptr;  // digit-major tile counts, scanned per digit
+  uint32_t* dtotal = nullptr;                       // per digit: keys with that digit
   uint32_t *flags = nullptr, *flags_scan = nullptr;
   uint32_t* scan_level[4][2] = {};  // per scan level: tile sums, scanned tile sums
   float *head = nullptr, *tail = nullptr;
@@ -144,8 +146,7 @@ struct GradWorkspace {
   uint32_t* bthrough = nullptr;  // per block: 1 if every chunk of the block is "through"
 };
 
-constexpr int kRadixBits = 8;
-constexpr int kRadix = 1 << kRadixBits;
+constexpr int kRadixBits = 8;  // widest radix digit
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
 constexpr int kChunk = 16;       // lookups per reduce chunk

@@ -6,11 +6,12 @@
 // Sorting the (row, bag) pairs by row puts all contributions to one row next to each
 // other, so that the reduction needs no atomics.
 //
-// Radix sort: 8-bit digits, least significant first, as many passes as the largest row
-// number needs.  One pass = tile histogram -> exclusive scan of the digit-major
-// histogram -> stable scatter.  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes,
+// Radix sort: least significant digit first, the fewest passes of at most 8-bit digits that
+// cover the largest row number, with equal digit widths (22-bit rows: 3 x 8 bits).  One pass
+// = tile histograms -> per digit, a scan over the tiles -> stable scatter (which adds the
+// scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes,
 // each wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same
-// digit are found with 8 ballots; the lowest of them adds the group's size to its
+// digit are found with one ballot per digit bit; the lowest of them adds the group's size to its
 // wavefront's private LDS counter, so every LDS counter has one writer per step and no
 // atomic is needed.  Ranks are taken in key order (wave, step, lane), which makes every
 // pass stable and the whole sort deterministic.
@@ -21,11 +22,12 @@ namespace {
 
 __device__ inline uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
 
-// Lanes of this wavefront whose (valid) digit equals this lane's digit.
+// Lanes of this wavefront whose (valid) RB-bit digit equals this lane's digit.
+template <int RB>
 __device__ inline uint64_t match_digit(uint32_t d, bool valid) {
   uint64_t m = __ballot(valid);
 #pragma unroll
-  for (int bit = 0; bit < kRadixBits; ++bit) {
+  for (int bit = 0; bit < RB; ++bit) {
     const bool x = (d >> bit) & 1u;
     const uint64_t bb = __ballot(x);
     m &= x ? bb : ~bb;
@@ -54,36 +56,91 @@ __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ 
   }
 }
 
+// Digit counts of one tile (LDS atomics: counts do not depend on the order of the adds).
+template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
                                                     int shift, uint32_t* __restrict__ hist,
                                                     int nblocks) {
-  __shared__ uint32_t cnt[4][kRadix];
-  for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+  constexpr int kRadix = 1 << RB;
+  constexpr int kSteps = kSortTile / 256;
+  __shared__ uint32_t cnt[kRadix];
+  for (int i = threadIdx.x; i < kRadix; i += 256) cnt[i] = 0;
   __syncthreads();
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * 1024;
-#pragma unroll 4
-  for (int st = 0; st < 16; ++st) {
-    const int64_t pos = base + st * 64 + lane;
-    const bool valid = pos < n;
-    const uint32_t d = valid ? (keys[pos] >> shift) & (kRadix - 1) : 0u;
-    const uint64_t m = match_digit(d, valid);
-    if (valid && (m & lanemask_lt(lane)) == 0) cnt[w][d] += static_cast<uint32_t>(__popcll(m));
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + threadIdx.x;
+  uint32_t kk[kSteps];
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const int64_t pos = base + st * 256;
+    kk[st] = pos < n ? keys[pos] : 0u;
   }
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st)
+    if (base + st * 256 < n) atomicAdd(&cnt[(kk[st] >> shift) & (kRadix - 1)], 1u);
   __syncthreads();
   for (int dg = threadIdx.x; dg < kRadix; dg += 256)
-    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[0][dg] + cnt[1][dg] + cnt[2][dg] + cnt[3][dg];
+    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[dg];
 }
 
+// Exclusive scan of x over the 256 threads of a block (every thread gets its prefix; `total`
+// receives the block sum).  `wsum` is 4 words of LDS.
+__device__ inline uint32_t block_exclusive_scan(uint32_t x, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t inc = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint32_t pre = 0;
+  for (int i = 0; i < w; ++i) pre += wsum[i];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();  // wsum is reused by the next call
+  return pre + inc - x;
+}
+
+// One block per digit: exclusive scan of that digit's tile counts (tile order), and the
+// digit's total.
+__global__ __launch_bounds__(256) void k_digit_scan(const uint32_t* __restrict__ hist,
+                                                    uint32_t* __restrict__ hist_scan, int nblocks,
+                                                    uint32_t* __restrict__ totals) {
+  __shared__ uint32_t wsum[4];
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * nblocks;
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < nblocks; b0 += 256 * 8) {
+    uint32_t v[8], sum = 0;
+    const int first = b0 + threadIdx.x * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = first + i < nblocks ? hist[row + first + i] : 0u;
+      sum += v[i];
+    }
+    uint32_t total;
+    uint32_t run = carry + block_exclusive_scan(sum, wsum, total);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (first + i < nblocks) hist_scan[row + first + i] = run;
+      run += v[i];
+    }
+    carry += total;
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = carry;
+}
+
+template <int RB>
 __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restrict__ keys_in,
                                                        const uint32_t* __restrict__ vals_in,
                                                        int64_t n, int shift,
                                                        const uint32_t* __restrict__ hist_scan,
+                                                       const uint32_t* __restrict__ totals,
                                                        uint32_t* __restrict__ keys_out,
                                                        uint32_t* __restrict__ vals_out, int nblocks) {
+  static_assert(RB <= 8, "one digit per thread in the digit-base scan");
+  constexpr int kRadix = 1 << RB;
   __shared__ uint32_t cnt[4][kRadix];
+  __shared__ uint32_t wsum[4];
   for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
-  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * 1024;
   uint32_t kk[16], vv[16], rk[16];
@@ -94,23 +151,31 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
     kk[st] = valid ? keys_in[pos] : 0u;
     vv[st] = valid ? vals_in[pos] : 0u;
   }
+  // where each digit starts in the output: exclusive scan of the digit totals, plus this
+  // tile's offset among the tiles
+  uint32_t total;
+  const uint32_t dbase =
+      block_exclusive_scan(threadIdx.x < kRadix ? totals[threadIdx.x] : 0u, wsum, total);
+  const uint32_t tbase = threadIdx.x < kRadix
+                             ? dbase + hist_scan[static_cast<int64_t>(threadIdx.x) * nblocks + blockIdx.x]
+                             : 0u;
 #pragma unroll
   for (int st = 0; st < 16; ++st) {
     const bool valid = base + st * 64 + lane < n;
     const uint32_t d = (kk[st] >> shift) & (kRadix - 1);
-    const uint64_t m = match_digit(d, valid);
+    const uint64_t m = match_digit<RB>(d, valid);
     const uint32_t before = static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
     const uint32_t pre = cnt[w][d];  // every lane reads before the group leader writes
     rk[st] = pre + before;
     if (valid && before == 0) cnt[w][d] = pre + static_cast<uint32_t>(__popcll(m));
   }
   __syncthreads();
-  for (int dg = threadIdx.x; dg < kRadix; dg += 256) {
-    uint32_t run = hist_scan[static_cast<int64_t>(dg) * nblocks + blockIdx.x];
+  if (threadIdx.x < kRadix) {
+    uint32_t run = tbase;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
-      const uint32_t c = cnt[ww][dg];
-      cnt[ww][dg] = run;
+      const uint32_t c = cnt[ww][threadIdx.x];
+      cnt[ww][threadIdx.x] = run;
       run += c;
     }
   }
@@ -216,11 +281,13 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
   GradWorkspace ws;
   ws.n = n;
   if (n <= 0) return ws;
-  ws.passes = (key_bits(total_rows) + kRadixBits - 1) / kRadixBits;
+  const int bits = key_bits(total_rows);
+  ws.passes = (bits + kRadixBits - 1) / kRadixBits;          // fewest passes of <= 8 bits
+  ws.rbits = ws.passes > 0 ? (bits + ws.passes - 1) / ws.passes : 0;  // equal widths
   ws.nblocks = (n + kSortTile - 1) / kSortTile;
   ws.nchunks = (n + kChunk - 1) / kChunk;
-  const int64_t m_hist = ws.nblocks * kRadix;
-  const int64_t scan_len = m_hist > n ? m_hist : n;
+  const int64_t m_hist = ws.nblocks * (int64_t{1} << ws.rbits);
+  const int64_t scan_len = n;
   char* p = static_cast<char*>(base);
   size_t off = 0;
   auto take = [&](size_t bytes) -> void* {
@@ -234,6 +301,7 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
   ws.vals1 = static_cast<uint32_t*>(take(4 * n));
   ws.hist = static_cast<uint32_t*>(take(4 * m_hist));
   ws.hist_scan = static_cast<uint32_t*>(take(4 * m_hist));
+  ws.dtotal = static_cast<uint32_t*>(take(4 << kRadixBits));
   ws.flags = static_cast<uint32_t*>(take(4 * n));
   ws.flags_scan = static_cast<uint32_t*>(take(4 * n));
   int64_t len = scan_len;
@@ -268,6 +336,41 @@ el_status launch_exclusive_scan(const uint32_t* in, uint32_t* out, int64_t n,
   return check_launch("scan");
 }
 
+namespace {
+
+template <int RB>
+el_status radix_pass_t(const GradWorkspace& ws, int shift, const uint32_t* kin, const uint32_t* vin,
+                       uint32_t* kout, uint32_t* vout, hipStream_t stream) {
+  const int nb = static_cast<int>(ws.nblocks);
+  hipLaunchKernelGGL(k_radix_hist<RB>, dim3(nb), dim3(256), 0, stream, kin, ws.n, shift, ws.hist, nb);
+  el_status st = check_launch("radix_hist");
+  if (st != EL_OK) return st;
+  hipLaunchKernelGGL(k_digit_scan, dim3(1 << RB), dim3(256), 0, stream,
+                     static_cast<const uint32_t*>(ws.hist), ws.hist_scan, nb, ws.dtotal);
+  if ((st = check_launch("radix_scan")) != EL_OK) return st;
+  hipLaunchKernelGGL(k_radix_scatter<RB>, dim3(nb), dim3(256), 0, stream, kin, vin, ws.n, shift,
+                     static_cast<const uint32_t*>(ws.hist_scan), static_cast<const uint32_t*>(ws.dtotal),
+                     kout, vout, nb);
+  return check_launch("radix_scatter");
+}
+
+el_status radix_pass(const GradWorkspace& ws, int shift, const uint32_t* kin, const uint32_t* vin,
+                     uint32_t* kout, uint32_t* vout, hipStream_t stream) {
+  switch (ws.rbits) {
+    case 1: return radix_pass_t<1>(ws, shift, kin, vin, kout, vout, stream);
+    case 2: return radix_pass_t<2>(ws, shift, kin, vin, kout, vout, stream);
+    case 3: return radix_pass_t<3>(ws, shift, kin, vin, kout, vout, stream);
+    case 4: return radix_pass_t<4>(ws, shift, kin, vin, kout, vout, stream);
+    case 5: return radix_pass_t<5>(ws, shift, kin, vin, kout, vout, stream);
+    case 6: return radix_pass_t<6>(ws, shift, kin, vin, kout, vout, stream);
+    case 7: return radix_pass_t<7>(ws, shift, kin, vin, kout, vout, stream);
+    case 8: return radix_pass_t<8>(ws, shift, kin, vin, kout, vout, stream);
+  }
+  return set_error(EL_ERR_UNSUPPORTED, "radix digit width out of range");
+}
+
+}  // namespace
+
 el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint32_t flags,
                                 GradWorkspace& ws, uint32_t** sorted_keys, uint32_t** sorted_vals,
                                 hipStream_t stream) {
@@ -279,17 +382,8 @@ el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint3
   el_status st = check_launch("build_keys");
   if (st != EL_OK) return st;
   uint32_t *kin = ws.keys0, *vin = ws.vals0, *kout = ws.keys1, *vout = ws.vals1;
-  const int nb = static_cast<int>(ws.nblocks);
   for (int pass = 0; pass < ws.passes; ++pass) {
-    const int shift = pass * kRadixBits;
-    hipLaunchKernelGGL(k_radix_hist, dim3(nb), dim3(256), 0, stream, kin, ws.n, shift, ws.hist, nb);
-    if ((st = check_launch("radix_hist")) != EL_OK) return st;
-    if ((st = launch_exclusive_scan(ws.hist, ws.hist_scan, ws.nblocks * kRadix, ws.scan_level,
-                                    stream)) != EL_OK)
-      return st;
-    hipLaunchKernelGGL(k_radix_scatter, dim3(nb), dim3(256), 0, stream, kin, vin, ws.n, shift,
-                       ws.hist_scan, kout, vout, nb);
-    if ((st = check_launch("radix_scatter")) != EL_OK) return st;
+    if ((st = radix_pass(ws, pass * ws.rbits, kin, vin, kout, vout, stream)) != EL_OK) return st;
     std::swap(kin, kout);
     std::swap(vin, vout);
   }

@@ -158,7 +158,7 @@ SORT_CASES = [
     ("f16-table-f32-grad", (3000, 17, 40000), 32, "f16", "f32", ("poisson", 5.0, 0, 12), "zipf", False, 500),
     ("hash-negative", (999, 7, 5000), 64, "bf16", "f32", ("poisson", 4.0, 0, 9), "uniform", True, 250),
     ("tiny-f32", (1000,) * 8, 16, "f32", "f32", ("one",), "uniform", False, 256),
-    ("four-radix-passes", (20_000_000, 5), 4, "f32", "f32", ("poisson", 3.0, 0, 8), "uniform", False, 3000),
+    ("27-bit-keys-three-passes", (20_000_000, 5), 4, "f32", "f32", ("poisson", 3.0, 0, 8), "uniform", False, 3000),
 ]
 
 
