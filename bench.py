@@ -6,9 +6,12 @@ on the train_step workload (B = 65536, 26 fp32 tables x 100,000 x 128, bf16 acti
 Zipf(1.05) hotness-1 indices, SGD lr 0.01).  Eight distinct index batches rotate across
 steps so that no step replays the previous one's rows from cache.
 
-Prints one JSON line: samples/s, the step time, the roofline of the dominant kernel
-(algorithmic bytes / its HIP-event time vs the 8 TB/s HBM peak) and the CPU oracle
-timed on a bounded sample of the same workload.
+Prints one JSON line: samples/s, the step time, per-call HIP-event times (mean, median,
+p10, p90) with algorithmic GB/s, the roofline of the dominant kernel (algorithmic bytes /
+its average HIP-event time vs the 8 TB/s HBM peak, and vs the measured bandwidth of a
+plain 4 GiB device copy), and the CPU oracle timed on a bounded sample of the same
+workload.  --workload picks another configuration (forward-only ones time the two
+forward calls).
 """
 import argparse
 import json
@@ -20,7 +23,22 @@ import numpy as np
 import torch
 
 HBM_PEAK_GBPS = 8000.0
-METRIC = "samples/s fwd+bwd (emb-bag + dot interaction) at batch 65536; achieved HBM GB/s"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "k_emb_bag_fwd": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                      "embedding_lookup_feature_amd/csrc/emb_bag_fwd.hip"],
+    "k_dot_fwd_mfma": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                       "embedding_lookup_feature_amd/csrc/dot_interact.hip"],
+    "k_dot_bwd_mfma": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                       "embedding_lookup_feature_amd/csrc/dot_interact.hip"],
+}
+KERNEL_OF_CALL = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
+                  "dot_interact_bwd": "k_dot_bwd_mfma"}
+
+
+def metric_name(wl):
+    what = "fwd+bwd" if wl.backward else "fwd"
+    return f"samples/s {what} (emb-bag + dot interaction) at batch {wl.batch}; achieved HBM GB/s"
 
 
 def algorithmic_bytes(wl, nnz):
@@ -38,16 +56,67 @@ def algorithmic_bytes(wl, nnz):
         "dot_interact_fwd": B * V * D * sa + B * S * sa,
         # dout in, x0 + emb in, dx0 + demb out
         "dot_interact_bwd": B * S * sa + 2 * B * V * D * sa,
-        # sort: 3 LSD passes of key+value read/write; gradients gathered once; rows read+written
+        # keys + bag ids read once, gradients gathered once, touched rows read + written (the
+        # sort's own passes are not counted)
         "emb_grad_reduce_update": None,  # filled in by the caller (needs the unique-row count)
     }
+
+
+def source_digest(paths):
+    """sha256 over the given files (repo-relative), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entries = json.load(f)
+    for e in entries.get("kernels", []):
+        if e["workload"] == workload and e["kernel"] == kernel:
+            if source_digest(e["sources"]) != e["sources_sha256"]:
+                return None
+            return e["bytes_per_launch"]
+    return None
+
+
+def copy_bandwidth(dev, gib=4, reps=3):
+    """Read + write GB/s of a plain device-to-device copy of `gib` GiB (the box's achievable
+    HBM bandwidth for a streaming kernel)."""
+    n = gib << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def pct(xs, q):
+    return float(np.percentile(np.asarray(xs), q))
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="train_step")
     ap.add_argument("--batches", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -55,6 +124,8 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
+    ap.add_argument("--no-copy-bw", action="store_true",
+                    help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -79,11 +150,15 @@ def main():
         batches.append((elf.Bags(idx, off, B), synth.make_x0(wl, dev, i), synth.make_dout(wl, dev, i), idx, off))
     emb = torch.empty((B, F, D), dtype=act, device=dev)
     out = torch.empty((B, wl.out_stride), dtype=act, device=dev)
-    dx0 = torch.empty((B, D), dtype=act, device=dev)
-    demb = torch.empty((B, F, D), dtype=act, device=dev)
-    ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches), dtype=torch.uint8, device=dev)
+    if wl.backward:
+        dx0 = torch.empty((B, D), dtype=act, device=dev)
+        demb = torch.empty((B, F, D), dtype=act, device=dev)
+        ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches),
+                         dtype=torch.uint8, device=dev)
 
     names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_reduce_update"]
+    if not wl.backward:
+        names = names[:2]
 
     def step(i, ev=None):
         bags, x0, G = batches[i % len(batches)][:3]
@@ -92,6 +167,8 @@ def main():
         if ev: ev[1].record()
         elf.dot_interact_fwd(x0, emb, out)
         if ev: ev[2].record()
+        if not wl.backward:
+            return
         elf.dot_interact_bwd(x0, emb, G, dx0, demb)
         if ev: ev[3].record()
         elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
@@ -120,13 +197,18 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # per-call durations: HIP events around each call, over the same number of steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per-call durations: HIP events around each call (recorded on the stream the calls are
+    # enqueued on, torch's current stream), over the same number of steps
+    nev = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
     torch.cuda.synchronize()
-    call_ms = {n: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs])) for k, n in enumerate(names)}
+    call_samples = {n: [e[k].elapsed_time(e[k + 1]) for e in evs] for k, n in enumerate(names)}
+    call_ms = {n: float(np.mean(v)) for n, v in call_samples.items()}
+
+    copy_gbps = None if args.no_copy_bw else copy_bandwidth(dev)
 
     nnz = batches[0][3].numel()
     algo = algorithmic_bytes(wl, nnz)
@@ -137,20 +219,31 @@ def main():
     st = 4 if wl.table_dtype == "f32" else 2
     sa = 4 if wl.act_dtype == "f32" else 2
     algo["emb_grad_reduce_update"] = 8 * nnz + nnz * D * sa + 2 * U * D * st
-    calls = {n: {"ms": round(call_ms[n], 4), "algo_bytes": int(algo[n]),
-                 "algo_gbps": round(algo[n] / (call_ms[n] * 1e-3) / 1e9, 1)} for n in names}
+    algo = {n: algo[n] for n in names}
+    calls = {}
+    for n in names:
+        v = call_samples[n]
+        c = {"ms": round(call_ms[n], 4), "median_ms": round(pct(v, 50), 4),
+             "p10_ms": round(pct(v, 10), 4), "p90_ms": round(pct(v, 90), 4),
+             "algo_bytes": int(algo[n]), "algo_gbps": round(algo[n] / (call_ms[n] * 1e-3) / 1e9, 1)}
+        if copy_gbps:
+            c["frac_of_copy"] = round(c["algo_gbps"] / copy_gbps, 4)
+        calls[n] = c
     step_bytes = sum(algo.values())
-    # dominant single-kernel call: the one with the longest time among the one-launch calls
-    single = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd"]
-    dom = max(single, key=lambda n: call_ms[n])
-    kernel = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
-              "dot_interact_bwd": "k_dot_bwd_mfma"}[dom]
+    # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
+    # short sort / reduce kernels, each well below the interaction kernels)
+    dom = max([n for n in names if n in KERNEL_OF_CALL], key=lambda n: call_ms[n])
+    kernel = KERNEL_OF_CALL[dom]
     achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(wl.name, kernel)}
+    if copy_gbps:
+        roofline["copy_gbps"] = round(copy_gbps, 1)
+        roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
 
     result = {
-        "metric": METRIC,
+        "metric": metric_name(wl),
         "value": round(B / (ms_per_step * 1e-3), 1),
         "unit": "samples/s",
         "n_gpus": 1,
@@ -160,10 +253,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if wl.act_dtype == "bf16" else wl.act_dtype,
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.description}", "global_batch": B,
-                   "tables": F, "rows_per_table": wl.rows[0], "dim": D,
+                   "tables": F, "rows_per_table": wl.rows[0] if len(set(wl.rows)) == 1 else "varied",
+                   "total_rows": wl.total_rows, "dim": D,
                    "table_dtype": wl.table_dtype, "act_dtype": wl.act_dtype, "nnz": int(nnz),
                    "unique_rows": U, "parallelism": "single-gpu"},
         "hbm_gbps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
@@ -175,34 +269,66 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(wl, W, ro, batch, seconds):
     """The CPU oracle over the first `n` samples of batch 0 (same tables), sized so that
-    the run takes about `seconds`; samples/s on one host core."""
+    the run takes about `seconds`; samples/s on one host core (the process is pinned to one
+    core while the oracle runs)."""
     from oracle import oracle as orc
-    from tests.helpers import sub_batch, to_np
+    from tests.helpers import compact_tables, sub_batch, to_np
 
     bags, x0, G, idx, off = batch
-    W_h, ro_h, idx_h, off_h = to_np(W), to_np(ro), to_np(idx), to_np(off)
+    idx_h, off_h = to_np(idx), to_np(off)
     x0_h, G_h = to_np(x0), to_np(G)
     F, B, D = wl.num_tables, wl.batch, wl.dim
+    table_bytes = W.numel() * W.element_size()
+    full_tables = table_bytes <= (4 << 30)
+    if full_tables:
+        W_h, ro_h = to_np(W), to_np(ro)
 
     def run(n):
         samples = np.arange(n)
         si, so, nb = sub_batch(idx_h, off_h, F, B, samples)
+        if full_tables:
+            Wn, ron = W_h, ro_h
+        else:  # only the rows the sample looks up (kept in row order)
+            Wn, ron, si, _ = compact_tables(W, to_np(ro), si, so, F, nb)
         t = time.perf_counter()
-        emb = orc.emb_bag_fwd(W_h, wl.table_dtype, ro_h, si, so, nb, D, wl.act_dtype)
+        emb = orc.emb_bag_fwd(Wn, wl.table_dtype, ron, si, so, nb, D, wl.act_dtype)
         orc.dot_interact_fwd(x0_h[:n], emb, wl.act_dtype, wl.act_dtype, wl.out_stride)
-        _, demb = orc.dot_interact_bwd(x0_h[:n], emb, wl.act_dtype, G_h[:n], wl.act_dtype, wl.act_dtype)
-        orc.grad_reduce_update(W_h, wl.table_dtype, ro_h, si, so, nb, demb, wl.act_dtype, wl.lr)
+        if wl.backward:
+            _, demb = orc.dot_interact_bwd(x0_h[:n], emb, wl.act_dtype, G_h[:n], wl.act_dtype, wl.act_dtype)
+            orc.grad_reduce_update(Wn, wl.table_dtype, ron, si, so, nb, demb, wl.act_dtype, wl.lr)
         return time.perf_counter() - t
 
-    probe_n = 256
-    dt = run(probe_n)
-    n = int(min(B, max(probe_n, probe_n * seconds / max(dt, 1e-6))))
-    dt = run(n)
+    model, nproc = cpu_info()
+    old = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old)})
+    try:
+        probe_n = 256
+        dt = run(probe_n)
+        n = int(min(B, max(probe_n, probe_n * seconds / max(dt, 1e-6))))
+        dt = run(n)
+    finally:
+        os.sched_setaffinity(0, old)
+    tables = "full tables" + ("; full-table SGD copy" if wl.backward else "") if full_tables \
+        else "only the looked-up rows of the tables"
     return {"value": round(n / dt, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {B} samples of batch 0 (all {F} tables; full-table SGD copy), "
-                      f"single-threaded C oracle, {dt:.1f} s"}
+            "sample": f"first {n} of {B} samples of batch 0 (all {F} tables, {tables}), "
+                      f"single-threaded C oracle pinned to one core, {dt:.1f} s",
+            "host_cpu": model, "host_cpus_visible": nproc}
 
 
 if __name__ == "__main__":

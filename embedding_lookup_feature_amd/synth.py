@@ -114,6 +114,20 @@ WORKLOADS = {
         bag=("poisson", 20.0, 1, 100), bottom_mlp=(13, 512, 256, 64), backward=True,
         description="B=16384, 100 bf16 tables x 1M x 64, bag length Poisson(20) clipped to [1,100], "
                     "Zipf(1.05), 101 vectors -> 5050 pairs, fwd+bwd+update"),
+    # secondary figure: the small tables at the large batch (cache-resident tables)
+    "train_small_tables": Workload(
+        "train_small_tables", 65536, (1000,) * 8, 16, "f32", "bf16", "zipf", 1.05,
+        bottom_mlp=(13, 64, 16), backward=True,
+        description="B=65536, 8 tables x 1000 x 16 fp32 (cache-resident), bf16 activations, "
+                    "Zipf(1.05) hotness 1, 9 vectors -> 36 pairs -> 52 padded to 56, fwd+bwd+SGD"),
+    # controls: uniform indices (no reuse, so the gathered bytes all come from HBM)
+    "fwd_core_uniform": Workload(
+        "fwd_core_uniform", 65536, (100_000,) * 26, 128, "f32", "bf16", "uniform", backward=False,
+        description="fwd_core shapes with uniform indices (control: no row reuse)"),
+    "large_table_uniform": Workload(
+        "large_table_uniform", 262144, tuple(large_table_rows()), 128, "f16", "f16", "uniform",
+        backward=False,
+        description="large_table shapes with uniform indices (control: no row reuse)"),
 }
 
 
