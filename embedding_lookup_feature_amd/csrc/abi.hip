@@ -151,6 +151,29 @@ el_status dot_interact_bwd(const void* x0, const void* emb, el_dtype in_dtype, i
                         grad_dtype, stream);
 }
 
+el_status emb_dot_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags, const void* x0,
+                      el_dtype act_dtype, void* emb_out, void* out, int32_t out_stride,
+                      hipStream_t stream) {
+  const char* fn = "emb_dot_fwd";
+  EL_TRY(check_tables(tab, fn));
+  EL_TRY(check_bags(tab, bags, fn));
+  if (flags & ~static_cast<uint32_t>(EL_FLAG_HASH_INDICES)) return bad(fn, "unknown flags");
+  const int32_t B = bags->batch;
+  EL_TRY(check_interaction(fn, B, tab->num_tables, tab->dim, out_stride, act_dtype, act_dtype, act_dtype));
+  EL_TRY(check_dense(fn, x0, B > 0, "x0"));
+  EL_TRY(check_dense(fn, emb_out, false, "emb_out"));
+  EL_TRY(check_dense(fn, out, B > 0, "out"));
+  if (B == 0) return EL_OK;
+  const el_status st = launch_emb_dot_fwd(*tab, *bags, flags, x0, act_dtype, emb_out, out, out_stride, stream);
+  if (st != EL_ERR_UNSUPPORTED) return st;
+  // shapes the fused kernel does not cover: the two calls one after the other
+  if (!emb_out)
+    return set_error(EL_ERR_UNSUPPORTED, "emb_dot_fwd: emb_out is required for this shape / dtype");
+  EL_TRY(launch_emb_bag_fwd(*tab, *bags, flags, emb_out, act_dtype, stream));
+  return launch_dot_fwd(x0, emb_out, act_dtype, B, tab->num_tables, tab->dim, out, act_dtype,
+                        out_stride, stream);
+}
+
 size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags) {
   if (check_tables(tab, "emb_grad_workspace_bytes") != EL_OK) return 0;
   if (check_bags(tab, bags, "emb_grad_workspace_bytes") != EL_OK) return 0;

@@ -22,35 +22,37 @@
 #include <utility>
 
 #include "el_internal.hpp"
+#include "el_mfma.hpp"
 
 namespace el {
+
+// Workgroups that loop over samples: launch as many as can be resident at once (occupancy
+// from the kernel's registers and LDS), never more than there are samples.
+int resident_grid(const void* kernel, int B, size_t lds_bytes, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  int per_cu = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({kernel, lds_bytes});
+    if (it != cache.end()) {
+      per_cu = it->second;
+    } else {
+      int n = 0, cus = 0, dev = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds_bytes) != hipSuccess) n = 4;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+      per_cu = (n > 0 ? n : 1) * (cus > 0 ? cus : 256);
+      cache[{kernel, lds_bytes}] = per_cu;
+    }
+  }
+  return B < per_cu ? B : per_cu;
+}
+
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// Native 4 x 32-bit vector (kept in registers by the optimiser, unlike HIP's uint4 class).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-template <class IT>
-__device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c);
-template <>
-__device__ inline f32x16 mfma32<BF16T>(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-template <>
-__device__ inline f32x16 mfma32<F16T>(const u32x4& a, const u32x4& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
 __device__ inline int64_t pair_pos(int i, int j) { return static_cast<int64_t>(i) * (i - 1) / 2 + j; }
-
-// Output row of the 32x32 MFMA accumulator: register r of lane l holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32.
-__device__ inline int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
 // One sample's inputs as a sequence of 16-byte chunks, lane-strided over the wavefront:
 // chunks [0, tile) are the V x D tile (row 0 = x0[b], rows 1.. = emb[b], contiguous in
@@ -96,10 +98,6 @@ __device__ inline void put_sample(char* lds, int pitch, int goff, int trash, int
   }
 }
 
-__device__ inline u32x4 lds16_or_zero(const char* lds, int off, bool ok) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (ok ? off : 0));
-  return ok ? v : u32x4{0, 0, 0, 0};
-}
 
 // ---------------------------------------------------------------------------------------
 // Forward, MFMA path.
@@ -120,9 +118,7 @@ __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict_
   const int obytes = (out_stride * static_cast<int>(sizeof(OS)) + 15) / 16 * 16;
   const int trash = obase + obytes;
   OS* ostage = reinterpret_cast<OS*>(lds + obase);
-  const int NT = (V + 31) / 32;
   const int lane = threadIdx.x;
-  const int half = lane >> 5, col = lane & 31;
   const int tile = V * (D / 8);
 
   u32x4 r[NQ];
@@ -137,25 +133,7 @@ __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict_
     for (int d = lane; d < D; d += 64)
       ostage[d] = OT::from_f(IT::to_f(*reinterpret_cast<const uint16_t*>(lds + d * 2)));
     for (int c = D + P + lane; c < out_stride; c += 64) ostage[c] = OT::from_f(0.0f);
-    for (int I = 0; I < NT; ++I) {
-      for (int J = 0; J <= I; ++J) {
-        f32x16 acc = {};
-        const int ra = I * 32 + col, rb = J * 32 + col;
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int cb = (2 * ks + half) * 16;  // byte offset of this lane's 8 elements
-          const u32x4 a = lds16_or_zero(lds, ra * pitch + cb, ra < V);
-          const u32x4 bv = (I == J) ? a : lds16_or_zero(lds, rb * pitch + cb, rb < V);
-          acc = mfma32<IT>(a, bv, acc);
-        }
-        const int j = J * 32 + col;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int i = I * 32 + acc_row(rr, lane);
-          const int off = (i < V && j < i) ? obase + (D + i * (i - 1) / 2 + j) * static_cast<int>(sizeof(OS)) : trash;
-          *reinterpret_cast<OS*>(lds + off) = OT::from_f(acc[rr]);
-        }
-      }
-    }
+    gram_lower_to_lds<IT, OT>(lds, pitch, V, D, obase, trash);
     __syncthreads();
     OS* orow = out + static_cast<int64_t>(b) * out_stride;
     if (SPL > 0 && vec_out) {
@@ -436,36 +414,12 @@ int grid_for(int B, size_t lds_bytes) {
   return B < g ? B : g;
 }
 
-// One-wavefront workgroups that loop over samples: launch as many as can be resident at
-// once (occupancy from the kernel's registers and LDS), never more than there are samples.
-int resident_grid(const void* kernel, int B, size_t lds_bytes, int block = 64) {
-  static std::mutex mu;
-  static std::map<std::pair<const void*, size_t>, int> cache;
-  int per_cu = 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find({kernel, lds_bytes});
-    if (it != cache.end()) {
-      per_cu = it->second;
-    } else {
-      int n = 0, cus = 0, dev = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds_bytes) != hipSuccess) n = 4;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-      per_cu = (n > 0 ? n : 1) * (cus > 0 ? cus : 256);
-      cache[{kernel, lds_bytes}] = per_cu;
-    }
-  }
-  return B < per_cu ? B : per_cu;
-}
-
 template <class IT, class OT, int NQ, int SPL>
 el_status launch_fwd_t(const void* x0, const void* emb, int B, int F, int D, void* out,
                        int out_stride, size_t lds, hipStream_t stream) {
   const int vec_out = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S)) % 16 == 0;
   auto kern = k_dot_fwd_mfma<IT, OT, NQ, SPL>;
-  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds)), dim3(64),
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64)), dim3(64),
                      lds, stream, static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B,
                      F, D, static_cast<typename OT::S*>(out), out_stride, vec_out);
   return check_launch("dot_interact_fwd");

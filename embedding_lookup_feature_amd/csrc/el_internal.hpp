@@ -171,6 +171,14 @@ el_status launch_reduce_update(const el_tables& tab, const el_bags& bags, const 
 el_status launch_exclusive_scan(const uint32_t* in, uint32_t* out, int64_t n,
                                 uint32_t* const level[4][2], hipStream_t stream);
 
+// Grid for workgroups of `block` threads that loop over B samples: as many as can be
+// resident at once (occupancy from the kernel's registers and `lds_bytes` of LDS), at most B.
+int resident_grid(const void* kernel, int B, size_t lds_bytes, int block);
+
+el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, void* emb_out, void* out,
+                             int out_stride, hipStream_t stream);
+
 el_status launch_validate(const el_tables& tab, const el_bags& bags, uint32_t flags,
                           int64_t* bad_count, hipStream_t stream);
 

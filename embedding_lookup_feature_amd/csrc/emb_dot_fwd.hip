@@ -1,0 +1,308 @@
+// emb_dot_fwd.hip -- the embedding-bag gather fused with the dot-interaction forward
+// (gfx950).
+//
+// Page "DLRM For PyTorch", §Model architecture: the pooled embedding vectors of a sample
+// (one per table) and the bottom-MLP output x0 feed the dot interaction.  Computed apart,
+// the pooled vectors make a round trip through HBM (written by the gather, read back by
+// the interaction).  Here one wavefront builds a sample's V x D tile straight in LDS: it
+// gathers the sample's table rows, sums each bag in fp32 in CSR order, rounds once to the
+// activation type (exactly as emb_bag_fwd does) and writes the rounded vectors to the LDS
+// tile (and, when asked, to emb_out for the backward); the Gram products then run on the
+// tile exactly as in dot_interact_fwd.  Results are bit-identical to the two separate calls.
+//
+// Pipeline per wavefront (grid-strided over samples j, j+G, ...): while sample j is
+// reduced and multiplied, the rows of sample j+G, the first indices of sample j+2G and the
+// CSR bounds of sample j+3G are in flight.  Every load is issued unconditionally (sample
+// numbers past the end are clamped), every store count is fixed and each trip issues its
+// loads before its stores, so waiting for a load never waits for a store (loads and stores
+// share one in-order completion counter).
+#include "el_internal.hpp"
+#include "el_mfma.hpp"
+
+namespace el {
+namespace {
+
+// 8 consecutive elements of a table row: 32 bytes (fp32) or 16 bytes (16-bit).
+template <class TT>
+struct Unit {
+  static constexpr int NV = static_cast<int>(sizeof(typename TT::S)) / 2;  // 16-byte vectors
+  u32x4 v[NV];
+};
+
+template <class TT>
+__device__ inline void load_unit(Unit<TT>& u, const typename TT::S* p) {
+#pragma unroll
+  for (int i = 0; i < Unit<TT>::NV; ++i) u.v[i] = reinterpret_cast<const u32x4*>(p)[i];
+}
+
+template <class TT>
+__device__ inline void unit_to_f(const Unit<TT>& u, float* f) {
+#pragma unroll
+  for (int i = 0; i < Unit<TT>::NV; ++i) {
+    const uint4 w = {u.v[i][0], u.v[i][1], u.v[i][2], u.v[i][3]};
+    unpack16<TT>(w, f + i * epv<TT>());
+  }
+}
+
+// An empty register use: the compiler waits here for the load that produced `v`.
+template <class T>
+__device__ inline void settle(const T& v) {
+  asm volatile("" ::"v"(v));
+}
+
+// 8 floats -> 8 x 16-bit of IT (round to nearest even), packed as 16 bytes.
+template <class IT>
+__device__ inline u32x4 pack8(const float* f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(IT::from_f(f[2 * i])) | (static_cast<uint32_t>(IT::from_f(f[2 * i + 1])) << 16);
+  return r;
+}
+
+// TT: table type; IT: activation type (16-bit: pooled vectors, x0 and out); NU: row units
+// (8 elements) per lane; SPL: 16-byte output-row chunks per lane; EMB: store emb_out.
+template <class TT, class IT, int NU, int SPL, bool EMB>
+__global__ __launch_bounds__(64) void k_emb_dot_fwd(
+    const typename TT::S* __restrict__ W, const int64_t* __restrict__ row_off,
+    const int32_t* __restrict__ idx, int32_t nnz, const int32_t* __restrict__ off, int32_t B,
+    int32_t F, int32_t D, uint32_t hash, const uint16_t* __restrict__ x0,
+    uint16_t* __restrict__ emb, uint16_t* __restrict__ out, int32_t out_stride) {
+  extern __shared__ uint4 smem[];
+  char* lds = reinterpret_cast<char*>(smem);
+  using S = typename TT::S;
+  const int lane = threadIdx.x;
+  const int V = F + 1;
+  const int P = V * (V - 1) / 2;
+  const int pitch = D * 2 + 16;
+  const int obase = V * pitch;
+  const int obytes = (out_stride * 2 + 15) / 16 * 16;
+  const int trash = obase + obytes;
+  uint16_t* ostage = reinterpret_cast<uint16_t*>(lds + obase);
+  const int nur = D / 8;       // units per row
+  const int units = F * nur;   // units per sample
+  const int G = gridDim.x;
+  const int last = B - 1;
+
+  // per table (lane t < F): first joint-table row and row count
+  uint32_t tbase = 0, trows = 1;
+  if (lane < F) {
+    tbase = static_cast<uint32_t>(row_off[lane]);
+    trows = static_cast<uint32_t>(row_off[lane + 1] - row_off[lane]);
+  }
+  // CSR bounds of sample j's bag in table `lane`
+  auto clampj = [&](int j) { return j < 0 ? 0 : (j < last ? j : last); };
+  auto load_bounds = [&](int j, int& s, int& e) {
+    const int g = (lane < F ? lane : 0) * B + clampj(j);
+    s = ld_stream(off + g);
+    e = ld_stream(off + g + 1);
+  };
+  // first index of the bag (any valid position when the bag is empty)
+  auto load_first = [&](int s) -> int32_t {
+    return ld_stream(idx + (s < 0 ? 0 : (s < nnz ? s : nnz - 1)));
+  };
+  // joint-table row of the first entry (row 0 for an empty bag: read, never used)
+  auto first_row = [&](int32_t r, int s, int e) -> uint32_t {
+    if (hash) r = floor_mod(r, static_cast<int32_t>(trows));
+    return e > s ? tbase + static_cast<uint32_t>(r) : 0u;
+  };
+  auto issue_rows = [&](int j, uint32_t rid, Unit<TT> (&rows)[NU], u32x4& xv) {
+    const int jc = clampj(j);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      int q = u * 64 + lane;
+      q = q < units ? q : units - 1;
+      const int t = q / nur, c = q - t * nur;
+      const uint32_t r = static_cast<uint32_t>(__shfl(static_cast<int>(rid), t));
+      load_unit<TT>(rows[u], W + static_cast<int64_t>(r) * D + c * 8);
+    }
+    const int xc = lane < nur ? lane : nur - 1;
+    xv = *reinterpret_cast<const u32x4*>(x0 + static_cast<int64_t>(jc) * D + xc * 8);
+  };
+
+  // prologue: bounds of samples j, j+G, j+2G; first indices of j, j+G; rows of j.  All of
+  // it lands before the loop starts (settle), so that the wait counts the compiler derives
+  // for the loop are those of its steady state alone.
+  int j = blockIdx.x;
+  int s0, e0, s1, e1, s2, e2;
+  load_bounds(j, s0, e0);
+  load_bounds(j + G, s1, e1);
+  load_bounds(j + 2 * G, s2, e2);
+  int32_t r1 = load_first(s1);
+  Unit<TT> rows[NU];
+  u32x4 xv;
+  issue_rows(j, first_row(load_first(s0), s0, e0), rows, xv);
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int i = 0; i < Unit<TT>::NV; ++i) settle(rows[u].v[i]);
+  settle(xv);
+  settle(s1); settle(e1); settle(s2); settle(e2); settle(r1);
+
+  for (; j < B; j += G) {
+    // (1) bounds of sample j+3G, first indices of sample j+2G
+    int s3, e3;
+    load_bounds(j + 3 * G, s3, e3);
+    const int32_t r2 = load_first(s2);
+
+    // (2) pool sample j: first rows (in registers), further entries of multi-hot bags in CSR
+    //     order, fp32; one rounding to the activation type, straight into the LDS tile
+    //     (rows 1..); x0 into row 0
+    const int nonempty = e0 > s0;
+    if (__ballot(lane < F && e0 - s0 > 1) == 0) {  // wave-uniform: hotness <= 1
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int q = u * 64 + lane;
+        q = q < units ? q : units - 1;  // lanes past the end repeat the last unit (same bytes)
+        const int t = q / nur, c = q - t * nur;
+        const bool ne = __shfl(nonempty, t) != 0;
+        float f[8];
+        unit_to_f<TT>(rows[u], f);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) f[x] = ne ? f[x] : 0.0f;
+        *reinterpret_cast<u32x4*>(lds + (1 + t) * pitch + c * 16) = pack8<IT>(f);
+      }
+    } else {  // multi-hot bags: the further entries one after the other (not pipelined)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int q = u * 64 + lane;
+        q = q < units ? q : units - 1;
+        const int t = q / nur, c = q - t * nur;
+        const bool ne = __shfl(nonempty, t) != 0;
+        const int bs = __shfl(s0, t), be = __shfl(e0, t);
+        const uint32_t tb = static_cast<uint32_t>(__shfl(static_cast<int>(tbase), t));
+        const int32_t nt = __shfl(static_cast<int>(trows), t);
+        float f[8];
+        unit_to_f<TT>(rows[u], f);
+        for (int k = bs + 1; k < be; ++k) {
+          int32_t r = idx[k];
+          if (hash) r = floor_mod(r, nt);
+          Unit<TT> w;
+          load_unit<TT>(w, W + static_cast<int64_t>(tb + static_cast<uint32_t>(r)) * D + c * 8);
+          float g[8];
+          unit_to_f<TT>(w, g);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) f[x] += g[x];
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) f[x] = ne ? f[x] : 0.0f;
+        *reinterpret_cast<u32x4*>(lds + (1 + t) * pitch + c * 16) = pack8<IT>(f);
+      }
+    }
+    *reinterpret_cast<u32x4*>(lds + (lane < nur ? lane * 16 : trash)) = xv;
+
+    // (3) rows of sample j+G (their first indices were loaded one trip ago) -- issued
+    //     before this trip's stores
+    issue_rows(j + G, first_row(r1, s1, e1), rows, xv);
+
+    // (4) emb_out from the tile; the interaction: x0 copy, zero padding, strict lower
+    //     triangle of the Gram matrix
+    __syncthreads();
+    if constexpr (EMB) {
+      const int64_t eb = static_cast<int64_t>(j) * F * D;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        int q = u * 64 + lane;
+        q = q < units ? q : units - 1;
+        const int t = q / nur, c = q - t * nur;
+        *reinterpret_cast<u32x4*>(emb + eb + static_cast<int64_t>(q) * 8) =
+            *reinterpret_cast<const u32x4*>(lds + (1 + t) * pitch + c * 16);
+      }
+    }
+    for (int d = lane; d < D; d += 64)
+      ostage[d] = IT::from_f(IT::to_f(*reinterpret_cast<const uint16_t*>(lds + d * 2)));
+    for (int c = D + P + lane; c < out_stride; c += 64) ostage[c] = 0;
+    gram_lower_to_lds<IT, IT>(lds, pitch, V, D, obase, trash);
+    __syncthreads();
+
+    // (5) the output row: a fixed number of 16-byte stores per lane
+    uint16_t* orow = out + static_cast<int64_t>(j) * out_stride;
+    const int nchunk = obytes / 16;
+#pragma unroll
+    for (int k = 0; k < SPL; ++k) {
+      int q = k * 64 + lane;
+      q = q < nchunk ? q : nchunk - 1;
+      reinterpret_cast<u32x4*>(orow)[q] = reinterpret_cast<const u32x4*>(ostage)[q];
+    }
+
+    s0 = s1; e0 = e1;
+    s1 = s2; e1 = e2;
+    s2 = s3; e2 = e3;
+    r1 = r2;
+  }
+}
+
+template <class TT, class IT, int NU, int SPL, bool EMB>
+el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
+                   void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
+  auto kern = k_emb_dot_fwd<TT, IT, NU, SPL, EMB>;
+  const int B = bags.batch;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64)),
+                     dim3(64), lds, stream, static_cast<const typename TT::S*>(tab.base),
+                     tab.row_offset, bags.indices, static_cast<int32_t>(bags.nnz), bags.offsets, B,
+                     tab.num_tables, tab.dim, (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
+                     static_cast<const uint16_t*>(x0), static_cast<uint16_t*>(emb_out),
+                     static_cast<uint16_t*>(out), out_stride);
+  return check_launch("emb_dot_fwd");
+}
+
+template <class TT, class IT, int NU, int SPL>
+el_status launch_emb(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
+                     void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
+  if (emb_out)
+    return launch_t<TT, IT, NU, SPL, true>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+  return launch_t<TT, IT, NU, SPL, false>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+}
+
+// Shape classes: row units per lane (NU) and output-row chunks per lane (SPL).
+template <class TT, class IT>
+el_status launch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
+                       void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
+  const int units = tab.num_tables * (tab.dim / 8);
+  const int ochunks = (out_stride * 2 + 15) / 16;
+#define EL_SPL(NU)                                                                                   \
+  do {                                                                                               \
+    if (ochunks <= 64) return launch_emb<TT, IT, NU, 1>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream); \
+    if (ochunks <= 256) return launch_emb<TT, IT, NU, 4>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream); \
+  } while (0)
+  if (units <= 2 * 64) EL_SPL(2);
+  else if (units <= 4 * 64) EL_SPL(4);
+  else if (units <= 7 * 64) EL_SPL(7);
+  else if (units <= 12 * 64) EL_SPL(12);
+  else if (units <= 16 * 64) EL_SPL(16);
+#undef EL_SPL
+  return EL_ERR_UNSUPPORTED;
+}
+
+template <class TT>
+el_status launch_act(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
+                     el_dtype act, void* emb_out, void* out, int out_stride, size_t lds,
+                     hipStream_t stream) {
+  if (act == EL_BF16) return launch_shape<TT, BF16T>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+  if (act == EL_F16) return launch_shape<TT, F16T>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+  return EL_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+// The fused kernel covers 16-bit activations, D % 16 == 0, F <= 64, 16-byte output rows and
+// a tile that fits in LDS; EL_ERR_UNSUPPORTED (nothing enqueued) otherwise.
+el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, void* emb_out, void* out,
+                             int out_stride, hipStream_t stream) {
+  const int F = tab.num_tables, D = tab.dim;
+  const size_t V = static_cast<size_t>(F) + 1;
+  const size_t obytes = (static_cast<size_t>(out_stride) * 2 + 15) / 16 * 16;
+  const size_t lds = V * (D * 2 + 16) + obytes + 16;
+  if (act_dtype == EL_F32 || D % 16 != 0 || F > 64 || (out_stride * 2) % 16 != 0 ||
+      lds > 64 * 1024 || bags.nnz == 0 || tab.total_rows == 0)
+    return EL_ERR_UNSUPPORTED;
+  switch (tab.dtype) {
+    case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
+    case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
+    case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
+  }
+  return EL_ERR_UNSUPPORTED;
+}
+
+}  // namespace el

@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         T, Bg = ctypes.POINTER(ElTables), ctypes.POINTER(ElBags)
         L.emb_bag_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp]
         L.dot_interact_fwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32, vp]
+        L.emb_dot_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp, vp, i32, vp]
         L.dot_interact_bwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32,
                                        vp, vp, ctypes.c_int, vp]
         L.emb_grad_workspace_bytes.argtypes = [T, Bg]
@@ -62,7 +63,7 @@ def lib() -> ctypes.CDLL:
         L.el_validate_bags.argtypes = [T, Bg, u32, vp, vp]
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
-        for name in ("emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd",
+        for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
                      "emb_grad_reduce_update", "emb_grad_sort", "el_validate_bags"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -159,6 +160,19 @@ def dot_interact_fwd(x0: torch.Tensor, emb: torch.Tensor, out: torch.Tensor, str
     B, F, D = emb.shape
     _check(lib().dot_interact_fwd(_dev(x0, "x0"), _dev(emb, "emb"), _dtype(emb, "emb"), B, F, D,
                                   _dev(out, "out"), _dtype(out, "out"), out.shape[1], _stream(stream)))
+    return out
+
+
+def emb_dot_fwd(tables: Tables, bags: Bags, x0: torch.Tensor, out: torch.Tensor,
+                emb_out: torch.Tensor = None, hash_indices=False, stream=None):
+    """emb_bag_fwd into emb_out followed by dot_interact_fwd into out, in one call (bit-identical
+    results); emb_out may be None when the pooled vectors are not needed."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    ep = _dev(emb_out, "emb_out") if emb_out is not None else None
+    if emb_out is not None and emb_out.dtype != x0.dtype:
+        raise ValueError("emb_out must have the activation dtype of x0")
+    _check(lib().emb_dot_fwd(ctypes.byref(tables.c), ctypes.byref(bags.c), flags, _dev(x0, "x0"),
+                             _dtype(x0, "x0"), ep, _dev(out, "out"), out.shape[1], _stream(stream)))
     return out
 
 

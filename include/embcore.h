@@ -102,6 +102,23 @@ EL_API el_status dot_interact_fwd(const void* x0, const void* emb, el_dtype in_d
                            int32_t out_stride, hipStream_t stream);
 
 /*
+ * The two forward calls in one (same page, §Model architecture: the pooled embeddings and
+ * the bottom-MLP output feed the dot interaction).  Same results, bit for bit, as
+ *   emb_bag_fwd(tab, bags, flags, emb_out, act_dtype);
+ *   dot_interact_fwd(x0, emb_out, act_dtype, B, F, D, out, act_dtype, out_stride);
+ * with B = bags->batch, F = tab->num_tables, D = tab->dim, but each sample's pooled vectors
+ * are built in on-chip memory and multiplied there, so they are not read back from HBM.
+ * emb_out ([B][F][D] of act_dtype, 16-byte aligned) may be NULL when the pooled vectors are
+ * not needed (inference); they are then not stored at all.  x0: [B][D], out:
+ * [B][out_stride] of act_dtype.  The fused kernel covers bf16 / fp16 activations with
+ * D % 16 == 0, F <= 64 and out_stride * 2 % 16 == 0; other shapes run the two calls in turn
+ * (emb_out required, else EL_ERR_UNSUPPORTED).
+ */
+EL_API el_status emb_dot_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, void* emb_out, void* out,
+                             int32_t out_stride, hipStream_t stream);
+
+/*
  * Dot interaction backward.  With G = dout[b] and the symmetric V x V matrix S,
  * S_ij = S_ji = G[D + p(i,j)] (i > j), S_ii = 0:
  *   dV = S V;   dx0[b] = G[0:D) + dV_0;   demb[b][t] = dV_{1+t}

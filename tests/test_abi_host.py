@@ -27,7 +27,7 @@ def ref(x):
 def test_library_loads_and_exports_every_declared_function():
     L = ec.lib()
     names = ec.header_functions()
-    assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd",
+    assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
                           "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version"}
     for n in names:
@@ -66,6 +66,21 @@ def test_emb_bag_fwd_rejects(tab, bg, flags, out, odt, status):
     rc = L.emb_bag_fwd(ref(tab) if tab is not None else None, ref(bg), flags, out, odt, None)
     assert rc == status
     assert "emb_bag_fwd" in ec.el_last_error()
+
+
+def test_emb_dot_fwd_rejects():
+    L = ec.lib()
+    T, Bg = ref(tables()), ref(bags())
+    assert L.emb_dot_fwd(T, Bg, 0, A, ec.EL_BF16, A, A, 478, None) == INVALID      # out_stride < D + P
+    assert L.emb_dot_fwd(T, Bg, 4, A, ec.EL_BF16, A, A, 480, None) == INVALID      # unknown flag
+    assert L.emb_dot_fwd(T, Bg, 0, 0, ec.EL_BF16, A, A, 480, None) == INVALID      # null x0
+    assert L.emb_dot_fwd(T, Bg, 0, A, ec.EL_BF16, A + 8, A, 480, None) == INVALID  # misaligned emb_out
+    assert L.emb_dot_fwd(T, Bg, 0, A, ec.EL_BF16, A, 0, 480, None) == INVALID      # null out
+    assert L.emb_dot_fwd(T, Bg, 0, A, 6, A, A, 480, None) == INVALID               # unknown dtype
+    assert L.emb_dot_fwd(None, Bg, 0, A, ec.EL_BF16, A, A, 480, None) == INVALID
+    assert "emb_dot_fwd" in ec.el_last_error()
+    # B == 0: valid, nothing enqueued
+    assert L.emb_dot_fwd(T, ref(bags(B=0, nnz=0)), 0, A, ec.EL_BF16, None, A, 480, None) == ec.EL_OK
 
 
 def test_dot_interact_rejects():

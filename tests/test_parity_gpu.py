@@ -114,6 +114,73 @@ def test_dot_interact_fwd_matches_oracle(case):
     assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
 
 
+FUSED_CASES = [
+    # label, rows, D, table dtype, act dtype, bag, index dist, hash, B, store emb
+    ("f32-bf16-26x128-zipf", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 1000, True),
+    ("f32-bf16-26x128-no-emb", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 1000, False),
+    ("f16-ragged-tables", (3, 70000, 1234), 128, "f16", "f16", ("one",), "zipf", False, 1500, True),
+    ("bf16-d64-multihot", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300, True),
+    ("f32-bf16-d16-empty-bags", (500,) * 5, 16, "f32", "bf16", ("poisson", 3.0, 0, 10), "uniform", False, 333, True),
+    ("f32-f16-hash", (999, 7, 5000), 32, "f32", "f16", ("one",), "uniform", True, 400, True),
+    ("bf16-64-tables", (300,) * 64, 32, "bf16", "bf16", ("one",), "uniform", False, 100, True),
+    ("bf16-one-table", (50,), 16, "bf16", "bf16", ("one",), "uniform", False, 64, False),
+    # shapes the fused kernel does not cover: the two calls in turn
+    ("fallback-f32-act", (1000,) * 8, 16, "f32", "f32", ("one",), "uniform", False, 300, True),
+    ("fallback-65-tables", (100,) * 65, 16, "bf16", "bf16", ("one",), "uniform", False, 50, True),
+    ("fallback-d8", (100,) * 4, 8, "bf16", "bf16", ("one",), "uniform", False, 65, True),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_emb_dot_fwd_matches_separate_calls_and_oracle(case):
+    label, rows, D, tdt, adt, bag, dist, hsh, B, store = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=adt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag, bottom_mlp=(13, 64, D))
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    x0 = synth.make_x0(wl, DEV)
+    at = synth.torch_dtype(adt)
+    F, S = wl.num_tables, wl.out_stride
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    # the two calls
+    emb_sep = torch.full((B, F, D), float("nan"), dtype=at, device=DEV)
+    out_sep = torch.full((B, S), float("nan"), dtype=at, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb_sep, hash_indices=hsh)
+    elf.dot_interact_fwd(x0, emb_sep, out_sep)
+    # the fused call
+    emb = torch.full((B, F, D), float("nan"), dtype=at, device=DEV) if store else None
+    out = torch.full((B, S), float("nan"), dtype=at, device=DEV)
+    elf.emb_dot_fwd(tab, bags, x0, out, emb, hash_indices=hsh)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out_sep.view(torch.uint8)), label + ": out differs from the two calls"
+    if store:
+        assert torch.equal(emb.view(torch.uint8), emb_sep.view(torch.uint8)), label + ": emb differs"
+    # and the oracle
+    emb_ref = orc.emb_bag_fwd(to_np(W), tdt, to_np(ro), to_np(idx), to_np(off), B, D, adt, hash_indices=hsh)
+    out_ref = orc.dot_interact_fwd(to_np(x0), emb_ref, adt, adt, S)
+    if store:
+        if bag == ("one",):
+            assert_bits(emb, emb_ref, label + " emb")
+        else:
+            assert_close(emb, emb_ref, adt, label + " emb")
+    P = (F + 1) * F // 2
+    assert_bits(out[:, :D], out_ref[:, :D], label + " x0 copy")
+    assert_close(out[:, D:D + P], out_ref[:, D:D + P], adt, label + " pairs")
+    assert_bits(out[:, D + P:], out_ref[:, D + P:], label + " padding")
+    # determinism
+    out2 = torch.empty_like(out)
+    elf.emb_dot_fwd(tab, bags, x0, out2, emb, hash_indices=hsh)
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+
+
+def test_emb_dot_fwd_without_emb_needs_the_fused_shapes():
+    wl = base_wl(batch=16, rows=(100,) * 65, dim=16, act_dtype="bf16", bottom_mlp=(13, 64, 16))
+    W, ro, idx, off = make_problem(wl)
+    x0 = synth.make_x0(wl, DEV)
+    out = torch.zeros((16, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(elf.EmbcoreError):
+        elf.emb_dot_fwd(elf.Tables(W, ro), elf.Bags(idx, off, 16), x0, out, None)
+
+
 BWD_CASES = [
     # label, F, D, in dtype, dout dtype, grad dtype, stride, B
     ("f32-tiny", 8, 16, "f32", "f32", "f32", None, 300),
