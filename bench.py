@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
+    ap.add_argument("--overlap-sort", action="store_true",
+                    help="run the gradient sort (emb_grad_prepare) on a side stream overlapping the "
+                         "forward and the interaction backward, then emb_grad_apply")
     ap.add_argument("--no-copy-bw", action="store_true",
                     help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
     args = ap.parse_args()
@@ -156,12 +159,30 @@ def main():
         ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches),
                          dtype=torch.uint8, device=dev)
 
-    names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_reduce_update"]
+    overlap = wl.backward and args.overlap_sort
     if not wl.backward:
-        names = names[:2]
+        names = ["emb_bag_fwd", "dot_interact_fwd"]
+    elif overlap:
+        names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_apply"]
+    else:
+        names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_reduce_update"]
+    main_stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream() if overlap else None  # default priority
+    applied = torch.cuda.Event()
+    prepared = torch.cuda.Event()
+    applied.record(main_stream)
 
-    def step(i, ev=None):
+    def step(i, ev=None, side_ev=None):
+        """One pass of the path over batch i.  With overlap, the sort of the lookups (it needs
+        only the indices) runs on a side stream while the forward and the interaction
+        backward run; the update waits for it."""
         bags, x0, G = batches[i % len(batches)][:3]
+        if overlap:
+            side.wait_event(applied)  # the workspace is free once the previous update is done
+            if side_ev: side_ev[0].record(side)
+            elf.emb_grad_prepare(tab, bags, ws, stream=side)
+            if side_ev: side_ev[1].record(side)
+            prepared.record(side)
         if ev: ev[0].record()
         elf.emb_bag_fwd(tab, bags, emb)
         if ev: ev[1].record()
@@ -171,7 +192,12 @@ def main():
             return
         elf.dot_interact_bwd(x0, emb, G, dx0, demb)
         if ev: ev[3].record()
-        elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
+        if overlap:
+            main_stream.wait_event(prepared)
+            elf.emb_grad_apply(tab, bags, demb, wl.lr, ws)
+            applied.record(main_stream)
+        else:
+            elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
         if ev: ev[4].record()
 
     if args.copy_calib_mib:
@@ -191,9 +217,11 @@ def main():
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record()
+    if side is not None:
+        side.wait_stream(main_stream)  # no side-stream work starts before t0
     for i in range(args.steps):
         step(i)
-    t1.record()
+    t1.record()  # the last update waited for the last sort, so all work is before t1
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
@@ -201,11 +229,14 @@ def main():
     # enqueued on, torch's current stream), over the same number of steps
     nev = len(names) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs[i], sevs[i] if overlap else None)
     torch.cuda.synchronize()
     call_samples = {n: [e[k].elapsed_time(e[k + 1]) for e in evs] for k, n in enumerate(names)}
+    if overlap:  # side stream: the sort, overlapping the calls above
+        call_samples["emb_grad_prepare"] = [e[0].elapsed_time(e[1]) for e in sevs]
     call_ms = {n: float(np.mean(v)) for n, v in call_samples.items()}
 
     copy_gbps = None if args.no_copy_bw else copy_bandwidth(dev)
@@ -219,17 +250,24 @@ def main():
     st = 4 if wl.table_dtype == "f32" else 2
     sa = 4 if wl.act_dtype == "f32" else 2
     algo["emb_grad_reduce_update"] = 8 * nnz + nnz * D * sa + 2 * U * D * st
-    algo = {n: algo[n] for n in names}
+    algo["emb_grad_apply"] = algo["emb_grad_reduce_update"]
+    # the sort: keys + bag ids read and written once per 8-bit radix pass
+    key_bits = max(1, int(wl.total_rows - 1).bit_length())
+    algo["emb_grad_prepare"] = 16 * nnz * ((key_bits + 7) // 8)
+    timed = list(call_samples)
+    algo = {n: algo[n] for n in timed}
     calls = {}
-    for n in names:
+    for n in timed:
         v = call_samples[n]
         c = {"ms": round(call_ms[n], 4), "median_ms": round(pct(v, 50), 4),
              "p10_ms": round(pct(v, 10), 4), "p90_ms": round(pct(v, 90), 4),
              "algo_bytes": int(algo[n]), "algo_gbps": round(algo[n] / (call_ms[n] * 1e-3) / 1e9, 1)}
         if copy_gbps:
             c["frac_of_copy"] = round(c["algo_gbps"] / copy_gbps, 4)
+        if n == "emb_grad_prepare":
+            c["stream"] = "side (overlaps the forward and the interaction backward)"
         calls[n] = c
-    step_bytes = sum(algo.values())
+    step_bytes = sum(algo[n] for n in names)  # the sort's passes are not counted
     # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
     # short sort / reduce kernels, each well below the interaction kernels)
     dom = max([n for n in names if n in KERNEL_OF_CALL], key=lambda n: call_ms[n])

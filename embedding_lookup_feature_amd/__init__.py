@@ -16,6 +16,8 @@ from .embcore import (  # noqa: F401
     el_version,
     emb_bag_fwd,
     emb_dot_fwd,
+    emb_grad_apply,
+    emb_grad_prepare,
     emb_grad_reduce_update,
     emb_grad_sort,
     emb_grad_workspace_bytes,

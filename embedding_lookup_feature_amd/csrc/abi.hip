@@ -104,6 +104,13 @@ el_status check_grad_call(const char* fn, const el_tables* tab, const el_bags* b
   return EL_OK;
 }
 
+el_status check_grad_input(const char* fn, const el_tables* tab, el_dtype grad_dtype) {
+  if (!dtype_valid(grad_dtype)) return bad(fn, "unknown gradient dtype");
+  if ((tab->dim * dtype_size(grad_dtype)) % 16 != 0)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dim * sizeof(grad dtype) must be a multiple of 16 bytes");
+  return EL_OK;
+}
+
 }  // namespace
 }  // namespace el
 
@@ -186,14 +193,36 @@ el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bags, uint
                                  size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "emb_grad_reduce_update";
   EL_TRY(check_grad_call(fn, tab, bags, flags, workspace, workspace_bytes));
-  if (!dtype_valid(grad_dtype)) return bad(fn, "unknown gradient dtype");
-  if ((tab->dim * dtype_size(grad_dtype)) % 16 != 0)
-    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dim * sizeof(grad dtype) must be a multiple of 16 bytes");
+  EL_TRY(check_grad_input(fn, tab, grad_dtype));
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
   EL_TRY(check_dense(fn, demb, true, "demb"));
   GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
   uint32_t *keys = nullptr, *vals = nullptr;
   EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
+  return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
+}
+
+el_status emb_grad_prepare(const el_tables* tab, const el_bags* bags, uint32_t flags, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "emb_grad_prepare";
+  EL_TRY(check_grad_call(fn, tab, bags, flags, workspace, workspace_bytes));
+  if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
+  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  return launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream);
+}
+
+el_status emb_grad_apply(const el_tables* tab, const el_bags* bags, uint32_t flags, const void* demb,
+                         el_dtype grad_dtype, float lr, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  const char* fn = "emb_grad_apply";
+  EL_TRY(check_grad_call(fn, tab, bags, flags, workspace, workspace_bytes));
+  EL_TRY(check_grad_input(fn, tab, grad_dtype));
+  if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
+  EL_TRY(check_dense(fn, demb, true, "demb"));
+  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  sorted_buffers(ws, &keys, &vals);
   return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
 }
 

@@ -160,6 +160,9 @@ el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint3
                                 GradWorkspace& ws, uint32_t** sorted_keys, uint32_t** sorted_vals,
                                 hipStream_t stream);
 
+// Where launch_grad_sort_core leaves the sorted keys / bag ids.
+void sorted_buffers(const GradWorkspace& ws, uint32_t** sorted_keys, uint32_t** sorted_vals);
+
 el_status launch_segments(const GradWorkspace& ws, const uint32_t* sorted_keys,
                           uint32_t* unique_rows, uint32_t* seg_offsets, uint32_t* num_unique,
                           hipStream_t stream);

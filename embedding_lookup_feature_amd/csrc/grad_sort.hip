@@ -9,12 +9,14 @@
 // Radix sort: least significant digit first, the fewest passes of at most 8-bit digits that
 // cover the largest row number, with equal digit widths (22-bit rows: 3 x 8 bits).  One pass
 // = tile histograms -> per digit, a scan over the tiles -> stable scatter (which adds the
-// scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes,
-// each wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same
-// digit are found with one ballot per digit bit; the lowest of them adds the group's size to its
+// scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes, each
+// wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same digit
+// are found with one ballot per digit bit; the lowest of them adds the group's size to its
 // wavefront's private LDS counter, so every LDS counter has one writer per step and no
 // atomic is needed.  Ranks are taken in key order (wave, step, lane), which makes every
-// pass stable and the whole sort deterministic.
+// pass stable and the whole sort deterministic.  The ranked tile is staged in LDS in
+// sorted order and written out run by run, so that neighbouring threads store to
+// neighbouring addresses.
 #include "el_internal.hpp"
 
 namespace el {
@@ -128,6 +130,10 @@ __global__ __launch_bounds__(256) void k_digit_scan(const uint32_t* __restrict__
   if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
+// Stable scatter of one tile.  The tile's keys are first ranked (per-wave LDS counters, one
+// writer per digit group and step), then staged in LDS in tile-local sorted order, and
+// finally written out by consecutive threads to consecutive positions of each digit's run,
+// so that the global stores are coalesced instead of one address per lane.
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restrict__ keys_in,
                                                        const uint32_t* __restrict__ vals_in,
@@ -136,32 +142,37 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
                                                        const uint32_t* __restrict__ totals,
                                                        uint32_t* __restrict__ keys_out,
                                                        uint32_t* __restrict__ vals_out, int nblocks) {
-  static_assert(RB <= 8, "one digit per thread in the digit-base scan");
+  static_assert(RB <= 8, "one digit per thread in the digit scans");
   constexpr int kRadix = 1 << RB;
-  __shared__ uint32_t cnt[4][kRadix];
+  constexpr int kSteps = kSortTile / 256;  // keys per thread
+  __shared__ uint32_t cnt[4][kRadix];      // per-wave digit counts, then per-wave bases
+  __shared__ uint32_t gofs[kRadix];        // global position of tile-local position 0, per digit
   __shared__ uint32_t wsum[4];
+  __shared__ uint32_t sk[kSortTile], sv[kSortTile];
   for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + w * 1024;
-  uint32_t kk[16], vv[16], rk[16];
+  const int64_t tile0 = static_cast<int64_t>(blockIdx.x) * kSortTile;
+  const int tn = static_cast<int>(n - tile0 < kSortTile ? n - tile0 : kSortTile);  // keys in the tile
+  const int base = w * (kSortTile / 4);  // this wave's keys: [base, base + kSortTile/4)
+  uint32_t kk[kSteps], vv[kSteps], rk[kSteps];
 #pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const int64_t pos = base + st * 64 + lane;
-    const bool valid = pos < n;
-    kk[st] = valid ? keys_in[pos] : 0u;
-    vv[st] = valid ? vals_in[pos] : 0u;
+  for (int st = 0; st < kSteps; ++st) {
+    const int p = base + st * 64 + lane;
+    const bool valid = p < tn;
+    kk[st] = valid ? keys_in[tile0 + p] : 0u;
+    vv[st] = valid ? vals_in[tile0 + p] : 0u;
   }
-  // where each digit starts in the output: exclusive scan of the digit totals, plus this
-  // tile's offset among the tiles
+  // global start of each digit: exclusive scan of the digit totals, plus this tile's offset
   uint32_t total;
   const uint32_t dbase =
       block_exclusive_scan(threadIdx.x < kRadix ? totals[threadIdx.x] : 0u, wsum, total);
-  const uint32_t tbase = threadIdx.x < kRadix
+  const uint32_t tglob = threadIdx.x < kRadix
                              ? dbase + hist_scan[static_cast<int64_t>(threadIdx.x) * nblocks + blockIdx.x]
                              : 0u;
+  // rank within the wave, in key order
 #pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    const bool valid = base + st * 64 + lane < n;
+  for (int st = 0; st < kSteps; ++st) {
+    const bool valid = base + st * 64 + lane < tn;
     const uint32_t d = (kk[st] >> shift) & (kRadix - 1);
     const uint64_t m = match_digit<RB>(d, valid);
     const uint32_t before = static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
@@ -170,23 +181,42 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
     if (valid && before == 0) cnt[w][d] = pre + static_cast<uint32_t>(__popcll(m));
   }
   __syncthreads();
+  // tile-local start of each digit (scan over digits), per-wave bases, global offsets
+  const uint32_t dc = threadIdx.x < kRadix ? cnt[0][threadIdx.x] + cnt[1][threadIdx.x] +
+                                                 cnt[2][threadIdx.x] + cnt[3][threadIdx.x]
+                                           : 0u;
+  const uint32_t lstart = block_exclusive_scan(dc, wsum, total);
   if (threadIdx.x < kRadix) {
-    uint32_t run = tbase;
+    uint32_t run = lstart;
 #pragma unroll
     for (int ww = 0; ww < 4; ++ww) {
       const uint32_t c = cnt[ww][threadIdx.x];
       cnt[ww][threadIdx.x] = run;
       run += c;
     }
+    gofs[threadIdx.x] = tglob - lstart;
   }
   __syncthreads();
+  // stage in tile-local sorted order
 #pragma unroll
-  for (int st = 0; st < 16; ++st) {
-    if (base + st * 64 + lane < n) {
+  for (int st = 0; st < kSteps; ++st) {
+    if (base + st * 64 + lane < tn) {
       const uint32_t d = (kk[st] >> shift) & (kRadix - 1);
-      const uint32_t dst = cnt[w][d] + rk[st];
-      keys_out[dst] = kk[st];
-      vals_out[dst] = vv[st];
+      const uint32_t loc = cnt[w][d] + rk[st];
+      sk[loc] = kk[st];
+      sv[loc] = vv[st];
+    }
+  }
+  __syncthreads();
+  // consecutive positions of a digit's run go to consecutive global positions
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    const int i = st * 256 + threadIdx.x;
+    if (i < tn) {
+      const uint32_t key = sk[i];
+      const uint32_t dst = gofs[(key >> shift) & (kRadix - 1)] + static_cast<uint32_t>(i);
+      keys_out[dst] = key;
+      vals_out[dst] = sv[i];
     }
   }
 }
@@ -387,9 +417,14 @@ el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint3
     std::swap(kin, kout);
     std::swap(vin, vout);
   }
-  *sorted_keys = kin;
-  *sorted_vals = vin;
+  sorted_buffers(ws, sorted_keys, sorted_vals);
   return EL_OK;
+}
+
+void sorted_buffers(const GradWorkspace& ws, uint32_t** sorted_keys, uint32_t** sorted_vals) {
+  const bool odd = ws.passes % 2 != 0;  // every pass swaps the buffers
+  *sorted_keys = odd ? ws.keys1 : ws.keys0;
+  *sorted_vals = odd ? ws.vals1 : ws.vals0;
 }
 
 el_status launch_segments(const GradWorkspace& ws, const uint32_t* sorted_keys,

@@ -59,12 +59,15 @@ def lib() -> ctypes.CDLL:
         L.emb_grad_workspace_bytes.argtypes = [T, Bg]
         L.emb_grad_workspace_bytes.restype = ctypes.c_size_t
         L.emb_grad_reduce_update.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
+        L.emb_grad_prepare.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp]
+        L.emb_grad_apply.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.emb_grad_sort.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp]
         L.el_validate_bags.argtypes = [T, Bg, u32, vp, vp]
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
         for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
-                     "emb_grad_reduce_update", "emb_grad_sort", "el_validate_bags"):
+                     "emb_grad_reduce_update", "emb_grad_prepare", "emb_grad_apply",
+                     "emb_grad_sort", "el_validate_bags"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,6 +206,23 @@ def emb_grad_reduce_update(tables: Tables, bags: Bags, demb: torch.Tensor, lr: f
     _check(lib().emb_grad_reduce_update(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
                                         _dev(demb, "demb"), _dtype(demb, "demb"), float(lr),
                                         _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def emb_grad_prepare(tables: Tables, bags: Bags, workspace: torch.Tensor, hash_indices=False,
+                     stream=None):
+    """First half of emb_grad_reduce_update: sort the lookups by row into `workspace`."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_grad_prepare(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                                  _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def emb_grad_apply(tables: Tables, bags: Bags, demb: torch.Tensor, lr: float, workspace: torch.Tensor,
+                   hash_indices=False, stream=None):
+    """Second half: segment reduce + SGD from the lookups emb_grad_prepare sorted."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_grad_apply(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                                _dev(demb, "demb"), _dtype(demb, "demb"), float(lr),
+                                _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def emb_grad_sort(tables: Tables, bags: Bags, workspace: torch.Tensor, sorted_rows, bag_ids,

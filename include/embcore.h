@@ -150,6 +150,25 @@ EL_API el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bag
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * emb_grad_reduce_update in two halves, so that the sort -- which depends only on the
+ * lookups -- can run on another stream while the forward and the interaction backward
+ * produce demb:
+ *   emb_grad_prepare: builds the (row, bag) keys of every lookup and sorts them into the
+ *     workspace;
+ *   emb_grad_apply:   the segment reduce of demb and the SGD row update, from the sorted
+ *     lookups that emb_grad_prepare left in the same workspace.
+ * prepare followed by apply gives bitwise the result of emb_grad_reduce_update.  Both calls
+ * take the same tables, bags and flags; the caller orders them (same stream, or an event
+ * between streams) and leaves the workspace and the index / offset arrays untouched in
+ * between.  Arguments as for emb_grad_reduce_update.
+ */
+EL_API el_status emb_grad_prepare(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+EL_API el_status emb_grad_apply(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                                const void* demb, el_dtype grad_dtype, float lr,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The sort and segment stage of emb_grad_reduce_update, exposed for inspection:
  *   sorted_rows[q], bag_ids[q] (q < nnz): global row (row_offset[t] + index) and bag id
  *     g = t*B + b of every lookup, sorted by row, equal rows in lookup order;

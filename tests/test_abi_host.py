@@ -28,7 +28,8 @@ def test_library_loads_and_exports_every_declared_function():
     L = ec.lib()
     names = ec.header_functions()
     assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
-                          "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_sort",
+                          "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_prepare",
+                          "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version"}
     for n in names:
         assert hasattr(L, n), n

@@ -334,6 +334,34 @@ def test_emb_grad_reduce_update_is_deterministic_and_lr0_is_identity():
     assert torch.equal(tab_w[2].view(torch.int32), W.view(torch.int32))
 
 
+@pytest.mark.parametrize("case", [SORT_CASES[0], SORT_CASES[-1], UPDATE_CASES[-1]],
+                         ids=[SORT_CASES[0][0], SORT_CASES[-1][0], UPDATE_CASES[-1][0]])
+def test_emb_grad_prepare_apply_equals_reduce_update(case):
+    """The two halves, on two streams ordered by an event, give the one-call result bit for
+    bit (and both match the oracle through the one-call test above)."""
+    wl, W, ro, idx, off = grad_problem(case)
+    hsh = case[7]
+    if case[0] == "one-row-per-table":
+        idx = torch.full_like(idx, 7)
+    demb = synth.make_demb(wl, DEV, dtype=wl.act_dtype)
+    W1, W2 = W.clone(), W.clone()
+    t1, b1 = elf.Tables(W1, ro), elf.Bags(idx, off, wl.batch)
+    t2 = elf.Tables(W2, ro)
+    ws1, ws2 = elf.alloc_workspace(t1, b1), elf.alloc_workspace(t1, b1)
+    ws2.fill_(0x5A)
+    elf.emb_grad_reduce_update(t1, b1, demb, wl.lr, ws1, hash_indices=hsh)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())  # ws2 fill and inputs ready
+    elf.emb_grad_prepare(t2, b1, ws2, hash_indices=hsh, stream=side)
+    done = torch.cuda.Event()
+    done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    elf.emb_grad_apply(t2, b1, demb, wl.lr, ws2, hash_indices=hsh)
+    torch.cuda.synchronize()
+    assert torch.equal(W1.view(torch.uint8), W2.view(torch.uint8))
+    assert not torch.equal(W1.view(torch.uint8), W.view(torch.uint8))
+
+
 def test_validate_bags_counts_defects():
     wl = base_wl(batch=100, rows=(10, 20), dim=16, table_dtype="f32", index_dist="uniform",
                  bag=("poisson", 3.0, 0, 6))
