@@ -10,8 +10,8 @@ Prints one JSON line: samples/s, the step time, per-call HIP-event times (mean, 
 p10, p90) with algorithmic GB/s, the roofline of the dominant kernel (algorithmic bytes /
 its average HIP-event time vs the 8 TB/s HBM peak, and vs the measured bandwidth of a
 plain 4 GiB device copy), and the CPU oracle timed on a bounded sample of the same
-workload.  --workload picks another configuration (forward-only ones time the two
-forward calls).
+workload.  --workload picks another configuration; forward-only ones time the fused
+emb_dot_fwd (no pooled vectors stored), or the two forward calls with --separate-fwd.
 """
 import argparse
 import json
@@ -28,12 +28,17 @@ KERNEL_SOURCES = {
     "k_emb_bag_fwd": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
                       "embedding_lookup_feature_amd/csrc/emb_bag_fwd.hip"],
     "k_dot_fwd_mfma": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                       "embedding_lookup_feature_amd/csrc/el_mfma.hpp",
                        "embedding_lookup_feature_amd/csrc/dot_interact.hip"],
     "k_dot_bwd_mfma": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                       "embedding_lookup_feature_amd/csrc/el_mfma.hpp",
                        "embedding_lookup_feature_amd/csrc/dot_interact.hip"],
+    "k_emb_dot_fwd": ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                      "embedding_lookup_feature_amd/csrc/el_mfma.hpp",
+                      "embedding_lookup_feature_amd/csrc/emb_dot_fwd.hip"],
 }
 KERNEL_OF_CALL = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
-                  "dot_interact_bwd": "k_dot_bwd_mfma"}
+                  "dot_interact_bwd": "k_dot_bwd_mfma", "emb_dot_fwd": "k_emb_dot_fwd"}
 
 
 def metric_name(wl):
@@ -54,6 +59,8 @@ def algorithmic_bytes(wl, nnz):
         "emb_bag_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * F * D * sa,
         # x0 + emb in, interaction rows out
         "dot_interact_fwd": B * V * D * sa + B * S * sa,
+        # rows + indices + offsets + x0 in, interaction rows out (pooled vectors stay on chip)
+        "emb_dot_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * D * sa + B * S * sa,
         # dout in, x0 + emb in, dx0 + demb out
         "dot_interact_bwd": B * S * sa + 2 * B * V * D * sa,
         # keys + bag ids read once, gradients gathered once, touched rows read + written (the
@@ -124,6 +131,9 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
+    ap.add_argument("--separate-fwd", action="store_true",
+                    help="forward-only workloads: time emb_bag_fwd + dot_interact_fwd instead of the "
+                         "fused emb_dot_fwd (which does not store the pooled vectors)")
     ap.add_argument("--overlap-sort", action="store_true",
                     help="run the gradient sort (emb_grad_prepare) on a side stream overlapping the "
                          "forward and the interaction backward, then emb_grad_apply")
@@ -160,7 +170,10 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     overlap = wl.backward and args.overlap_sort
-    if not wl.backward:
+    fused_fwd = not wl.backward and not args.separate_fwd
+    if fused_fwd:
+        names = ["emb_dot_fwd"]
+    elif not wl.backward:
         names = ["emb_bag_fwd", "dot_interact_fwd"]
     elif overlap:
         names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_apply"]
@@ -184,6 +197,10 @@ def main():
             if side_ev: side_ev[1].record(side)
             prepared.record(side)
         if ev: ev[0].record()
+        if fused_fwd:  # forward only: the pooled vectors are not needed afterwards
+            elf.emb_dot_fwd(tab, bags, x0, out, None)
+            if ev: ev[1].record()
+            return
         elf.emb_bag_fwd(tab, bags, emb)
         if ev: ev[1].record()
         elf.dot_interact_fwd(x0, emb, out)

@@ -37,37 +37,51 @@ __device__ inline uint64_t match_digit(uint32_t d, bool valid) {
   return m;
 }
 
-// key = global row of the joint table, val = bag id; one thread per bag.
+// key = global row of the joint table, val = bag id, for every lookup position.  A block
+// takes 256 consecutive bags: their CSR bounds go to LDS, and the block's threads walk the
+// bags' lookup positions (contiguous) with unit stride, so loads and stores are coalesced
+// whatever the bag lengths; each position finds its bag by binary search over the bounds.
 __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ row_off,
                                                     const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ off, int32_t B,
                                                     int32_t nbags, uint32_t hash,
                                                     uint32_t* __restrict__ keys,
                                                     uint32_t* __restrict__ vals) {
-  const int g = blockIdx.x * 256 + threadIdx.x;
-  if (g >= nbags) return;
-  const int t = g / B;
-  const int64_t base = row_off[t];
-  const int32_t n = hash ? static_cast<int32_t>(row_off[t + 1] - base) : 1;
-  const int s = ld_stream(off + g), e = ld_stream(off + g + 1);
-  for (int k = s; k < e; ++k) {
+  __shared__ int32_t bound[257];
+  const int g0 = blockIdx.x * 256;
+  const int nb = nbags - g0 < 256 ? nbags - g0 : 256;  // bags of this block
+  for (int i = threadIdx.x; i <= nb; i += 256) bound[i] = ld_stream(off + g0 + i);
+  __syncthreads();
+  const int s = bound[0], e = bound[nb];
+  for (int k = s + static_cast<int>(threadIdx.x); k < e; k += 256) {
+    // last i in [0, nb) with bound[i] <= k: the bag holding position k
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (bound[mid] <= k) lo = mid; else hi = mid - 1;
+    }
+    const int g = g0 + lo;
+    const int t = g / B;
+    const int64_t base = row_off[t];
     int32_t r = ld_stream(idx + k);
-    if (hash) r = floor_mod(r, n);
+    if (hash) r = floor_mod(r, static_cast<int32_t>(row_off[t + 1] - base));
     keys[k] = static_cast<uint32_t>(base + r);
     vals[k] = static_cast<uint32_t>(g);
   }
 }
 
-// Digit counts of one tile (LDS atomics: counts do not depend on the order of the adds).
+// Digit counts of one tile (LDS atomics into one sub-histogram per wavefront, so that only
+// lanes of one wavefront contend; counts do not depend on the order of the adds).
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
                                                     int shift, uint32_t* __restrict__ hist,
                                                     int nblocks) {
   constexpr int kRadix = 1 << RB;
   constexpr int kSteps = kSortTile / 256;
-  __shared__ uint32_t cnt[kRadix];
-  for (int i = threadIdx.x; i < kRadix; i += 256) cnt[i] = 0;
+  __shared__ uint32_t cnt[4][kRadix];
+  for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
+  const int w = threadIdx.x >> 6;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + threadIdx.x;
   uint32_t kk[kSteps];
 #pragma unroll
@@ -77,10 +91,10 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
   }
 #pragma unroll
   for (int st = 0; st < kSteps; ++st)
-    if (base + st * 256 < n) atomicAdd(&cnt[(kk[st] >> shift) & (kRadix - 1)], 1u);
+    if (base + st * 256 < n) atomicAdd(&cnt[w][(kk[st] >> shift) & (kRadix - 1)], 1u);
   __syncthreads();
   for (int dg = threadIdx.x; dg < kRadix; dg += 256)
-    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[dg];
+    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[0][dg] + cnt[1][dg] + cnt[2][dg] + cnt[3][dg];
 }
 
 // Exclusive scan of x over the 256 threads of a block (every thread gets its prefix; `total`
