@@ -146,7 +146,7 @@ struct GradWorkspace {
   uint32_t* bthrough = nullptr;  // per block: 1 if every chunk of the block is "through"
 };
 
-constexpr int kRadixBits = 8;  // widest radix digit
+constexpr int kRadixBits = 8;  // widest radix digit (wider digits measured slower)
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
 constexpr int kChunk = 16;       // lookups per reduce chunk

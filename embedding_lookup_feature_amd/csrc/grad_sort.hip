@@ -6,8 +6,8 @@
 // Sorting the (row, bag) pairs by row puts all contributions to one row next to each
 // other, so that the reduction needs no atomics.
 //
-// Radix sort: least significant digit first, the fewest passes of at most 8-bit digits that
-// cover the largest row number, with equal digit widths (22-bit rows: 3 x 8 bits).  One pass
+// Radix sort: least significant digit first, the fewest passes of at most kRadixBits-bit
+// digits that cover the largest row number, with equal digit widths (22-bit rows: 3 x 8 bits).  One pass
 // = tile histograms -> per digit, a scan over the tiles -> stable scatter (which adds the
 // scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes, each
 // wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same digit
@@ -40,7 +40,8 @@ __device__ inline uint64_t match_digit(uint32_t d, bool valid) {
 // key = global row of the joint table, val = bag id, for every lookup position.  A block
 // takes 256 consecutive bags: their CSR bounds go to LDS, and the block's threads walk the
 // bags' lookup positions (contiguous) with unit stride, so loads and stores are coalesced
-// whatever the bag lengths; each position finds its bag by binary search over the bounds.
+// whatever the bag lengths; each position finds its bag in the bounds (one probe when the
+// bags hold one lookup each, else a binary search).
 __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ row_off,
                                                     const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ off, int32_t B,
@@ -54,11 +55,16 @@ __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ 
   __syncthreads();
   const int s = bound[0], e = bound[nb];
   for (int k = s + static_cast<int>(threadIdx.x); k < e; k += 256) {
-    // last i in [0, nb) with bound[i] <= k: the bag holding position k
-    int lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (bound[mid] <= k) lo = mid; else hi = mid - 1;
+    // the bag holding position k: the last i in [0, nb) with bound[i] <= k.  First guess:
+    // every bag holds one lookup; otherwise binary search.
+    int lo = k - s < nb - 1 ? k - s : nb - 1;
+    if (!(bound[lo] <= k && k < bound[lo + 1])) {
+      lo = 0;
+      int hi = nb - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bound[mid] <= k) lo = mid; else hi = mid - 1;
+      }
     }
     const int g = g0 + lo;
     const int t = g / B;
@@ -147,7 +153,8 @@ __global__ __launch_bounds__(256) void k_digit_scan(const uint32_t* __restrict__
 // Stable scatter of one tile.  The tile's keys are first ranked (per-wave LDS counters, one
 // writer per digit group and step), then staged in LDS in tile-local sorted order, and
 // finally written out by consecutive threads to consecutive positions of each digit's run,
-// so that the global stores are coalesced instead of one address per lane.
+// so that the global stores are coalesced instead of one address per lane.  Thread i owns
+// the DPT consecutive digits [i*DPT, (i+1)*DPT) in the digit scans.
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restrict__ keys_in,
                                                        const uint32_t* __restrict__ vals_in,
@@ -156,11 +163,12 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
                                                        const uint32_t* __restrict__ totals,
                                                        uint32_t* __restrict__ keys_out,
                                                        uint32_t* __restrict__ vals_out, int nblocks) {
-  static_assert(RB <= 8, "one digit per thread in the digit scans");
   constexpr int kRadix = 1 << RB;
-  constexpr int kSteps = kSortTile / 256;  // keys per thread
-  __shared__ uint32_t cnt[4][kRadix];      // per-wave digit counts, then per-wave bases
-  __shared__ uint32_t gofs[kRadix];        // global position of tile-local position 0, per digit
+  constexpr int DPT = kRadix > 256 ? kRadix / 256 : 1;  // digits per thread in the scans
+  constexpr int kSteps = kSortTile / 256;                // keys per thread
+  static_assert(kSortTile <= 65535, "tile-local positions are 16-bit");
+  __shared__ uint16_t cnt[4][kRadix];  // per-wave digit counts, then per-wave bases
+  __shared__ uint32_t gofs[kRadix];    // global position of tile-local position 0, per digit
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t sk[kSortTile], sv[kSortTile];
   for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
@@ -176,13 +184,27 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
     kk[st] = valid ? keys_in[tile0 + p] : 0u;
     vv[st] = valid ? vals_in[tile0 + p] : 0u;
   }
-  // global start of each digit: exclusive scan of the digit totals, plus this tile's offset
-  uint32_t total;
-  const uint32_t dbase =
-      block_exclusive_scan(threadIdx.x < kRadix ? totals[threadIdx.x] : 0u, wsum, total);
-  const uint32_t tglob = threadIdx.x < kRadix
-                             ? dbase + hist_scan[static_cast<int64_t>(threadIdx.x) * nblocks + blockIdx.x]
-                             : 0u;
+  // global start of each of this thread's digits: exclusive scan of the digit totals plus
+  // this tile's offset among the tiles
+  const int d0 = threadIdx.x * DPT;
+  const bool owns = d0 < kRadix;
+  uint32_t tglob[DPT];
+  {
+    uint32_t tot[DPT], sum = 0;
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) {
+      tot[x] = owns ? totals[d0 + x] : 0u;
+      tglob[x] = owns ? hist_scan[static_cast<int64_t>(d0 + x) * nblocks + blockIdx.x] : 0u;
+      sum += tot[x];
+    }
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(sum, wsum, total);
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) {
+      tglob[x] += run;
+      run += tot[x];
+    }
+  }
   // rank within the wave, in key order
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
@@ -192,23 +214,34 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
     const uint32_t before = static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
     const uint32_t pre = cnt[w][d];  // every lane reads before the group leader writes
     rk[st] = pre + before;
-    if (valid && before == 0) cnt[w][d] = pre + static_cast<uint32_t>(__popcll(m));
+    if (valid && before == 0) cnt[w][d] = static_cast<uint16_t>(pre + __popcll(m));
   }
   __syncthreads();
   // tile-local start of each digit (scan over digits), per-wave bases, global offsets
-  const uint32_t dc = threadIdx.x < kRadix ? cnt[0][threadIdx.x] + cnt[1][threadIdx.x] +
-                                                 cnt[2][threadIdx.x] + cnt[3][threadIdx.x]
-                                           : 0u;
-  const uint32_t lstart = block_exclusive_scan(dc, wsum, total);
-  if (threadIdx.x < kRadix) {
-    uint32_t run = lstart;
+  {
+    uint32_t dc[DPT], sum = 0;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const uint32_t c = cnt[ww][threadIdx.x];
-      cnt[ww][threadIdx.x] = run;
-      run += c;
+    for (int x = 0; x < DPT; ++x) {
+      dc[x] = owns ? static_cast<uint32_t>(cnt[0][d0 + x]) + cnt[1][d0 + x] + cnt[2][d0 + x] + cnt[3][d0 + x]
+                   : 0u;
+      sum += dc[x];
     }
-    gofs[threadIdx.x] = tglob - lstart;
+    uint32_t total;
+    uint32_t lstart = block_exclusive_scan(sum, wsum, total);
+    if (owns) {
+#pragma unroll
+      for (int x = 0; x < DPT; ++x) {
+        uint32_t run = lstart;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+          const uint32_t c = cnt[ww][d0 + x];
+          cnt[ww][d0 + x] = static_cast<uint16_t>(run);
+          run += c;
+        }
+        gofs[d0 + x] = tglob[x] - lstart;
+        lstart += dc[x];
+      }
+    }
   }
   __syncthreads();
   // stage in tile-local sorted order
@@ -326,7 +359,7 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
   ws.n = n;
   if (n <= 0) return ws;
   const int bits = key_bits(total_rows);
-  ws.passes = (bits + kRadixBits - 1) / kRadixBits;          // fewest passes of <= 8 bits
+  ws.passes = (bits + kRadixBits - 1) / kRadixBits;          // fewest passes of <= kRadixBits
   ws.rbits = ws.passes > 0 ? (bits + ws.passes - 1) / ws.passes : 0;  // equal widths
   ws.nblocks = (n + kSortTile - 1) / kSortTile;
   ws.nchunks = (n + kChunk - 1) / kChunk;
@@ -409,6 +442,9 @@ el_status radix_pass(const GradWorkspace& ws, int shift, const uint32_t* kin, co
     case 6: return radix_pass_t<6>(ws, shift, kin, vin, kout, vout, stream);
     case 7: return radix_pass_t<7>(ws, shift, kin, vin, kout, vout, stream);
     case 8: return radix_pass_t<8>(ws, shift, kin, vin, kout, vout, stream);
+    case 9: return radix_pass_t<9>(ws, shift, kin, vin, kout, vout, stream);
+    case 10: return radix_pass_t<10>(ws, shift, kin, vin, kout, vout, stream);
+    case 11: return radix_pass_t<11>(ws, shift, kin, vin, kout, vout, stream);
   }
   return set_error(EL_ERR_UNSUPPORTED, "radix digit width out of range");
 }
