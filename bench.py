@@ -1,7 +1,8 @@
 """Throughput of the embedding-bag + dot-interaction training step on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input already resident in HBM:
-  emb_bag_fwd -> dot_interact_fwd -> dot_interact_bwd -> emb_grad_reduce_update
+  emb_dot_fwd (the gather + the interaction forward) -> dot_interact_bwd ->
+  emb_grad_reduce_update
 on the train_step workload (B = 65536, 26 fp32 tables x 100,000 x 128, bf16 activations,
 Zipf(1.05) hotness-1 indices, SGD lr 0.01).  Eight distinct index batches rotate across
 steps so that no step replays the previous one's rows from cache.
@@ -59,8 +60,10 @@ def algorithmic_bytes(wl, nnz):
         "emb_bag_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * F * D * sa,
         # x0 + emb in, interaction rows out
         "dot_interact_fwd": B * V * D * sa + B * S * sa,
-        # rows + indices + offsets + x0 in, interaction rows out (pooled vectors stay on chip)
-        "emb_dot_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * D * sa + B * S * sa,
+        # rows + indices + offsets + x0 in, interaction rows out (+ pooled vectors out when
+        # the backward needs them); the pooled vectors are not read back from HBM
+        "emb_dot_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * D * sa + B * S * sa
+                       + (B * F * D * sa if wl.backward else 0),
         # dout in, x0 + emb in, dx0 + demb out
         "dot_interact_bwd": B * S * sa + 2 * B * V * D * sa,
         # keys + bag ids read once, gradients gathered once, touched rows read + written (the
@@ -132,8 +135,9 @@ def main():
                     help="before warm-up, copy a buffer of this many MiB once (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
     ap.add_argument("--separate-fwd", action="store_true",
-                    help="forward-only workloads: time emb_bag_fwd + dot_interact_fwd instead of the "
-                         "fused emb_dot_fwd (which does not store the pooled vectors)")
+                    help="time emb_bag_fwd + dot_interact_fwd instead of emb_dot_fwd (which, for "
+                         "forward-only workloads, does not store the pooled vectors at all, and in "
+                         "training runs the two kernels on cache-sized chunks of samples)")
     ap.add_argument("--overlap-sort", action="store_true",
                     help="run the gradient sort (emb_grad_prepare) on a side stream overlapping the "
                          "forward and the interaction backward, then emb_grad_apply")
@@ -170,15 +174,14 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     overlap = wl.backward and args.overlap_sort
-    fused_fwd = not wl.backward and not args.separate_fwd
-    if fused_fwd:
-        names = ["emb_dot_fwd"]
-    elif not wl.backward:
-        names = ["emb_bag_fwd", "dot_interact_fwd"]
+    fused_fwd = not args.separate_fwd
+    fwd_names = ["emb_dot_fwd"] if fused_fwd else ["emb_bag_fwd", "dot_interact_fwd"]
+    if not wl.backward:
+        names = fwd_names
     elif overlap:
-        names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_apply"]
+        names = fwd_names + ["dot_interact_bwd", "emb_grad_apply"]
     else:
-        names = ["emb_bag_fwd", "dot_interact_fwd", "dot_interact_bwd", "emb_grad_reduce_update"]
+        names = fwd_names + ["dot_interact_bwd", "emb_grad_reduce_update"]
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else None  # default priority
     applied = torch.cuda.Event()
@@ -197,25 +200,28 @@ def main():
             if side_ev: side_ev[1].record(side)
             prepared.record(side)
         if ev: ev[0].record()
+        k = 1
         if fused_fwd:  # forward only: the pooled vectors are not needed afterwards
-            elf.emb_dot_fwd(tab, bags, x0, out, None)
-            if ev: ev[1].record()
-            return
-        elf.emb_bag_fwd(tab, bags, emb)
-        if ev: ev[1].record()
-        elf.dot_interact_fwd(x0, emb, out)
-        if ev: ev[2].record()
+            elf.emb_dot_fwd(tab, bags, x0, out, emb if wl.backward else None)
+        else:
+            elf.emb_bag_fwd(tab, bags, emb)
+            if ev: ev[k].record()
+            k += 1
+            elf.dot_interact_fwd(x0, emb, out)
+        if ev: ev[k].record()
+        k += 1
         if not wl.backward:
             return
         elf.dot_interact_bwd(x0, emb, G, dx0, demb)
-        if ev: ev[3].record()
+        if ev: ev[k].record()
+        k += 1
         if overlap:
             main_stream.wait_event(prepared)
             elf.emb_grad_apply(tab, bags, demb, wl.lr, ws)
             applied.record(main_stream)
         else:
             elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
-        if ev: ev[4].record()
+        if ev: ev[k].record()
 
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
@@ -286,8 +292,10 @@ def main():
         calls[n] = c
     step_bytes = sum(algo[n] for n in names)  # the sort's passes are not counted
     # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
-    # short sort / reduce kernels, each well below the interaction kernels)
-    dom = max([n for n in names if n in KERNEL_OF_CALL], key=lambda n: call_ms[n])
+    # short sort / reduce kernels, each well below the interaction kernels; in training
+    # emb_dot_fwd is a sequence of gather and interaction launches)
+    single = [n for n in names if n in KERNEL_OF_CALL and not (n == "emb_dot_fwd" and wl.backward)]
+    dom = max(single, key=lambda n: call_ms[n])
     kernel = KERNEL_OF_CALL[dom]
     achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

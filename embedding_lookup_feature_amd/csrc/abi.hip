@@ -171,14 +171,7 @@ el_status emb_dot_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
   EL_TRY(check_dense(fn, emb_out, false, "emb_out"));
   EL_TRY(check_dense(fn, out, B > 0, "out"));
   if (B == 0) return EL_OK;
-  const el_status st = launch_emb_dot_fwd(*tab, *bags, flags, x0, act_dtype, emb_out, out, out_stride, stream);
-  if (st != EL_ERR_UNSUPPORTED) return st;
-  // shapes the fused kernel does not cover: the two calls one after the other
-  if (!emb_out)
-    return set_error(EL_ERR_UNSUPPORTED, "emb_dot_fwd: emb_out is required for this shape / dtype");
-  EL_TRY(launch_emb_bag_fwd(*tab, *bags, flags, emb_out, act_dtype, stream));
-  return launch_dot_fwd(x0, emb_out, act_dtype, B, tab->num_tables, tab->dim, out, act_dtype,
-                        out_stride, stream);
+  return launch_emb_dot_fwd(*tab, *bags, flags, x0, act_dtype, emb_out, out, out_stride, stream);
 }
 
 size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags) {

@@ -116,8 +116,10 @@ inline bool dtype_valid(int d) { return d == EL_F32 || d == EL_F16 || d == EL_BF
 // ---------------------------------------------------------------------------------------
 // Launchers (validated arguments only).
 // ---------------------------------------------------------------------------------------
+// Samples [b0, b0 + Bc) only (Bc < 0: all B); `out` is the whole [B][F][D] array.
 el_status launch_emb_bag_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
-                             void* out, el_dtype out_dtype, hipStream_t stream);
+                             void* out, el_dtype out_dtype, hipStream_t stream, int b0 = 0,
+                             int Bc = -1);
 
 el_status launch_dot_fwd(const void* x0, const void* emb, el_dtype in_dtype, int B, int F, int D,
                          void* out, el_dtype out_dtype, int out_stride, hipStream_t stream);

@@ -4,9 +4,11 @@
 // feature; the embedding vector of a sample for a table is here the sum of the rows its
 // bag names (hotness 1 = one row).  Bags are table-major (bag g = t*B + b).
 //
-// Mapping.  A wavefront gathers NB = NG * U consecutive bags in one pass and exits: the
-// wave is cut into NG groups of L lanes (L = row bytes / 16, rounded up to a power of two;
-// a group covers one row with 16-byte loads) and every group pools U bags.
+// Mapping.  A launch covers the samples [b0, b0 + Bc) (all of them for emb_bag_fwd); its
+// bags are numbered table-major within that range.  A wavefront gathers NB = NG * U
+// consecutive bags in one pass and exits: the wave is cut into NG groups of L lanes
+// (L = row bytes / 16, rounded up to a power of two; a group covers one row with 16-byte
+// loads) and every group pools U bags.
 //   1. lane i < NB streams in the CSR bounds of bag i and the first row of its table
 //      (independent loads, one round trip), then the bag's first index;
 //   2. every group issues the first-row loads of its U bags back to back, so U row loads
@@ -34,7 +36,8 @@ template <class TT, class OT, int L, int NVL>
 __global__ __launch_bounds__(256) void k_emb_bag_fwd(
     const typename TT::S* __restrict__ W, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ off, int32_t B, int32_t F,
-    int32_t D, int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int32_t nbags) {
+    int32_t D, int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int32_t nbags,
+    int32_t b0, int32_t Bc) {
   constexpr int E = epv<TT>();
   constexpr int NG = 64 / L;                  // bag groups per wave
   constexpr int U = bags_per_group<L, NVL>();  // bags per group
@@ -52,9 +55,10 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
   int s = 0, e = 0, r0 = 0, t = -1, b = 0, nt = 1;
   int64_t base = 0;
   if (lane < NB && g0l + lane < nbags) {
-    const int g = g0 + lane;
-    t = g / B;
-    b = g - t * B;
+    const int gc = g0 + lane;  // bag of the launch: table t, sample b0 + (gc - t * Bc)
+    t = gc / Bc;
+    b = b0 + (gc - t * Bc);
+    const int g = t * B + b;
     s = ld_stream(off + g);
     e = ld_stream(off + g + 1);
     base = row_off[t];
@@ -144,42 +148,42 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
 
 template <class TT, class OT, int L, int NVL>
 el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                   int nvec, hipStream_t stream) {
+                   int nvec, int b0, int Bc, hipStream_t stream) {
   constexpr int NB = (64 / L) * bags_per_group<L, NVL>();
-  const int64_t nbags = static_cast<int64_t>(tab.num_tables) * bags.batch;
+  const int64_t nbags = static_cast<int64_t>(tab.num_tables) * Bc;
   const int64_t waves = (nbags + NB - 1) / NB;
   const int blocks = round_up8((waves + 3) / 4);
   hipLaunchKernelGGL((k_emb_bag_fwd<TT, OT, L, NVL>), dim3(blocks), dim3(256), 0, stream,
                      static_cast<const typename TT::S*>(tab.base), tab.row_offset, bags.indices,
                      bags.offsets, bags.batch, tab.num_tables, tab.dim, nvec,
                      (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
-                     static_cast<typename OT::S*>(out), static_cast<int32_t>(nbags));
+                     static_cast<typename OT::S*>(out), static_cast<int32_t>(nbags), b0, Bc);
   return check_launch("emb_bag_fwd");
 }
 
 template <class TT, class OT>
 el_status dispatch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                         hipStream_t stream) {
+                         int b0, int Bc, hipStream_t stream) {
   const int nvec = static_cast<int>(tab.dim * sizeof(typename TT::S) / 16);
-  if (nvec <= 1) return launch_t<TT, OT, 1, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 2) return launch_t<TT, OT, 2, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 4) return launch_t<TT, OT, 4, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 8) return launch_t<TT, OT, 8, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 16) return launch_t<TT, OT, 16, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 32) return launch_t<TT, OT, 32, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 64) return launch_t<TT, OT, 64, 1>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 128) return launch_t<TT, OT, 64, 2>(tab, bags, flags, out, nvec, stream);
-  if (nvec <= 256) return launch_t<TT, OT, 64, 4>(tab, bags, flags, out, nvec, stream);
+  if (nvec <= 1) return launch_t<TT, OT, 1, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 2) return launch_t<TT, OT, 2, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 4) return launch_t<TT, OT, 4, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 8) return launch_t<TT, OT, 8, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 16) return launch_t<TT, OT, 16, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 32) return launch_t<TT, OT, 32, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 64) return launch_t<TT, OT, 64, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 128) return launch_t<TT, OT, 64, 2>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 256) return launch_t<TT, OT, 64, 4>(tab, bags, flags, out, nvec, b0, Bc, stream);
   return set_error(EL_ERR_UNSUPPORTED, "emb_bag_fwd: rows longer than 4096 bytes are not supported");
 }
 
 template <class TT>
 el_status dispatch_out(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                       el_dtype out_dtype, hipStream_t stream) {
+                       el_dtype out_dtype, int b0, int Bc, hipStream_t stream) {
   switch (out_dtype) {
-    case EL_F32: return dispatch_shape<TT, F32T>(tab, bags, flags, out, stream);
-    case EL_F16: return dispatch_shape<TT, F16T>(tab, bags, flags, out, stream);
-    case EL_BF16: return dispatch_shape<TT, BF16T>(tab, bags, flags, out, stream);
+    case EL_F32: return dispatch_shape<TT, F32T>(tab, bags, flags, out, b0, Bc, stream);
+    case EL_F16: return dispatch_shape<TT, F16T>(tab, bags, flags, out, b0, Bc, stream);
+    case EL_BF16: return dispatch_shape<TT, BF16T>(tab, bags, flags, out, b0, Bc, stream);
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown output dtype");
 }
@@ -187,11 +191,12 @@ el_status dispatch_out(const el_tables& tab, const el_bags& bags, uint32_t flags
 }  // namespace
 
 el_status launch_emb_bag_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                             el_dtype out_dtype, hipStream_t stream) {
+                             el_dtype out_dtype, hipStream_t stream, int b0, int Bc) {
+  if (Bc < 0) Bc = bags.batch;
   switch (tab.dtype) {
-    case EL_F32: return dispatch_out<F32T>(tab, bags, flags, out, out_dtype, stream);
-    case EL_F16: return dispatch_out<F16T>(tab, bags, flags, out, out_dtype, stream);
-    case EL_BF16: return dispatch_out<BF16T>(tab, bags, flags, out, out_dtype, stream);
+    case EL_F32: return dispatch_out<F32T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
+    case EL_F16: return dispatch_out<F16T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
+    case EL_BF16: return dispatch_out<BF16T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown table dtype");
 }

@@ -7,8 +7,12 @@
 // the interaction).  Here one wavefront builds a sample's V x D tile straight in LDS: it
 // gathers the sample's table rows, sums each bag in fp32 in CSR order, rounds once to the
 // activation type (exactly as emb_bag_fwd does) and writes the rounded vectors to the LDS
-// tile (and, when asked, to emb_out for the backward); the Gram products then run on the
-// tile exactly as in dot_interact_fwd.  Results are bit-identical to the two separate calls.
+// tile (the kernel can also store them to emb_out); the Gram products then run on the tile
+// exactly as in dot_interact_fwd.  Results are bit-identical to the two separate calls.
+// Gathering sample by sample touches every table at once and so loses the L2 locality of
+// the table-major gather; the fused kernel is therefore used only when the pooled vectors
+// are not stored (inference), and emb_dot_fwd with emb_out runs the two kernels on chunks of
+// samples instead (launch_emb_dot_fwd).
 //
 // Pipeline per wavefront (grid-strided over samples j, j+G, ...): while sample j is
 // reduced and multiplied, the rows of sample j+G, the first indices of sample j+2G and the
@@ -249,9 +253,8 @@ el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, co
 template <class TT, class IT, int NU, int SPL>
 el_status launch_emb(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
                      void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
-  if (emb_out)
-    return launch_t<TT, IT, NU, SPL, true>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
-  return launch_t<TT, IT, NU, SPL, false>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+  (void)emb_out;  // the fused kernel runs only when the pooled vectors are not wanted
+  return launch_t<TT, IT, NU, SPL, false>(tab, bags, flags, x0, nullptr, out, out_stride, lds, stream);
 }
 
 // Shape classes: row units per lane (NU) and output-row chunks per lane (SPL).
@@ -285,22 +288,46 @@ el_status launch_act(const el_tables& tab, const el_bags& bags, uint32_t flags, 
 
 }  // namespace
 
-// The fused kernel covers 16-bit activations, D % 16 == 0, F <= 64, 16-byte output rows and
-// a tile that fits in LDS; EL_ERR_UNSUPPORTED (nothing enqueued) otherwise.
+// With emb_out: the gather (table-major, for its L2 locality) and the interaction run on
+// chunks of samples whose pooled vectors fit in the memory-side cache, each chunk's
+// interaction right after its gather, so that the pooled vectors are read back from that
+// cache rather than from HBM.  Without emb_out: the fused kernel, which covers 16-bit
+// activations, D % 16 == 0, F <= 64, 16-byte output rows and a tile that fits in LDS
+// (EL_ERR_UNSUPPORTED, nothing enqueued, otherwise).
 el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
                              const void* x0, el_dtype act_dtype, void* emb_out, void* out,
                              int out_stride, hipStream_t stream) {
-  const int F = tab.num_tables, D = tab.dim;
+  const int F = tab.num_tables, D = tab.dim, B = bags.batch;
+  if (emb_out) {
+    constexpr int64_t kChunkBytes = 224ll << 20;  // below the 256 MB memory-side cache
+    const int64_t es = static_cast<int64_t>(dtype_size(act_dtype));
+    const int64_t per = static_cast<int64_t>(F) * D * es;  // pooled bytes per sample
+    const int64_t nch = (per * B + kChunkBytes - 1) / kChunkBytes;
+    const int chunk = static_cast<int>((B + nch - 1) / nch);
+    for (int b0 = 0; b0 < B; b0 += chunk) {
+      const int bc = B - b0 < chunk ? B - b0 : chunk;
+      el_status st = launch_emb_bag_fwd(tab, bags, flags, emb_out, act_dtype, stream, b0, bc);
+      if (st != EL_OK) return st;
+      const int64_t b = b0;
+      st = launch_dot_fwd(static_cast<const char*>(x0) + b * D * es,
+                          static_cast<const char*>(emb_out) + b * per, act_dtype, bc, F, D,
+                          static_cast<char*>(out) + b * out_stride * es,
+                          act_dtype, out_stride, stream);
+      if (st != EL_OK) return st;
+    }
+    return EL_OK;
+  }
   const size_t V = static_cast<size_t>(F) + 1;
   const size_t obytes = (static_cast<size_t>(out_stride) * 2 + 15) / 16 * 16;
   const size_t lds = V * (D * 2 + 16) + obytes + 16;
   if (act_dtype == EL_F32 || D % 16 != 0 || F > 64 || (out_stride * 2) % 16 != 0 ||
       lds > 64 * 1024 || bags.nnz == 0 || tab.total_rows == 0)
-    return EL_ERR_UNSUPPORTED;
+    return set_error(EL_ERR_UNSUPPORTED, "emb_dot_fwd: without emb_out the shape must suit the fused "
+                                         "kernel (16-bit activations, D % 16 == 0, F <= 64, 16-byte rows)");
   switch (tab.dtype) {
-    case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
-    case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
-    case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, emb_out, out, out_stride, lds, stream);
+    case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
+    case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
+    case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
   }
   return EL_ERR_UNSUPPORTED;
 }

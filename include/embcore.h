@@ -106,13 +106,13 @@ EL_API el_status dot_interact_fwd(const void* x0, const void* emb, el_dtype in_d
  * the bottom-MLP output feed the dot interaction).  Same results, bit for bit, as
  *   emb_bag_fwd(tab, bags, flags, emb_out, act_dtype);
  *   dot_interact_fwd(x0, emb_out, act_dtype, B, F, D, out, act_dtype, out_stride);
- * with B = bags->batch, F = tab->num_tables, D = tab->dim, but each sample's pooled vectors
- * are built in on-chip memory and multiplied there, so they are not read back from HBM.
- * emb_out ([B][F][D] of act_dtype, 16-byte aligned) may be NULL when the pooled vectors are
- * not needed (inference); they are then not stored at all.  x0: [B][D], out:
- * [B][out_stride] of act_dtype.  The fused kernel covers bf16 / fp16 activations with
- * D % 16 == 0, F <= 64 and out_stride * 2 % 16 == 0; other shapes run the two calls in turn
- * (emb_out required, else EL_ERR_UNSUPPORTED).
+ * with B = bags->batch, F = tab->num_tables, D = tab->dim.  With emb_out ([B][F][D] of
+ * act_dtype, 16-byte aligned) the two kernels run on chunks of samples sized so that each
+ * chunk's pooled vectors are read back from the memory-side cache.  emb_out may be NULL
+ * when the pooled vectors are not needed (inference): one fused kernel then builds each
+ * sample's vectors in on-chip memory and never stores them; it covers bf16 / fp16
+ * activations with D % 16 == 0, F <= 64 and out_stride * 2 % 16 == 0 (other shapes:
+ * EL_ERR_UNSUPPORTED).  x0: [B][D], out: [B][out_stride] of act_dtype.
  */
 EL_API el_status emb_dot_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
                              const void* x0, el_dtype act_dtype, void* emb_out, void* out,
