@@ -71,7 +71,7 @@ __device__ inline void fetch_sample(const uint16_t* __restrict__ x0, const uint1
   const int64_t g_base = static_cast<int64_t>(b) * out_stride - static_cast<int64_t>(tile) * 8;
 #pragma unroll
   for (int u = 0; u < NQ; ++u) {
-    int q = u * 64 + static_cast<int>(threadIdx.x);
+    int q = u * 64 + static_cast<int>(threadIdx.x & 63);
     q = q < total ? q : total - 1;
     const uint16_t* src;
     if constexpr (WITH_GRAD) {
@@ -91,7 +91,7 @@ __device__ inline void put_sample(char* lds, int pitch, int goff, int trash, int
   const int nv = D / 8;
 #pragma unroll
   for (int u = 0; u < NQ; ++u) {
-    const int q = u * 64 + static_cast<int>(threadIdx.x);
+    const int q = u * 64 + static_cast<int>(threadIdx.x & 63);
     const int row = q / nv, c = q - row * nv;
     const int off = q < tile ? row * pitch + c * 16 : (q < total ? goff + (q - tile) * 16 : trash);
     *reinterpret_cast<u32x4*>(lds + off) = r[u];
@@ -100,16 +100,30 @@ __device__ inline void put_sample(char* lds, int pitch, int goff, int trash, int
 
 
 // ---------------------------------------------------------------------------------------
-// Forward, MFMA path.
-// LDS: V x D tile (pitch 2D+16) | one output row (16-byte rounded) | 16-byte scratch slot.
+// Forward, MFMA path.  WPB independent wavefronts per workgroup, each with its own LDS
+// region and its own samples (workgroups of several wavefronts let more wavefronts be
+// resident per CU than one-wavefront workgroups do).
+// LDS per wavefront: V x D tile (pitch 2D+16) | one output row (16-byte rounded) | 16-byte
+// scratch slot.
 // ---------------------------------------------------------------------------------------
-template <class IT, class OT, int NQ, int SPL>
-__global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict__ x0,
-                                                     const uint16_t* __restrict__ emb, int B, int F,
-                                                     int D, typename OT::S* __restrict__ out,
-                                                     int out_stride, int vec_out) {
+// Orders this wavefront's LDS accesses around it (the wavefront's LDS operations execute in
+// order; this keeps the compiler from moving them across).
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <class IT, class OT, int NQ, int SPL, int WPB>
+__global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __restrict__ x0,
+                                                           const uint16_t* __restrict__ emb, int B,
+                                                           int F, int D,
+                                                           typename OT::S* __restrict__ out,
+                                                           int out_stride, int vec_out,
+                                                           int wave_lds) {
   extern __shared__ uint4 smem[];
-  char* lds = reinterpret_cast<char*>(smem);
+  const int wave = threadIdx.x >> 6;
+  char* lds = reinterpret_cast<char*>(smem) + wave * wave_lds;
   using OS = typename OT::S;
   const int V = F + 1;
   const int P = V * (V - 1) / 2;
@@ -118,23 +132,24 @@ __global__ __launch_bounds__(64) void k_dot_fwd_mfma(const uint16_t* __restrict_
   const int obytes = (out_stride * static_cast<int>(sizeof(OS)) + 15) / 16 * 16;
   const int trash = obase + obytes;
   OS* ostage = reinterpret_cast<OS*>(lds + obase);
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int tile = V * (D / 8);
+  const int stride = gridDim.x * WPB;
 
   u32x4 r[NQ];
-  int b = blockIdx.x;
+  int b = blockIdx.x * WPB + wave;
   if (b < B) fetch_sample<NQ, false>(x0, emb, x0, 0, b, F, D, tile, tile, r);
-  for (; b < B; b += gridDim.x) {
+  for (; b < B; b += stride) {
     put_sample<NQ>(lds, pitch, 0, trash, D, tile, tile, r);
-    if (b + static_cast<int>(gridDim.x) < B)
-      fetch_sample<NQ, false>(x0, emb, x0, 0, b + gridDim.x, F, D, tile, tile, r);
-    __syncthreads();
+    if (b + stride < B)
+      fetch_sample<NQ, false>(x0, emb, x0, 0, b + stride, F, D, tile, tile, r);
+    wave_sync();
     // x0 copy (converted to the output type; exact when the types agree) and zero padding
     for (int d = lane; d < D; d += 64)
       ostage[d] = OT::from_f(IT::to_f(*reinterpret_cast<const uint16_t*>(lds + d * 2)));
     for (int c = D + P + lane; c < out_stride; c += 64) ostage[c] = OT::from_f(0.0f);
     gram_lower_to_lds<IT, OT>(lds, pitch, V, D, obase, trash);
-    __syncthreads();
+    wave_sync();
     OS* orow = out + static_cast<int64_t>(b) * out_stride;
     if (SPL > 0 && vec_out) {
       // a fixed number of 16-byte stores per lane (lanes past the end repeat the last chunk
@@ -414,15 +429,29 @@ int grid_for(int B, size_t lds_bytes) {
   return B < g ? B : g;
 }
 
+template <class IT, class OT, int NQ, int SPL, int WPB>
+el_status launch_fwd_w(const void* x0, const void* emb, int B, int F, int D, void* out,
+                       int out_stride, size_t wave_lds, hipStream_t stream) {
+  const int vec_out = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S)) % 16 == 0;
+  auto kern = k_dot_fwd_mfma<IT, OT, NQ, SPL, WPB>;
+  const int blocks = resident_grid(reinterpret_cast<const void*>(kern), (B + WPB - 1) / WPB,
+                                   WPB * wave_lds, 64 * WPB);
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(64 * WPB), WPB * wave_lds, stream,
+                     static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B, F, D,
+                     static_cast<typename OT::S*>(out), out_stride, vec_out, static_cast<int>(wave_lds));
+  return check_launch("dot_interact_fwd");
+}
+
+// Up to 4 wavefronts per workgroup, as many as fit in 64 KB of LDS.
 template <class IT, class OT, int NQ, int SPL>
 el_status launch_fwd_t(const void* x0, const void* emb, int B, int F, int D, void* out,
                        int out_stride, size_t lds, hipStream_t stream) {
-  const int vec_out = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S)) % 16 == 0;
-  auto kern = k_dot_fwd_mfma<IT, OT, NQ, SPL>;
-  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64)), dim3(64),
-                     lds, stream, static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B,
-                     F, D, static_cast<typename OT::S*>(out), out_stride, vec_out);
-  return check_launch("dot_interact_fwd");
+  const size_t wave_lds = (lds + 15) / 16 * 16;
+  if (4 * wave_lds <= kMaxLds)
+    return launch_fwd_w<IT, OT, NQ, SPL, 4>(x0, emb, B, F, D, out, out_stride, wave_lds, stream);
+  if (2 * wave_lds <= kMaxLds)
+    return launch_fwd_w<IT, OT, NQ, SPL, 2>(x0, emb, B, F, D, out, out_stride, wave_lds, stream);
+  return launch_fwd_w<IT, OT, NQ, SPL, 1>(x0, emb, B, F, D, out, out_stride, wave_lds, stream);
 }
 
 // Shape classes of the MFMA forward: input chunks per lane (NQ) and output-row chunks per
