@@ -81,6 +81,7 @@ __device__ inline void sgd4(typename WT::S* w, const typename Raw4<WT>::type& ol
 }
 
 constexpr int CH = kChunk;  // lookups per chunk
+constexpr int kFixChunks = 32;  // chunks per fix-up wavefront (owners on lanes 0..31)
 
 // L lanes per row, each covering 4 elements per vector, NV vectors per lane.
 template <class GT, class WT, int L, int NV>
@@ -331,9 +332,9 @@ __device__ inline void fix_long(int64_t c, uint32_t key, int64_t nchunks, int32_
   }
 }
 
-// One wavefront per 64 consecutive chunks.  Ballots give the "owner" and "through" flags of
-// its chunks (and of the 64 after them), so every owning chunk sees at once where its run
-// ends.  Runs ending at most S chunks after their owner ("short", the common case) are
+// One wavefront per kFixChunks (32) consecutive chunks.  Ballots give the "owner" flags of
+// its chunks and the "through" flags of the 128 chunks from its first, so every owning chunk
+// sees at once where its run ends.  Runs ending at most S chunks after their owner ("short", the common case) are
 // finished by lane groups of LG lanes, 64/LG owners side by side: the group loads the tail
 // partial, the S head partials (clamped to the end chunk) and the table row together, adds
 // them in chunk order and updates the row.  Longer runs are then finished one after the
@@ -347,10 +348,10 @@ __global__ __launch_bounds__(256) void k_seg_fixup(
     const uint32_t* __restrict__ bthrough, int64_t nblk) {
   constexpr int NGW = 64 / LG;  // owner groups per wavefront
   const int lane = threadIdx.x & 63;
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * 64;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kFixChunks;
   if (c0 >= nchunks) return;  // wave-uniform
   const int64_t cl = c0 + lane, ch = c0 + 64 + lane;
-  const bool own = cl < nchunks && owner[cl] != 0;
+  const bool own = lane < kFixChunks && cl < nchunks && owner[cl] != 0;
   const uint64_t tm0 = __ballot(cl < nchunks && through[cl] != 0);
   const uint64_t tm1 = __ballot(ch < nchunks && through[ch] != 0);
   // row of this lane's chunk (the last key of the chunk: the run it owns)
@@ -440,7 +441,7 @@ el_status fixup_t(const el_tables& tab, const GradWorkspace& ws, const uint32_t*
                      ws.nchunks, ws.nblk, tab.dim, nv4, ws.bsum, ws.bthrough);
   el_status st = check_launch("segment_blocksum");
   if (st != EL_OK) return st;
-  hipLaunchKernelGGL((k_seg_fixup<WT, LG, NVG, S, LF, NV>), dim3(blocks_for(ws.nchunks, 256)), dim3(256),
+  hipLaunchKernelGGL((k_seg_fixup<WT, LG, NVG, S, LF, NV>), dim3(blocks_for(ws.nchunks, 4 * kFixChunks)), dim3(256),
                      0, stream,
                      keys, ws.n, ws.nchunks, tab.dim, nv4, static_cast<typename WT::S*>(tab.base), lr,
                      static_cast<const float*>(ws.head), static_cast<const float*>(ws.tail),
