@@ -47,15 +47,19 @@ def test_train_step_full_size():
     W0, ro_h, idx_h, off_h = to_np(W), to_np(ro), to_np(idx), to_np(off)
     tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
 
-    # gather: every output, bit for bit
+    # forward as the benchmark runs it (emb_dot_fwd with pooled output): the gather bit for
+    # bit everywhere, the same bits as the two separate calls
     emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
-    elf.emb_bag_fwd(tab, bags, emb)
+    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    elf.emb_dot_fwd(tab, bags, x0, out, emb)
     r_emb = orc.emb_bag_fwd(W0, "f32", ro_h, idx_h, off_h, B, D, "bf16")
-    assert_bits(emb, r_emb, "train_step emb_bag_fwd")
+    assert_bits(emb, r_emb, "train_step emb_dot_fwd pooled output")
+    out_sep = torch.empty_like(out)
+    elf.dot_interact_fwd(x0, emb, out_sep)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_sep.view(torch.int16))
 
     # interaction forward / backward on sampled samples (each side's own pooled input)
-    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
-    elf.dot_interact_fwd(x0, emb, out)
     dx0 = torch.empty((B, D), dtype=torch.bfloat16, device=DEV)
     demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
     elf.dot_interact_bwd(x0, emb, G, dx0, demb)
@@ -105,11 +109,15 @@ def test_large_table_full_size_sampled():
     W, ro = synth.make_tables(wl, DEV)
     idx, off = synth.make_indices(wl, DEV)
     x0 = synth.make_x0(wl, DEV)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
     emb = torch.empty((B, F, D), dtype=torch.float16, device=DEV)
-    elf.emb_bag_fwd(elf.Tables(W, ro), elf.Bags(idx, off, B), emb)
+    elf.emb_bag_fwd(tab, bags, emb)
     out = torch.empty((B, wl.out_stride), dtype=torch.float16, device=DEV)
-    elf.dot_interact_fwd(x0, emb, out)
+    elf.emb_dot_fwd(tab, bags, x0, out, None)  # the fused forward, as the benchmark runs it
+    out_sep = torch.empty_like(out)
+    elf.dot_interact_fwd(x0, emb, out_sep)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_sep.view(torch.int16))
     s = sample_ids(B)
     si, so, nb = sub_batch(to_np(idx), to_np(off), F, B, s)
     Wc, roc, sic, _ = compact_tables(W, to_np(ro), si, so, F, nb)
@@ -133,9 +141,8 @@ def test_multi_hot_full_size():
     G = synth.make_dout(wl, DEV)
     tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
     emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
-    elf.emb_bag_fwd(tab, bags, emb)
     out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
-    elf.dot_interact_fwd(x0, emb, out)
+    elf.emb_dot_fwd(tab, bags, x0, out, emb)  # as the benchmark runs it
     dx0 = torch.empty((B, D), dtype=torch.bfloat16, device=DEV)
     demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
     elf.dot_interact_bwd(x0, emb, G, dx0, demb)
@@ -182,3 +189,69 @@ def test_multi_hot_full_size():
     mask = torch.ones(wl.total_rows, dtype=torch.bool, device=DEV)
     mask[torch.from_numpy(rows).to(DEV)] = False
     assert torch.equal(W[mask].view(torch.int16), W_fresh[mask].view(torch.int16))
+
+
+def test_fwd_core_full_size_fused_forward():
+    """B = 65536, 26 x 100,000 x 128 fp32 tables, bf16 activations, Zipf(1.05): the fused
+    forward without pooled output (the benchmark's forward-only configuration), every
+    output row against the two separate calls, sampled rows against the oracle."""
+    wl = synth.WORKLOADS["fwd_core"]
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    elf.emb_dot_fwd(tab, bags, x0, out, None)
+    emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb)
+    out_sep = torch.empty_like(out)
+    elf.dot_interact_fwd(x0, emb, out_sep)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_sep.view(torch.int16))
+    s = sample_ids(B)
+    si, so, nb = sub_batch(to_np(idx), to_np(off), F, B, s)
+    Wc, roc, sic, _ = compact_tables(W, to_np(ro), si, so, F, nb)
+    r_emb = orc.emb_bag_fwd(Wc, "f32", roc, sic, so, nb, D, "bf16")
+    r_out = orc.dot_interact_fwd(to_np(x0)[s], r_emb, "bf16", "bf16", wl.out_stride)
+    sel = torch.from_numpy(s).to(DEV)
+    P = wl.num_pairs
+    assert_bits(out[sel][:, :D], r_out[:, :D], "fwd_core x0 copy")
+    assert_close(out[sel][:, D:D + P], r_out[:, D:D + P], "bf16", "fwd_core pairs")
+    assert_bits(out[sel][:, D + P:], r_out[:, D + P:], "fwd_core padding")
+
+
+def test_train_small_tables_full_size_chain():
+    """B = 65536, 8 x 1000 x 16 fp32 tables (cache-resident), bf16 activations, Zipf(1.05):
+    the benchmark's calls (emb_dot_fwd with pooled output, dot_interact_bwd,
+    emb_grad_reduce_update) over the whole batch, every output against the oracle."""
+    wl = synth.WORKLOADS["train_small_tables"]
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    G = synth.make_dout(wl, DEV)
+    W0, ro_h, idx_h, off_h = to_np(W), to_np(ro), to_np(idx), to_np(off)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    emb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((B, wl.out_stride), dtype=torch.bfloat16, device=DEV)
+    elf.emb_dot_fwd(tab, bags, x0, out, emb)
+    dx0 = torch.empty((B, D), dtype=torch.bfloat16, device=DEV)
+    demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+    torch.cuda.synchronize()
+
+    r_emb = orc.emb_bag_fwd(W0, "f32", ro_h, idx_h, off_h, B, D, "bf16")
+    assert_bits(emb, r_emb, "train_small emb")
+    r_out = orc.dot_interact_fwd(to_np(x0), r_emb, "bf16", "bf16", wl.out_stride)
+    assert_close(out, r_out, "bf16", "train_small out")
+    r_dx0, r_demb = orc.dot_interact_bwd(to_np(x0), r_emb, "bf16", to_np(G), "bf16", "bf16")
+    assert_close(dx0, r_dx0, "bf16", "train_small dx0")
+    assert_close(demb, r_demb, "bf16", "train_small demb")
+    # the update on a synthetic gradient (the same input on both sides), every row
+    dsyn = synth.make_demb(wl, DEV)
+    ws = elf.alloc_workspace(tab, bags)
+    elf.emb_grad_reduce_update(tab, bags, dsyn, wl.lr, ws)
+    torch.cuda.synchronize()
+    r_W = orc.grad_reduce_update(W0, "f32", ro_h, idx_h, off_h, B, to_np(dsyn), "bf16", wl.lr)
+    assert_close(W, r_W, "f32", "train_small SGD")
