@@ -2,7 +2,8 @@
 
 One step = the whole hot path over one batch of synthetic input already resident in HBM:
   emb_dot_fwd (the gather + the interaction forward) -> dot_interact_bwd ->
-  emb_grad_reduce_update
+  emb_grad_apply, with emb_grad_prepare (the sort of the lookups, which needs only the
+  indices) on a side stream from the end of the forward, overlapping the backward
 on the train_step workload (B = 65536, 26 fp32 tables x 100,000 x 128, bf16 activations,
 Zipf(1.05) hotness-1 indices, SGD lr 0.01).  Eight distinct index batches rotate across
 steps so that no step replays the previous one's rows from cache.
@@ -138,9 +139,9 @@ def main():
                     help="time emb_bag_fwd + dot_interact_fwd instead of emb_dot_fwd (which, for "
                          "forward-only workloads, does not store the pooled vectors at all, and in "
                          "training runs the two kernels on cache-sized chunks of samples)")
-    ap.add_argument("--overlap-sort", action="store_true",
-                    help="run the gradient sort (emb_grad_prepare) on a side stream overlapping the "
-                         "forward and the interaction backward, then emb_grad_apply")
+    ap.add_argument("--overlap-sort", choices=["none", "fwd", "bwd"], default="bwd",
+                    help="run the gradient sort (emb_grad_prepare) on a side stream, from the start of "
+                         "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply")
     ap.add_argument("--no-copy-bw", action="store_true",
                     help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
     args = ap.parse_args()
@@ -173,7 +174,7 @@ def main():
         ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches),
                          dtype=torch.uint8, device=dev)
 
-    overlap = wl.backward and args.overlap_sort
+    overlap = wl.backward and args.overlap_sort != "none"
     fused_fwd = not args.separate_fwd
     fwd_names = ["emb_dot_fwd"] if fused_fwd else ["emb_bag_fwd", "dot_interact_fwd"]
     if not wl.backward:
@@ -186,19 +187,23 @@ def main():
     side = torch.cuda.Stream() if overlap else None  # default priority
     applied = torch.cuda.Event()
     prepared = torch.cuda.Event()
+    fwd_done = torch.cuda.Event()
     applied.record(main_stream)
+
+    def start_sort(bags, side_ev):
+        side.wait_event(applied)  # the workspace is free once the previous update is done
+        if side_ev: side_ev[0].record(side)
+        elf.emb_grad_prepare(tab, bags, ws, stream=side)
+        if side_ev: side_ev[1].record(side)
+        prepared.record(side)
 
     def step(i, ev=None, side_ev=None):
         """One pass of the path over batch i.  With overlap, the sort of the lookups (it needs
         only the indices) runs on a side stream while the forward and the interaction
         backward run; the update waits for it."""
         bags, x0, G = batches[i % len(batches)][:3]
-        if overlap:
-            side.wait_event(applied)  # the workspace is free once the previous update is done
-            if side_ev: side_ev[0].record(side)
-            elf.emb_grad_prepare(tab, bags, ws, stream=side)
-            if side_ev: side_ev[1].record(side)
-            prepared.record(side)
+        if overlap and args.overlap_sort == "fwd":
+            start_sort(bags, side_ev)
         if ev: ev[0].record()
         k = 1
         if fused_fwd:  # forward only: the pooled vectors are not needed afterwards
@@ -212,6 +217,10 @@ def main():
         k += 1
         if not wl.backward:
             return
+        if overlap and args.overlap_sort == "bwd":
+            fwd_done.record(main_stream)
+            side.wait_event(fwd_done)
+            start_sort(bags, side_ev)
         elf.dot_interact_bwd(x0, emb, G, dx0, demb)
         if ev: ev[k].record()
         k += 1
@@ -288,7 +297,8 @@ def main():
         if copy_gbps:
             c["frac_of_copy"] = round(c["algo_gbps"] / copy_gbps, 4)
         if n == "emb_grad_prepare":
-            c["stream"] = "side (overlaps the forward and the interaction backward)"
+            c["stream"] = "side (overlaps " + ("the forward and " if args.overlap_sort == "fwd" else "") + \
+                          "the interaction backward)"
         calls[n] = c
     step_bytes = sum(algo[n] for n in names)  # the sort's passes are not counted
     # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
