@@ -338,7 +338,9 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, W, ro, batches[0], args.cpu_seconds)
+        result["cpu_baseline"], omp = cpu_baseline(wl, W, ro, batches[0], args.cpu_seconds)
+        if omp:
+            result["cpu_baseline_openmp"] = omp
     print(json.dumps(result), flush=True)
 
 
@@ -396,12 +398,27 @@ def cpu_baseline(wl, W, ro, batch, seconds):
         dt = run(n)
     finally:
         os.sched_setaffinity(0, old)
+    # the same oracle source built with OpenMP (bags / samples over all host threads; the
+    # update stays serial), on the same sample
+    from oracle import build as obuild
+    omp = None
+    if os.path.exists(obuild.LIB_OMP):
+        prev = orc.use_library(obuild.LIB_OMP)
+        try:
+            dt_omp = run(n)
+        finally:
+            orc.restore_library(prev)
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(old)
+        omp = {"value": round(n / dt_omp, 1), "unit": "samples/s", "cores": threads,
+               "kind": "oracle, OpenMP build (forward and interaction backward threaded)",
+               "sample": f"the same {n} samples, {dt_omp:.1f} s"}
     tables = "full tables" + ("; full-table SGD copy" if wl.backward else "") if full_tables \
         else "only the looked-up rows of the tables"
-    return {"value": round(n / dt, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {B} samples of batch 0 (all {F} tables, {tables}), "
-                      f"single-threaded C oracle pinned to one core, {dt:.1f} s",
-            "host_cpu": model, "host_cpus_visible": nproc}
+    res = {"value": round(n / dt, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
+           "sample": f"first {n} of {B} samples of batch 0 (all {F} tables, {tables}), "
+                     f"single-threaded C oracle pinned to one core, {dt:.1f} s",
+           "host_cpu": model, "host_cpus_visible": nproc}
+    return res, omp
 
 
 if __name__ == "__main__":

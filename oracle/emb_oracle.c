@@ -197,25 +197,35 @@ int oracle_emb_bag_fwd(const void* W, int w_dtype, const int64_t* row_offset, in
   int64_t nbags = (int64_t)F * B;
   int rc = check_offsets(offsets, nbags);
   if (rc) return rc;
-  double* acc = (double*)malloc(sizeof(double) * (size_t)D);
-  if (!acc) return OR_NO_MEMORY;
-  for (int t = 0; t < F; ++t) {
-    for (int b = 0; b < B; ++b) {
-      int64_t g = (int64_t)t * B + b;
-      for (int d = 0; d < D; ++d) acc[d] = 0.0;
-      for (int64_t k = offsets[g]; k < offsets[g + 1]; ++k) {
-        int64_t row = resolve_row(row_offset, t, indices[k], hash);
-        if (row < 0) { free(acc); return OR_BAD_INDEX; }
-        for (int d = 0; d < D; ++d) {
-          double w = load_elem(W, w_dtype, (size_t)row * D + d);
-          acc[d] = (k == offsets[g]) ? w : acc[d] + w;
+  int bad = 0, nomem = 0;
+  /* Bags are independent; an OpenMP build splits them over threads (same arithmetic per
+   * bag, so the same bits); the plain build ignores the pragmas. */
+#pragma omp parallel reduction(| : bad, nomem)
+  {
+    double* acc = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!acc) nomem = 1;
+#pragma omp for collapse(2) schedule(static)
+    for (int t = 0; t < F; ++t) {
+      for (int b = 0; b < B; ++b) {
+        if (!acc) continue;
+        int64_t g = (int64_t)t * B + b;
+        for (int d = 0; d < D; ++d) acc[d] = 0.0;
+        for (int64_t k = offsets[g]; k < offsets[g + 1]; ++k) {
+          int64_t row = resolve_row(row_offset, t, indices[k], hash);
+          if (row < 0) { bad = 1; break; }
+          for (int d = 0; d < D; ++d) {
+            double w = load_elem(W, w_dtype, (size_t)row * D + d);
+            acc[d] = (k == offsets[g]) ? w : acc[d] + w;
+          }
         }
+        for (int d = 0; d < D; ++d)
+          store_elem(out, out_dtype, ((size_t)b * F + t) * D + d, acc[d]);
       }
-      for (int d = 0; d < D; ++d)
-        store_elem(out, out_dtype, ((size_t)b * F + t) * D + d, acc[d]);
     }
+    free(acc);
   }
-  free(acc);
+  if (nomem) return OR_NO_MEMORY;
+  if (bad) return OR_BAD_INDEX;
   return OR_OK;
 }
 
@@ -245,6 +255,7 @@ int oracle_dot_interact_fwd(const void* x0, const void* emb, int in_dtype, int B
   int V = F + 1;
   int64_t P = (int64_t)V * (V - 1) / 2;
   if (F < 1 || D < 1 || B < 0 || out_stride < D + P) return OR_BAD_SHAPE;
+#pragma omp parallel for schedule(static)
   for (int b = 0; b < B; ++b) {
     size_t row = (size_t)b * out_stride;
     for (int d = 0; d < D; ++d) store_elem(out, out_dtype, row + d, vec_elem(x0, emb, in_dtype, b, F, D, 0, d));
@@ -275,6 +286,7 @@ int oracle_dot_interact_bwd(const void* x0, const void* emb, int in_dtype, int B
   int V = F + 1;
   int64_t P = (int64_t)V * (V - 1) / 2;
   if (F < 1 || D < 1 || B < 0 || out_stride < D + P) return OR_BAD_SHAPE;
+#pragma omp parallel for schedule(static)
   for (int b = 0; b < B; ++b) {
     size_t row = (size_t)b * out_stride;
     for (int k = 0; k < V; ++k) {

@@ -550,3 +550,40 @@ def test_bad_offsets_rejected():
     offsets = np.array([0, 2, 1], np.int32)
     with pytest.raises(ValueError):
         orc.emb_bag_fwd(np.zeros((4, 2)), "f64", row_offset, np.zeros(2, np.int32), offsets, 2, 2, "f64")
+
+
+def test_openmp_build_gives_the_plain_builds_bits():
+    """The OpenMP build of the oracle (used only to time the CPU baseline on all host
+    threads) splits independent bags / samples over threads and must give the plain build's
+    bits."""
+    import os
+    from oracle import build as obuild
+    if not os.path.exists(obuild.LIB_OMP):
+        obuild.build()
+    rng = np.random.default_rng(11)
+    F, B, D = 5, 37, 24
+    rows = np.array([7, 30, 1, 12, 50])
+    ro = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    W = rng.standard_normal((int(ro[-1]), D)).astype(np.float32)
+    lens = rng.integers(0, 4, F * B)
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    t_of = np.repeat(np.arange(F).repeat(B), lens)
+    idx = (rng.integers(0, 1 << 20, off[-1]) % rows[t_of]).astype(np.int32)
+    x0 = rng.standard_normal((B, D)).astype(np.float32)
+    S = D + (F + 1) * F // 2
+    G = rng.standard_normal((B, S)).astype(np.float32)
+
+    def chain():
+        emb = orc.emb_bag_fwd(W, "f32", ro, idx, off, B, D, "f32")
+        out = orc.dot_interact_fwd(x0, emb, "f32", "f32", S)
+        dx0, demb = orc.dot_interact_bwd(x0, emb, "f32", G, "f32", "f32")
+        return [a.copy() for a in (emb, out, dx0, demb)]
+
+    plain = chain()
+    prev = orc.use_library(obuild.LIB_OMP)
+    try:
+        threaded = chain()
+    finally:
+        orc.restore_library(prev)
+    for a, b in zip(plain, threaded):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
