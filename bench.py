@@ -142,6 +142,10 @@ def main():
     ap.add_argument("--overlap-sort", choices=["none", "fwd", "bwd"], default="bwd",
                     help="run the gradient sort (emb_grad_prepare) on a side stream, from the start of "
                          "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply")
+    ap.add_argument("--inference-sweep", action="store_true",
+                    help="forward-only latency / throughput over batch sizes 1 .. 1,048,576 on the "
+                         "large fp16 tables (emb_dot_fwd, pooled vectors not stored); one JSON line "
+                         "per batch size instead of the step line")
     ap.add_argument("--no-copy-bw", action="store_true",
                     help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
     args = ap.parse_args()
@@ -156,6 +160,9 @@ def main():
         raise SystemExit("no GPU visible")
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.inference_sweep:
+        inference_sweep(dev, args.workload if args.workload != "train_step" else "large_table")
+        return
     wl = synth.WORKLOADS[args.workload]
     B, F, D = wl.batch, wl.num_tables, wl.dim
     act = synth.act_dtype(wl)
@@ -342,6 +349,42 @@ def main():
         if omp:
             result["cpu_baseline_openmp"] = omp
     print(json.dumps(result), flush=True)
+
+
+def inference_sweep(dev, workload, sizes=(1, 16, 256, 4096, 65536, 262144, 1048576), iters=100):
+    """Forward-only serving figure: for each batch size, `iters` single calls of emb_dot_fwd
+    (gather + interaction, pooled vectors kept on chip), each timed with its own HIP events;
+    latency percentiles and samples/s = B / mean latency.  Two index batches alternate."""
+    import embedding_lookup_feature_amd as elf
+    from embedding_lookup_feature_amd import synth
+    base = synth.WORKLOADS[workload]
+    W, ro = synth.make_tables(base, dev)
+    tab = elf.Tables(W, ro)
+    for B in sizes:
+        wl = base.scaled(batch=B)
+        batches = []
+        for i in range(2):
+            idx, off = synth.make_indices(wl, dev, batch_id=i)
+            batches.append((elf.Bags(idx, off, B), synth.make_x0(wl, dev, i)))
+        out = torch.empty((B, wl.out_stride), dtype=synth.act_dtype(wl), device=dev)
+        for i in range(10):
+            elf.emb_dot_fwd(tab, batches[i % 2][0], batches[i % 2][1], out, None)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for i, (e0, e1) in enumerate(ev):
+            e0.record()
+            elf.emb_dot_fwd(tab, batches[i % 2][0], batches[i % 2][1], out, None)
+            e1.record()
+        torch.cuda.synchronize()
+        lat = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        print(json.dumps({"metric": f"forward latency and samples/s, {wl.name}", "batch": B,
+                          "mean_ms": round(float(lat.mean()), 4), "p50_ms": round(pct(lat, 50), 4),
+                          "p90_ms": round(pct(lat, 90), 4), "p95_ms": round(pct(lat, 95), 4),
+                          "p99_ms": round(pct(lat, 99), 4),
+                          "samples_per_s": round(B / (float(lat.mean()) * 1e-3), 1),
+                          "iters": iters, "data": "synthetic"}), flush=True)
+        del batches, out
+        torch.cuda.empty_cache()
 
 
 def cpu_info():

@@ -7,8 +7,8 @@
 // the interaction).  Here one wavefront builds a sample's V x D tile straight in LDS: it
 // gathers the sample's table rows, sums each bag in fp32 in CSR order, rounds once to the
 // activation type (exactly as emb_bag_fwd does) and writes the rounded vectors to the LDS
-// tile (the kernel can also store them to emb_out); the Gram products then run on the tile
-// exactly as in dot_interact_fwd.  Results are bit-identical to the two separate calls.
+// tile; the Gram products then run on the tile exactly as in dot_interact_fwd.  Results are
+// bit-identical to the two separate calls.
 // Gathering sample by sample touches every table at once and so loses the L2 locality of
 // the table-major gather; the fused kernel is therefore used only when the pooled vectors
 // are not stored (inference), and emb_dot_fwd with emb_out runs the two kernels on chunks of
@@ -65,13 +65,13 @@ __device__ inline u32x4 pack8(const float* f) {
 }
 
 // TT: table type; IT: activation type (16-bit: pooled vectors, x0 and out); NU: row units
-// (8 elements) per lane; SPL: 16-byte output-row chunks per lane; EMB: store emb_out.
-template <class TT, class IT, int NU, int SPL, bool EMB>
+// (8 elements) per lane; SPL: 16-byte output-row chunks per lane.
+template <class TT, class IT, int NU, int SPL>
 __global__ __launch_bounds__(64) void k_emb_dot_fwd(
     const typename TT::S* __restrict__ W, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ idx, int32_t nnz, const int32_t* __restrict__ off, int32_t B,
     int32_t F, int32_t D, uint32_t hash, const uint16_t* __restrict__ x0,
-    uint16_t* __restrict__ emb, uint16_t* __restrict__ out, int32_t out_stride) {
+    uint16_t* __restrict__ out, int32_t out_stride) {
   extern __shared__ uint4 smem[];
   char* lds = reinterpret_cast<char*>(smem);
   using S = typename TT::S;
@@ -199,20 +199,8 @@ __global__ __launch_bounds__(64) void k_emb_dot_fwd(
     //     before this trip's stores
     issue_rows(j + G, first_row(r1, s1, e1), rows, xv);
 
-    // (4) emb_out from the tile; the interaction: x0 copy, zero padding, strict lower
-    //     triangle of the Gram matrix
+    // (4) the interaction: x0 copy, zero padding, strict lower triangle of the Gram matrix
     __syncthreads();
-    if constexpr (EMB) {
-      const int64_t eb = static_cast<int64_t>(j) * F * D;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        int q = u * 64 + lane;
-        q = q < units ? q : units - 1;
-        const int t = q / nur, c = q - t * nur;
-        *reinterpret_cast<u32x4*>(emb + eb + static_cast<int64_t>(q) * 8) =
-            *reinterpret_cast<const u32x4*>(lds + (1 + t) * pitch + c * 16);
-      }
-    }
     for (int d = lane; d < D; d += 64)
       ostage[d] = IT::from_f(IT::to_f(*reinterpret_cast<const uint16_t*>(lds + d * 2)));
     for (int c = D + P + lane; c < out_stride; c += 64) ostage[c] = 0;
@@ -236,37 +224,29 @@ __global__ __launch_bounds__(64) void k_emb_dot_fwd(
   }
 }
 
-template <class TT, class IT, int NU, int SPL, bool EMB>
+template <class TT, class IT, int NU, int SPL>
 el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
-                   void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
-  auto kern = k_emb_dot_fwd<TT, IT, NU, SPL, EMB>;
+                   void* out, int out_stride, size_t lds, hipStream_t stream) {
+  auto kern = k_emb_dot_fwd<TT, IT, NU, SPL>;
   const int B = bags.batch;
   hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64)),
                      dim3(64), lds, stream, static_cast<const typename TT::S*>(tab.base),
                      tab.row_offset, bags.indices, static_cast<int32_t>(bags.nnz), bags.offsets, B,
                      tab.num_tables, tab.dim, (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
-                     static_cast<const uint16_t*>(x0), static_cast<uint16_t*>(emb_out),
-                     static_cast<uint16_t*>(out), out_stride);
+                     static_cast<const uint16_t*>(x0), static_cast<uint16_t*>(out), out_stride);
   return check_launch("emb_dot_fwd");
-}
-
-template <class TT, class IT, int NU, int SPL>
-el_status launch_emb(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
-                     void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
-  (void)emb_out;  // the fused kernel runs only when the pooled vectors are not wanted
-  return launch_t<TT, IT, NU, SPL, false>(tab, bags, flags, x0, nullptr, out, out_stride, lds, stream);
 }
 
 // Shape classes: row units per lane (NU) and output-row chunks per lane (SPL).
 template <class TT, class IT>
 el_status launch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
-                       void* emb_out, void* out, int out_stride, size_t lds, hipStream_t stream) {
+                       void* out, int out_stride, size_t lds, hipStream_t stream) {
   const int units = tab.num_tables * (tab.dim / 8);
   const int ochunks = (out_stride * 2 + 15) / 16;
 #define EL_SPL(NU)                                                                                   \
   do {                                                                                               \
-    if (ochunks <= 64) return launch_emb<TT, IT, NU, 1>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream); \
-    if (ochunks <= 256) return launch_emb<TT, IT, NU, 4>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream); \
+    if (ochunks <= 64) return launch_t<TT, IT, NU, 1>(tab, bags, flags, x0, out, out_stride, lds, stream); \
+    if (ochunks <= 256) return launch_t<TT, IT, NU, 4>(tab, bags, flags, x0, out, out_stride, lds, stream); \
   } while (0)
   if (units <= 2 * 64) EL_SPL(2);
   else if (units <= 4 * 64) EL_SPL(4);
@@ -279,10 +259,10 @@ el_status launch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags
 
 template <class TT>
 el_status launch_act(const el_tables& tab, const el_bags& bags, uint32_t flags, const void* x0,
-                     el_dtype act, void* emb_out, void* out, int out_stride, size_t lds,
+                     el_dtype act, void* out, int out_stride, size_t lds,
                      hipStream_t stream) {
-  if (act == EL_BF16) return launch_shape<TT, BF16T>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
-  if (act == EL_F16) return launch_shape<TT, F16T>(tab, bags, flags, x0, emb_out, out, out_stride, lds, stream);
+  if (act == EL_BF16) return launch_shape<TT, BF16T>(tab, bags, flags, x0, out, out_stride, lds, stream);
+  if (act == EL_F16) return launch_shape<TT, F16T>(tab, bags, flags, x0, out, out_stride, lds, stream);
   return EL_ERR_UNSUPPORTED;
 }
 
@@ -325,9 +305,9 @@ el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t
     return set_error(EL_ERR_UNSUPPORTED, "emb_dot_fwd: without emb_out the shape must suit the fused "
                                          "kernel (16-bit activations, D % 16 == 0, F <= 64, 16-byte rows)");
   switch (tab.dtype) {
-    case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
-    case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
-    case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, nullptr, out, out_stride, lds, stream);
+    case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
+    case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
+    case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
   }
   return EL_ERR_UNSUPPORTED;
 }
