@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "el_internal.hpp"
@@ -30,21 +31,21 @@ namespace el {
 // from the kernel's registers and LDS), never more than there are samples.
 int resident_grid(const void* kernel, int B, size_t lds_bytes, int block) {
   static std::mutex mu;
-  static std::map<std::pair<const void*, size_t>, int> cache;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;  // (device, kernel, LDS)
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   int per_cu = 0;
   {
     std::lock_guard<std::mutex> lock(mu);
-    auto it = cache.find({kernel, lds_bytes});
+    auto it = cache.find({dev, kernel, lds_bytes});
     if (it != cache.end()) {
       per_cu = it->second;
     } else {
-      int n = 0, cus = 0, dev = 0;
+      int n = 0, cus = 0;
       if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, block, lds_bytes) != hipSuccess) n = 4;
-      if (hipGetDevice(&dev) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 256;
       per_cu = (n > 0 ? n : 1) * (cus > 0 ? cus : 256);
-      cache[{kernel, lds_bytes}] = per_cu;
+      cache[{dev, kernel, lds_bytes}] = per_cu;
     }
   }
   return B < per_cu ? B : per_cu;

@@ -76,18 +76,21 @@ __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ 
   }
 }
 
-// Digit counts of one tile (LDS atomics into one sub-histogram per wavefront, so that only
-// lanes of one wavefront contend; counts do not depend on the order of the adds).
+// Digit counts of one tile.  LDS atomics into kSub sub-histograms (wavefront and lane group),
+// so that few lanes contend for one counter even when a tile holds many equal keys (the hot
+// rows of skewed indices); counts do not depend on the order of the adds.
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
                                                     int shift, uint32_t* __restrict__ hist,
                                                     int nblocks) {
   constexpr int kRadix = 1 << RB;
   constexpr int kSteps = kSortTile / 256;
-  __shared__ uint32_t cnt[4][kRadix];
-  for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+  constexpr int kLaneGroups = RB <= 8 ? 8 : 2;  // sub-histograms per wavefront
+  constexpr int kSub = 4 * kLaneGroups;
+  __shared__ uint32_t cnt[kSub][kRadix];
+  for (int i = threadIdx.x; i < kSub * kRadix; i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  const int w = threadIdx.x >> 6;
+  const int sub = (threadIdx.x >> 6) * kLaneGroups + (threadIdx.x & 63) % kLaneGroups;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kSortTile + threadIdx.x;
   uint32_t kk[kSteps];
 #pragma unroll
@@ -97,10 +100,14 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
   }
 #pragma unroll
   for (int st = 0; st < kSteps; ++st)
-    if (base + st * 256 < n) atomicAdd(&cnt[w][(kk[st] >> shift) & (kRadix - 1)], 1u);
+    if (base + st * 256 < n) atomicAdd(&cnt[sub][(kk[st] >> shift) & (kRadix - 1)], 1u);
   __syncthreads();
-  for (int dg = threadIdx.x; dg < kRadix; dg += 256)
-    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = cnt[0][dg] + cnt[1][dg] + cnt[2][dg] + cnt[3][dg];
+  for (int dg = threadIdx.x; dg < kRadix; dg += 256) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) c += cnt[k][dg];
+    hist[static_cast<int64_t>(dg) * nblocks + blockIdx.x] = c;
+  }
 }
 
 // Exclusive scan of x over the 256 threads of a block (every thread gets its prefix; `total`
