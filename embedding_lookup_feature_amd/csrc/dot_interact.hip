@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
   const int P = V * (V - 1) / 2;
   const int NT = (V + 31) / 32;
   const int VP = NT * 32;
-  const int DT = D / 32;
+  const int DT = (D + 31) / 32;  // D % 16 == 0; a last tile of 16 rows is half empty
   const int tpitch = VP * 2 + 16;
   const int goff = D * tpitch;
   const int gchunks = (D + P + 7) / 8;
@@ -301,16 +301,19 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
         }
       }
       f32x16 acc = {};
-      const char* arow = lds + (dt * 32 + col) * tpitch + half * 16;
+      const int arow = (dt * 32 + col) * tpitch + half * 16;
+      const bool dok = dt * 32 + col < D;  // rows of V^T past D are zero
 #pragma unroll
       for (int ks = 0; ks < KSM; ++ks)
-        if (ks < KS) acc = mfma32<IT>(*reinterpret_cast<const u32x4*>(arow + ks * 32), Sop[ks], acc);
+        if (ks < KS) acc = mfma32<IT>(lds16_or_zero(lds, arow + ks * 32, dok), Sop[ks], acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d0 = dt * 32 + q * 8 + half * 4;
-        float f[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
-        store_n<GT, 4>(reinterpret_cast<GS*>(lds + ooff + v * opitch + d0 * GSZ), f);
-        if (v == 0) store_n<F32T, 4>(reinterpret_cast<float*>(lds + r0off + d0 * 4), f);
+        if (d0 < D) {
+          float f[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+          store_n<GT, 4>(reinterpret_cast<GS*>(lds + ooff + v * opitch + d0 * GSZ), f);
+          if (v == 0) store_n<F32T, 4>(reinterpret_cast<float*>(lds + r0off + d0 * 4), f);
+        }
       }
     }
     __syncthreads();
@@ -541,7 +544,9 @@ el_status bwd_typed(const void* x0, const void* emb, int B, int F, int D, const 
     const size_t lds = static_cast<size_t>(D) * (VP * 2 + 16) + gchunks * 16 +
                        VP * (D * sizeof(typename GT::S) + 16) + static_cast<size_t>(D) * 4 + 16;
     // 16-byte chunks of the gradient row must stay inside the row: stride multiple of 8
-    if (D % 32 == 0 && V <= 128 && lds <= kMaxLds && out_stride % 8 == 0) {
+    // D = 16: the fp32 FMA kernel (one wavefront per sample) is faster than a half-empty
+    // 32-row MFMA tile driven by four wavefronts
+    if (D % 16 == 0 && D >= 32 && V <= 128 && lds <= kMaxLds && out_stride % 8 == 0) {
       const el_status st = launch_bwd_mfma<IT, GT>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
       if (st != EL_ERR_UNSUPPORTED) return st;
     }

@@ -193,6 +193,8 @@ BWD_CASES = [
     ("bf16-128-vectors", 127, 32, "bf16", "bf16", "bf16", None, 8),
     ("bf16-f32-dout-fma-path", 26, 128, "bf16", "f32", "bf16", None, 50),
     ("bf16-d16-fma-path", 8, 16, "bf16", "bf16", "bf16", None, 70),
+    ("f16-d48-half-tile", 26, 48, "f16", "f16", "f16", None, 300),
+    ("bf16-d24-fma-path", 5, 24, "bf16", "bf16", "bf16", None, 50),
 ]
 
 
