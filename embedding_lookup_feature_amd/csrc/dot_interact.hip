@@ -20,6 +20,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <type_traits>
 #include <utility>
 
 #include "el_internal.hpp"
@@ -175,7 +176,8 @@ __global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __res
 //   B = S    (lane: one vector v, 8 consecutive vectors)     -> rebuilt from the gradient row,
 //   C = dV^T (lane: one vector v, runs of 4 consecutive d)   -> 8-byte LDS writes.
 // A workgroup of 4 wavefronts works on one sample at a time (grid-strided over samples,
-// the next sample's loads issued before the current one is computed).  Loading: every
+// the loads of the sample PD strides ahead issued before the current one is computed,
+// into one of PD register buffers).  Loading: every
 // thread takes pairs of rows of one 8-element column block (2 x 16-byte loads), interleaves
 // them into 8 two-vector words and writes those into V^T.  Compute: the 32 x 32 output
 // tiles (vector tile, dimension tile) are dealt round-robin to the 4 wavefronts.  Store:
@@ -183,9 +185,16 @@ __global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __res
 // there from an fp32 copy of dV_0.  dout has the input's 16-bit type (S is then exact).
 // LDS: V^T [D][VP] | gradient row | VP x D output block | dV_0 in fp32 | scratch slot.
 // UPT: row pairs per thread; GPT: gradient-row chunks per thread held in registers
-// (0: loaded straight into LDS when the sample starts); KSM: K steps (>= KS).
+// (0: loaded straight into LDS when the sample starts); KSM: K steps (>= KS); PD: samples
+// in flight per workgroup (1, or 2 with GPT > 0: a third measured no faster).
 // ---------------------------------------------------------------------------------------
-template <class IT, class GT, int UPT, int GPT, int KSM>
+template <int N>
+using Buf = std::integral_constant<int, N>;
+
+// An empty register use: the compiler waits here for the load that produced `v`.
+__device__ inline void settle(const u32x4& v) { asm volatile("" ::"v"(v)); }
+
+template <class IT, class GT, int UPT, int GPT, int KSM, int PD>
 __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
                                                       const uint16_t* __restrict__ emb, int B, int F,
                                                       int D, const uint16_t* __restrict__ dout,
@@ -215,9 +224,13 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
   const int npairs = VP / 2;
   const int units = npairs * (D / 8);  // (row pair, column block); row pair fastest
 
-  u32x4 t[UPT][2];
-  u32x4 g[GPT > 0 ? GPT : 1];
-  auto fetch = [&](int bb) {
+  static_assert(PD == 1 || (PD == 2 && GPT > 0),
+                "several samples in flight need the gradient row in registers");
+  u32x4 t[PD][UPT][2];
+  u32x4 g[PD][GPT > 0 ? GPT : 1];
+  // Loads of sample bb into register buffer BF.
+  auto fetch = [&](int bb, auto bf) {
+    constexpr int BF = decltype(bf)::value;
     const int64_t xb = static_cast<int64_t>(bb) * D;
     const int64_t eb = static_cast<int64_t>(bb) * F * D - D;  // row v >= 1 at eb + v * D
 #pragma unroll
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
         const int v = rp * 2 + m;
         const int vc = v < V ? v : 0;
         const uint16_t* src = (vc == 0 ? x0 + xb : emb + eb + static_cast<int64_t>(vc) * D) + c * 8;
-        t[uu][m] = *reinterpret_cast<const u32x4*>(src);  // rows >= V are masked in put()
+        t[BF][uu][m] = *reinterpret_cast<const u32x4*>(src);  // rows >= V are masked in put()
       }
     }
     if constexpr (GPT > 0) {
@@ -239,17 +252,31 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
       for (int gg = 0; gg < GPT; ++gg) {
         int q = gg * 256 + tid;
         q = q < gchunks ? q : gchunks - 1;
-        g[gg] = *reinterpret_cast<const u32x4*>(dout + gb + q * 8);
+        g[BF][gg] = *reinterpret_cast<const u32x4*>(dout + gb + q * 8);
       }
     }
   };
-  auto put = [&](int bb) {
+  auto settle_buf = [&](auto bf) {
+    constexpr int BF = decltype(bf)::value;
+#pragma unroll
+    for (int uu = 0; uu < UPT; ++uu) {
+      settle(t[BF][uu][0]);
+      settle(t[BF][uu][1]);
+    }
+    if constexpr (GPT > 0) {
+#pragma unroll
+      for (int gg = 0; gg < GPT; ++gg) settle(g[BF][gg]);
+    }
+  };
+  // Register buffer BF (sample bb) -> LDS.
+  auto put = [&](int bb, auto bf) {
+    constexpr int BF = decltype(bf)::value;
 #pragma unroll
     for (int uu = 0; uu < UPT; ++uu) {
       const int u = uu * 256 + tid;
       const int c = u / npairs, rp = u - c * npairs;
-      const u32x4 r0 = rp * 2 < V ? t[uu][0] : u32x4{0, 0, 0, 0};
-      const u32x4 r1 = rp * 2 + 1 < V ? t[uu][1] : u32x4{0, 0, 0, 0};
+      const u32x4 r0 = rp * 2 < V ? t[BF][uu][0] : u32x4{0, 0, 0, 0};
+      const u32x4 r1 = rp * 2 + 1 < V ? t[BF][uu][1] : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // value e of both rows, row 2rp in the low half: V^T[c*8 + e][2rp .. 2rp+1]
@@ -264,7 +291,7 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
 #pragma unroll
       for (int gg = 0; gg < GPT; ++gg) {
         const int q = gg * 256 + tid;
-        *reinterpret_cast<u32x4*>(lds + (q < gchunks ? goff + q * 16 : trash)) = g[gg];
+        *reinterpret_cast<u32x4*>(lds + (q < gchunks ? goff + q * 16 : trash)) = g[BF][gg];
       }
     } else {
       const uint16_t* grow = dout + static_cast<int64_t>(bb) * out_stride;
@@ -273,11 +300,13 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
     }
   };
 
-  int b = blockIdx.x;
-  if (b < B) fetch(b);
-  for (; b < B; b += gridDim.x) {
-    put(b);
-    if (b + static_cast<int>(gridDim.x) < B) fetch(b + gridDim.x);
+  // One sample: LDS fill from buffer BF, that buffer refilled with the sample PD strides
+  // on (clamped to the last sample, so that every trip issues the same loads and stores
+  // and the compiler's wait counts stay exact), compute, store.
+  const int NG = gridDim.x;
+  auto sample = [&](int b, auto bf) {
+    put(b, bf);
+    fetch(min(b + PD * NG, B - 1), bf);
     __syncthreads();
     int cur_vt = -1;
     u32x4 Sop[KSM];  // S[v][k], k = 16 ks + 8 half + e
@@ -332,14 +361,35 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
       *reinterpret_cast<uint4*>(derow + static_cast<int64_t>(q) * 16) =
           *reinterpret_cast<const uint4*>(lds + ooff + row * opitch + c * 16);
     }
-    constexpr int EPC = 16 / GSZ;  // elements per 16-byte chunk of the gradient
     {
-      const int q = tid < nv ? tid : nv - 1;
-      float f[EPC];
+      // Thread q takes the 8 values of gradient-row chunk q, the chunk it wrote itself in
+      // put(): the next sample's put() cannot overwrite them before they are read.
+      const int nd = D / 8;
+      const int q = tid < nd ? tid : nd - 1;
+      float f[8];
 #pragma unroll
-      for (int x = 0; x < EPC; ++x)
-        f[x] = reinterpret_cast<const float*>(lds + r0off)[q * EPC + x] + IT::to_f(G[q * EPC + x]);
-      store_n<GT, EPC>(dx0 + static_cast<int64_t>(b) * D + q * EPC, f);
+      for (int x = 0; x < 8; ++x)
+        f[x] = reinterpret_cast<const float*>(lds + r0off)[q * 8 + x] + IT::to_f(G[q * 8 + x]);
+      store_n<GT, 8>(dx0 + static_cast<int64_t>(b) * D + q * 8, f);
+    }
+  };
+
+  int b = blockIdx.x;
+  if (b >= B) return;
+  // Prologue loads land before the loop (settle), so that the wait counts the compiler
+  // derives for the loop are those of its steady state alone.
+  fetch(b, Buf<0>{});
+  if constexpr (PD == 2) fetch(min(b + NG, B - 1), Buf<1>{});
+  settle_buf(Buf<0>{});
+  if constexpr (PD == 2) settle_buf(Buf<1>{});
+  for (;;) {
+    sample(b, Buf<0>{});
+    b += NG;
+    if (b >= B) break;
+    if constexpr (PD == 2) {
+      sample(b, Buf<1>{});
+      b += NG;
+      if (b >= B) break;
     }
   }
 }
@@ -498,10 +548,10 @@ el_status fwd_typed(const void* x0, const void* emb, int B, int F, int D, void* 
   return check_launch("dot_interact_fwd");
 }
 
-template <class IT, class GT, int UPT, int GPT, int KSM>
+template <class IT, class GT, int UPT, int GPT, int KSM, int PD>
 el_status launch_bwd_t(const void* x0, const void* emb, int B, int F, int D, const void* dout,
                        int out_stride, void* dx0, void* demb, size_t lds, hipStream_t stream) {
-  auto kern = k_dot_bwd_mfma<IT, GT, UPT, GPT, KSM>;
+  auto kern = k_dot_bwd_mfma<IT, GT, UPT, GPT, KSM, PD>;
   hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 256)),
                      dim3(256), lds, stream, static_cast<const uint16_t*>(x0),
                      static_cast<const uint16_t*>(emb), B, F, D, static_cast<const uint16_t*>(dout),
@@ -520,15 +570,15 @@ el_status launch_bwd_mfma(const void* x0, const void* emb, int B, int F, int D, 
   const int gchunks = (D + V * (V - 1) / 2 + 7) / 8;
   if (V <= 32) {
     if (units <= 256 && gchunks <= 256)
-      return launch_bwd_t<IT, GT, 1, 1, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+      return launch_bwd_t<IT, GT, 1, 1, 2, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 512 && gchunks <= 512)
-      return launch_bwd_t<IT, GT, 2, 2, 2>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+      return launch_bwd_t<IT, GT, 2, 2, 2, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   } else if (V <= 64) {
-    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 4>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 4>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   } else if (V <= 128) {
-    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
-    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 8>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   }
   return EL_ERR_UNSUPPORTED;
 }

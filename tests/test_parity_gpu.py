@@ -185,6 +185,10 @@ BWD_CASES = [
     # label, F, D, in dtype, dout dtype, grad dtype, stride, B
     ("f32-tiny", 8, 16, "f32", "f32", "f32", None, 300),
     ("bf16-27x128", 26, 128, "bf16", "bf16", "bf16", None, 1000),
+    # several samples per workgroup: both register buffers of the two-deep prefetch in turn,
+    # an odd number of samples, the clamped prefetch past the last sample
+    ("bf16-27x128-many-trips", 26, 128, "bf16", "bf16", "bf16", None, 5001),
+    ("bf16-27x256-f32-grad", 26, 256, "bf16", "bf16", "f32", None, 700),
     ("f16-27x128", 26, 128, "f16", "f16", "f16", None, 300),
     ("bf16-101x64", 100, 64, "bf16", "bf16", "bf16", None, 60),
     ("bf16-101x64-odd-stride", 100, 64, "bf16", "bf16", "bf16", 5114 + 1, 20),
