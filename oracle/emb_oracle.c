@@ -13,6 +13,9 @@
  *     strict lower triangle of the (F+1) x (F+1) Gram matrix of the vectors of a sample.
  *   - §Command-line options, --hash_indices: an index is replaced by index mod table size.
  *   - §Command-line options, --lr / --embedding_dim: plain SGD on the embedding rows.
+ *   - §Model architecture and --bottom_mlp_sizes / --top_mlp_sizes: the dense layers of the
+ *     bottom and top MLPs (forward, backward), a logistic loss on the final logit, and plain
+ *     SGD on the dense parameters.
  * Where the page is silent (sum pooling over CSR bags, pair order, concat order, zero
  * padding, rounding), the plainest reading is taken; the readings are listed in the
  * repository's design notes.
@@ -418,4 +421,126 @@ int oracle_grad_reduce_update(void* W, int w_dtype, const int64_t* row_offset, i
   return OR_OK;
 }
 
-int oracle_version(void) { return 1; }
+/* ------------------------------------------------------------------------------------ */
+/* Dense layers, logistic loss, dense SGD                                                */
+/* ------------------------------------------------------------------------------------ */
+/*
+ * Page "DLRM For PyTorch", §Model architecture: the dense features go through the bottom
+ * MLP, a series of linear layers each followed by a ReLU; the concatenated interaction
+ * output goes through the top MLP, a series of dense layers with activations, and the model
+ * ends in one number read as the likelihood of a click.  §Command-line options gives the
+ * layer widths (--bottom_mlp_sizes 512,256,128; --top_mlp_sizes 1024,1024,512,256,1).
+ * The page names no loss; a click likelihood from one logit is read as the logistic
+ * (binary cross-entropy) loss, averaged over the batch.  Weights follow the usual dense
+ * layer layout: w[n][k] maps input feature k to output feature n.
+ */
+
+/*
+ * Forward of one dense layer:
+ *   y[m][n] = act( sum_k x[m][k] * w[n][k] + bias[n] ),   act = ReLU (max(., 0)) or identity.
+ * x is [M] rows of stride ldx (the first K used), w is [N][K], bias is fp32 [N] or NULL,
+ * y is [M] rows of stride ldy (the first N written).  One rounding per output.
+ */
+int oracle_linear_fwd(const void* x, int x_dtype, int M, int K, int ldx, const void* w,
+                      int w_dtype, int N, const float* bias, int relu, void* y, int y_dtype,
+                      int ldy) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return OR_BAD_DTYPE;
+  if (M < 0 || K < 1 || N < 1 || ldx < K || ldy < N) return OR_BAD_SHAPE;
+#pragma omp parallel for schedule(static)
+  for (int m = 0; m < M; ++m) {
+    for (int n = 0; n < N; ++n) {
+      double s = 0.0;
+      for (int k = 0; k < K; ++k)
+        s += load_elem(x, x_dtype, (size_t)m * ldx + k) * load_elem(w, w_dtype, (size_t)n * K + k);
+      if (bias) s += (double)bias[n];
+      if (relu && !(s > 0.0)) s = 0.0;
+      store_elem(y, y_dtype, (size_t)m * ldy + n, s);
+    }
+  }
+  return OR_OK;
+}
+
+/*
+ * Backward of one dense layer, given dz = dL/d(pre-activation) [M][N] (stride ldz):
+ *   dx[m][k] = sum_n dz[m][n] * w[n][k]         (times 1[xmask[m][k] > 0] when xmask is given:
+ *                                                 the ReLU of the layer below, whose output
+ *                                                 x is; this makes dx the dz of that layer)
+ *   dw[n][k] = sum_m dz[m][n] * x[m][k]
+ *   db[n]    = sum_m dz[m][n]
+ * dx (stride ldx) may be NULL (first layer).  Sums in double, ascending index order, one
+ * rounding per output.
+ */
+int oracle_linear_bwd(const void* x, int x_dtype, int M, int K, int ldx, const void* w,
+                      int w_dtype, int N, const void* dz, int dz_dtype, int ldz,
+                      const void* xmask, void* dx, int dx_dtype, void* dw, void* db,
+                      int wgrad_dtype) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(dz_dtype) || !dtype_ok(dx_dtype) ||
+      !dtype_ok(wgrad_dtype))
+    return OR_BAD_DTYPE;
+  if (M < 0 || K < 1 || N < 1 || ldx < K || ldz < N) return OR_BAD_SHAPE;
+  if (dx) {
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; ++m) {
+      for (int k = 0; k < K; ++k) {
+        double s = 0.0;
+        for (int n = 0; n < N; ++n)
+          s += load_elem(dz, dz_dtype, (size_t)m * ldz + n) * load_elem(w, w_dtype, (size_t)n * K + k);
+        if (xmask && !(load_elem(xmask, x_dtype, (size_t)m * ldx + k) > 0.0)) s = 0.0;
+        store_elem(dx, dx_dtype, (size_t)m * ldx + k, s);
+      }
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int n = 0; n < N; ++n) {
+    for (int k = 0; k < K; ++k) {
+      double s = 0.0;
+      for (int m = 0; m < M; ++m)
+        s += load_elem(dz, dz_dtype, (size_t)m * ldz + n) * load_elem(x, x_dtype, (size_t)m * ldx + k);
+      store_elem(dw, wgrad_dtype, (size_t)n * K + k, s);
+    }
+    double s = 0.0;
+    for (int m = 0; m < M; ++m) s += load_elem(dz, dz_dtype, (size_t)m * ldz + n);
+    store_elem(db, wgrad_dtype, (size_t)n, s);
+  }
+  return OR_OK;
+}
+
+/*
+ * Logistic loss on one logit per sample, label y in {0, 1} (fp32):
+ *   loss = (1/M) sum_m [ max(z,0) - z*y + log(1 + exp(-|z|)) ]      (= -log p or -log(1-p),
+ *                                                                     p = 1/(1+exp(-z)))
+ *   dz[m] = (p_m - y_m) / M
+ * `loss` receives the double value; dz is rounded once to dz_dtype.
+ */
+int oracle_bce_logits(const void* z, int z_dtype, const float* labels, int M, double* loss,
+                      void* dz, int dz_dtype) {
+  if (!dtype_ok(z_dtype) || !dtype_ok(dz_dtype)) return OR_BAD_DTYPE;
+  if (M < 1) return OR_BAD_SHAPE;
+  double s = 0.0;
+  for (int m = 0; m < M; ++m) {
+    double v = load_elem(z, z_dtype, (size_t)m), y = (double)labels[m];
+    s += (v > 0.0 ? v : 0.0) - v * y + log1p(exp(-fabs(v)));
+    double p = 1.0 / (1.0 + exp(-v));
+    store_elem(dz, dz_dtype, (size_t)m, (p - y) / (double)M);
+  }
+  *loss = s / (double)M;
+  return OR_OK;
+}
+
+/*
+ * Plain SGD on a dense parameter kept in fp32 (the page keeps the MLPs in mixed precision:
+ * an fp32 master copy, a 16-bit copy for the products):
+ *   master[i] <- round_f32( master[i] - lr * grad[i] ),   copy[i] <- round_copy( master[i] )
+ * copy may be NULL.
+ */
+int oracle_sgd_dense(float* master, const float* grad, int64_t n, float lr, void* copy,
+                     int copy_dtype) {
+  if (copy && !dtype_ok(copy_dtype)) return OR_BAD_DTYPE;
+  for (int64_t i = 0; i < n; ++i) {
+    master[i] = (float)((double)master[i] - (double)lr * (double)grad[i]);
+    if (copy) store_elem(copy, copy_dtype, (size_t)i, (double)master[i]);
+  }
+  return OR_OK;
+}
+
+int oracle_version(void) { return 2; }

@@ -50,8 +50,14 @@ def _configure(L):
                                             ctypes.c_float]
     L.oracle_round_f64.argtypes = [vp, i64, i32, vp]
     L.oracle_widen.argtypes = [vp, i64, i32, vp]
+    L.oracle_linear_fwd.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, i32]
+    L.oracle_linear_bwd.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, i32, i32, vp, vp,
+                                    i32, vp, vp, i32]
+    L.oracle_bce_logits.argtypes = [vp, i32, vp, i32, vp, vp, i32]
+    L.oracle_sgd_dense.argtypes = [vp, vp, i64, ctypes.c_float, vp, i32]
     for name in ("oracle_emb_bag_fwd", "oracle_dot_interact_fwd", "oracle_dot_interact_bwd",
-                 "oracle_grad_sort", "oracle_grad_reduce_update", "oracle_version"):
+                 "oracle_grad_sort", "oracle_grad_reduce_update", "oracle_linear_fwd",
+                 "oracle_linear_bwd", "oracle_bce_logits", "oracle_sgd_dense", "oracle_version"):
         getattr(L, name).restype = ctypes.c_int
     L.oracle_round_f64.restype = None
     L.oracle_widen.restype = None
@@ -174,6 +180,70 @@ def grad_reduce_update(W, w_dtype, row_offset, indices, offsets, batch, demb, gr
                                            int(hash_indices), _ptr(demb), _CODES[grad_dtype],
                                            ctypes.c_float(lr)))
     return W
+
+
+def linear_fwd(x, x_dtype, w, w_dtype, bias, relu, y_dtype, K=None, ldy=None):
+    """Dense layer forward y = act(x[:, :K] w^T + bias); x [M][ldx], w [N][K], bias fp32 [N]
+    or None.  Returns y [M][ldy] (columns past N untouched: the NaN fill of ``empty``)."""
+    x = _as(x, x_dtype)
+    w = _as(w, w_dtype)
+    M, ldx = x.shape
+    N, Kw = w.shape
+    K = Kw if K is None else K
+    assert K == Kw
+    ldy = N if ldy is None else ldy
+    y = empty((M, ldy), y_dtype)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    _check(lib().oracle_linear_fwd(_ptr(x), _CODES[x_dtype], M, K, ldx, _ptr(w), _CODES[w_dtype],
+                                   N, None if b is None else _ptr(b), int(bool(relu)), _ptr(y),
+                                   _CODES[y_dtype], ldy))
+    return y
+
+
+def linear_bwd(x, x_dtype, w, w_dtype, dz, dz_dtype, dx_dtype=None, relu_mask=False,
+               wgrad_dtype="f32"):
+    """Dense layer backward from dz = dL/d(pre-activation) [M][ldz].
+
+    Returns (dx [M][ldx] or None, dw [N][K], db [N]).  dx is computed when `dx_dtype` is given;
+    with `relu_mask` it is multiplied by 1[x > 0] (the ReLU of the layer below)."""
+    x = _as(x, x_dtype)
+    w = _as(w, w_dtype)
+    dz = _as(dz, dz_dtype)
+    M, ldx = x.shape
+    N, K = w.shape
+    ldz = dz.shape[1]
+    dx = None if dx_dtype is None else empty((M, ldx), dx_dtype)
+    dw = empty((N, K), wgrad_dtype)
+    db = empty((N,), wgrad_dtype)
+    _check(lib().oracle_linear_bwd(_ptr(x), _CODES[x_dtype], M, K, ldx, _ptr(w), _CODES[w_dtype],
+                                   N, _ptr(dz), _CODES[dz_dtype], ldz,
+                                   _ptr(x) if relu_mask else None,
+                                   None if dx is None else _ptr(dx),
+                                   _CODES[dx_dtype or "f32"], _ptr(dw), _ptr(db),
+                                   _CODES[wgrad_dtype]))
+    return dx, dw, db
+
+
+def bce_logits(z, z_dtype, labels, dz_dtype):
+    """Batch-mean logistic loss on logits z [M] (labels fp32 in {0,1}); returns (loss, dz)."""
+    z = _as(z, z_dtype).reshape(-1)
+    labels = np.ascontiguousarray(labels, dtype=np.float32).reshape(-1)
+    loss = np.zeros(1, np.float64)
+    dz = empty(z.shape, dz_dtype)
+    _check(lib().oracle_bce_logits(_ptr(z), _CODES[z_dtype], _ptr(labels), z.size, _ptr(loss),
+                                   _ptr(dz), _CODES[dz_dtype]))
+    return float(loss[0]), dz
+
+
+def sgd_dense(master, grad, lr, copy_dtype=None):
+    """SGD on an fp32 master copy; returns (new master, 16-bit copy or None).  Inputs are
+    not modified."""
+    master = np.array(np.ascontiguousarray(master, dtype=np.float32), copy=True)
+    grad = np.ascontiguousarray(grad, dtype=np.float32)
+    copy = None if copy_dtype is None else empty(master.shape, copy_dtype)
+    _check(lib().oracle_sgd_dense(_ptr(master), _ptr(grad), master.size, ctypes.c_float(lr),
+                                  None if copy is None else _ptr(copy), _CODES[copy_dtype or "f32"]))
+    return master, copy
 
 
 def use_library(path):

@@ -39,6 +39,23 @@ MUTANTS = [
      "double r = floor(n) * quantum;"),
     ("subnormal quantum not clamped", "if (E < emin) E = emin;", ""),
     ("padding not zeroed", "for (int64_t c = D + P; c < out_stride; ++c) store_elem(out, out_dtype, row + c, 0.0);", ""),
+    ("dense layer reads its weights transposed",
+     "s += load_elem(x, x_dtype, (size_t)m * ldx + k) * load_elem(w, w_dtype, (size_t)n * K + k);",
+     "s += load_elem(x, x_dtype, (size_t)m * ldx + k) * load_elem(w, w_dtype, ((size_t)k * N + n) % ((size_t)N * K));"),
+    ("dense layer drops its bias", "if (bias) s += (double)bias[n];", ""),
+    ("ReLU not applied", "if (relu && !(s > 0.0)) s = 0.0;", ""),
+    ("input gradient without the ReLU mask",
+     "if (xmask && !(load_elem(xmask, x_dtype, (size_t)m * ldx + k) > 0.0)) s = 0.0;", ""),
+    ("weight gradient pairs dz with the wrong sample",
+     "s += load_elem(dz, dz_dtype, (size_t)m * ldz + n) * load_elem(x, x_dtype, (size_t)m * ldx + k);",
+     "s += load_elem(dz, dz_dtype, (size_t)m * ldz + n) * load_elem(x, x_dtype, (size_t)((m + 1) % M) * ldx + k);"),
+    ("bias gradient sums one column", "for (int m = 0; m < M; ++m) s += load_elem(dz, dz_dtype, (size_t)m * ldz + n);",
+     "for (int m = 0; m < M; ++m) s += load_elem(dz, dz_dtype, (size_t)m * ldz);"),
+    ("logistic gradient sign", "store_elem(dz, dz_dtype, (size_t)m, (p - y) / (double)M);",
+     "store_elem(dz, dz_dtype, (size_t)m, (y - p) / (double)M);"),
+    ("loss not averaged", "*loss = s / (double)M;", "*loss = s;"),
+    ("dense SGD sign", "master[i] = (float)((double)master[i] - (double)lr * (double)grad[i]);",
+     "master[i] = (float)((double)master[i] + (double)lr * (double)grad[i]);"),
 ]
 
 
@@ -67,6 +84,15 @@ def battery():
         lambda: pins.test_grad_update_equals_dense_sgd(5),
         pins.test_grad_update_invariants,
         pins.test_grad_update_single_repeated_row_is_column_sum,
+        lambda: pins.test_linear_fwd_matches_float64_matmul_on_exact_values(True),
+        pins.test_linear_fwd_respects_row_strides,
+        pins.test_linear_bwd_central_differences_exact,
+        pins.test_linear_bwd_mask_is_the_relu_derivative,
+        pins.test_linear_bwd_transposition_identity,
+        pins.test_bce_closed_forms,
+        pins.test_bce_gradient_central_differences,
+        pins.test_sgd_dense_special_cases,
+        pins.test_mlp_chain_gradient_central_differences,
     ]
 
 

@@ -587,3 +587,207 @@ def test_openmp_build_gives_the_plain_builds_bits():
         orc.restore_library(prev)
     for a, b in zip(plain, threaded):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------------------
+# dense layers, logistic loss, dense SGD (page "DLRM For PyTorch", §Model architecture:
+# bottom MLP = linear layers with ReLU; top MLP ending in one logit; --bottom_mlp_sizes,
+# --top_mlp_sizes)
+# ----------------------------------------------------------------------------------------
+
+def _exact_grid(rng, shape, lo=-8, hi=9, scale=0.125):
+    """Small multiples of 1/8: exact in bf16, and every product and short sum of them is
+    exact in binary32 and binary64."""
+    return rng.integers(lo, hi, size=shape).astype(np.float64) * scale
+
+
+@pytest.mark.parametrize("relu", [False, True])
+def test_linear_fwd_matches_float64_matmul_on_exact_values(relu):
+    """Library routine: float64 matmul.  On values whose sums are exact, the oracle's bf16
+    output must be torch's bf16 rounding of numpy's result, bit for bit; with random float64
+    inputs it must agree with numpy to float64 rounding."""
+    rng = np.random.default_rng(5)
+    M, K, N = 9, 12, 7
+    x, w = _exact_grid(rng, (M, K)), _exact_grid(rng, (N, K))
+    b = _exact_grid(rng, (N,)).astype(np.float32)
+    ref = x @ w.T + b
+    if relu:
+        ref = np.maximum(ref, 0.0)
+    xb, wb = f32_to_bf16_bits_torch(x), f32_to_bf16_bits_torch(w)
+    got = orc.linear_fwd(xb, "bf16", wb, "bf16", b, relu, "bf16")
+    assert np.array_equal(got, f32_to_bf16_bits_torch(ref))
+    xr, wr = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    ref = xr @ wr.T + b
+    if relu:
+        ref = np.maximum(ref, 0.0)
+    got = orc.linear_fwd(xr, "f64", wr, "f64", b, relu, "f64")
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_linear_fwd_respects_row_strides():
+    """Special case: a layer over the first K columns of a wider row equals the layer over
+    the sliced matrix; the output's extra columns are not written."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((5, 16))
+    w = rng.standard_normal((3, 13))
+    got = orc.linear_fwd(x, "f64", w, "f64", None, False, "f64", K=13, ldy=8)
+    ref = orc.linear_fwd(np.ascontiguousarray(x[:, :13]), "f64", w, "f64", None, False, "f64")
+    assert np.array_equal(got[:, :3], ref)
+    assert np.all(np.isnan(got[:, 3:]))
+
+
+def test_linear_bwd_central_differences_exact():
+    """L = sum(G * (x W^T + b)) is linear in each of x, W, b, so central differences give the
+    exact partial derivatives (up to float64 rounding): they must equal dx, dW, db of the
+    backward with dz = G."""
+    rng = np.random.default_rng(7)
+    M, K, N = 5, 4, 3
+    x, w = rng.standard_normal((M, K)), rng.standard_normal((N, K))
+    b = rng.standard_normal(N).astype(np.float32).astype(np.float64)
+    G = rng.standard_normal((M, N))
+
+    def L(x_, w_, b_):
+        y = orc.linear_fwd(x_, "f64", w_, "f64", None, False, "f64")
+        return float(np.sum(G * (y + b_)))
+
+    dx, dw, db = orc.linear_bwd(x, "f64", w, "f64", G, "f64", dx_dtype="f64", wgrad_dtype="f64")
+    h = 0.5
+    for (arr, grad) in ((x, dx), (w, dw)):
+        for idx in np.ndindex(arr.shape):
+            p, m = arr.copy(), arr.copy()
+            p[idx] += h
+            m[idx] -= h
+            args_p = (p, w, b) if arr is x else (x, p, b)
+            args_m = (m, w, b) if arr is x else (x, m, b)
+            fd = (L(*args_p) - L(*args_m)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-10 * max(1.0, abs(fd))
+    for n in range(N):
+        p, m = b.copy(), b.copy()
+        p[n] += h
+        m[n] -= h
+        assert abs((L(x, w, p) - L(x, w, m)) / (2 * h) - db[n]) < 1e-10
+
+
+def test_linear_bwd_mask_is_the_relu_derivative():
+    """With the ReLU mask, dx is the derivative of sum(G * (relu(x) W^T)) w.r.t. x: checked by
+    central differences at points away from the kink (x = 0 entries give 0)."""
+    rng = np.random.default_rng(8)
+    M, K, N = 4, 6, 5
+    x = rng.standard_normal((M, K))
+    x[np.abs(x) < 0.2] = 0.5
+    x[0, 0] = 0.0
+    w, G = rng.standard_normal((N, K)), rng.standard_normal((M, N))
+    dx, _, _ = orc.linear_bwd(x, "f64", w, "f64", G, "f64", dx_dtype="f64", relu_mask=True,
+                              wgrad_dtype="f64")
+
+    def L(x_):
+        return float(np.sum(G * (np.maximum(x_, 0.0) @ w.T)))
+
+    h = 0.05
+    for idx in np.ndindex(x.shape):
+        if x[idx] == 0.0:
+            assert dx[idx] == 0.0
+            continue
+        p, m = x.copy(), x.copy()
+        p[idx] += h
+        m[idx] -= h
+        assert abs((L(p) - L(m)) / (2 * h) - dx[idx]) < 1e-10
+
+
+def test_linear_bwd_transposition_identity():
+    """<dx, x> = <dW, W> = sum(dz * (x W^T)): both gradients contract the same bilinear form."""
+    rng = np.random.default_rng(9)
+    M, K, N = 7, 5, 6
+    x, w, dz = rng.standard_normal((M, K)), rng.standard_normal((N, K)), rng.standard_normal((M, N))
+    dx, dw, db = orc.linear_bwd(x, "f64", w, "f64", dz, "f64", dx_dtype="f64", wgrad_dtype="f64")
+    ref = float(np.sum(dz * (x @ w.T)))
+    assert abs(np.sum(dx * x) - ref) < 1e-10
+    assert abs(np.sum(dw * w) - ref) < 1e-10
+    assert np.max(np.abs(db - dz.sum(axis=0))) < 1e-12
+
+
+def test_bce_closed_forms():
+    """z = 0: loss log 2, dz = (1/2 - y)/M.  Label symmetry loss(z, y) = loss(-z, 1 - y).
+    Saturation: z = -1000, y = 1 costs 1000 and z = 1000, y = 1 costs 0, with no overflow."""
+    y = np.array([0, 1, 1, 0], np.float32)
+    loss, dz = orc.bce_logits(np.zeros(4), "f64", y, "f64")
+    assert abs(loss - np.log(2.0)) < 1e-15
+    assert np.array_equal(dz, (0.5 - y) / 4)
+    rng = np.random.default_rng(10)
+    z = rng.standard_normal(64) * 5
+    lab = (rng.random(64) < 0.3).astype(np.float32)
+    l1, _ = orc.bce_logits(z, "f64", lab, "f64")
+    l2, _ = orc.bce_logits(-z, "f64", 1 - lab, "f64")
+    assert abs(l1 - l2) < 1e-14
+    l3, d3 = orc.bce_logits(np.array([-1000.0, 1000.0]), "f64", np.array([1, 1], np.float32), "f64")
+    assert abs(l3 - 500.0) < 1e-12
+    assert np.array_equal(d3, np.array([-0.5, 0.0]))
+    # -log of the predicted probability of the true label, term by term
+    p = 1 / (1 + np.exp(-z))
+    ref = -np.mean(np.where(lab == 1, np.log(p), np.log1p(-p)))
+    assert abs(l1 - ref) < 1e-12
+
+
+def test_bce_gradient_central_differences():
+    rng = np.random.default_rng(12)
+    M = 16
+    z = rng.standard_normal(M) * 3
+    lab = (rng.random(M) < 0.5).astype(np.float32)
+    _, dz = orc.bce_logits(z, "f64", lab, "f64")
+    h = 1e-5
+    for m in range(M):
+        p, q = z.copy(), z.copy()
+        p[m] += h
+        q[m] -= h
+        fd = (orc.bce_logits(p, "f64", lab, "f64")[0] - orc.bce_logits(q, "f64", lab, "f64")[0]) / (2 * h)
+        assert abs(fd - dz[m]) < 1e-9
+
+
+def test_sgd_dense_special_cases():
+    """lr = 0 keeps the master bits; an exact step; the 16-bit copy is torch's rounding of the
+    new master."""
+    rng = np.random.default_rng(13)
+    m = rng.standard_normal(257).astype(np.float32)
+    g = rng.standard_normal(257).astype(np.float32)
+    new, copy = orc.sgd_dense(m, g, 0.0, "bf16")
+    assert np.array_equal(new.view(np.uint32), m.view(np.uint32))
+    assert np.array_equal(copy, f32_to_bf16_bits_torch(m))
+    new, _ = orc.sgd_dense(np.array([1.0, -3.0], np.float32), np.array([2.0, 4.0], np.float32), 0.25)
+    assert np.array_equal(new, np.array([0.5, -4.0], np.float32))
+    new, copy = orc.sgd_dense(m, g, 0.01, "bf16")
+    ref = (m.astype(np.float64) - np.float64(np.float32(0.01)) * g.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(new.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(copy, f32_to_bf16_bits_torch(ref))
+
+
+def test_mlp_chain_gradient_central_differences():
+    """A two-layer ReLU MLP, one logit and the logistic loss, all in float64: the backward
+    chain (loss gradient -> logit layer -> masked hidden layer) must match central differences
+    of the loss w.r.t. the first layer's weights and the dense input."""
+    rng = np.random.default_rng(14)
+    M, K, H = 6, 5, 4
+    x = rng.standard_normal((M, K))
+    w1, b1 = rng.standard_normal((H, K)), rng.standard_normal(H).astype(np.float32)
+    w2, b2 = rng.standard_normal((1, H)), rng.standard_normal(1).astype(np.float32)
+    lab = (rng.random(M) < 0.5).astype(np.float32)
+
+    def loss(x_, w1_):
+        h1 = orc.linear_fwd(x_, "f64", w1_, "f64", b1, True, "f64")
+        z = orc.linear_fwd(h1, "f64", w2, "f64", b2, False, "f64")
+        return orc.bce_logits(z, "f64", lab, "f64")[0]
+
+    h1 = orc.linear_fwd(x, "f64", w1, "f64", b1, True, "f64")
+    z = orc.linear_fwd(h1, "f64", w2, "f64", b2, False, "f64")
+    _, dz = orc.bce_logits(z, "f64", lab, "f64")
+    dh1, _, _ = orc.linear_bwd(h1, "f64", w2, "f64", dz.reshape(M, 1), "f64", dx_dtype="f64",
+                               relu_mask=True, wgrad_dtype="f64")
+    dx, dw1, _ = orc.linear_bwd(x, "f64", w1, "f64", dh1, "f64", dx_dtype="f64", wgrad_dtype="f64")
+    h = 1e-6
+    for arr, grad, which in ((w1, dw1, 1), (x, dx, 0)):
+        for idx in list(np.ndindex(arr.shape))[:12]:
+            p, q = arr.copy(), arr.copy()
+            p[idx] += h
+            q[idx] -= h
+            fd = (loss(p, w1) - loss(q, w1)) / (2 * h) if which == 0 else \
+                (loss(x, p) - loss(x, q)) / (2 * h)
+            assert abs(fd - grad[idx]) < 1e-7
