@@ -21,4 +21,10 @@ from .embcore import (  # noqa: F401
     emb_grad_reduce_update,
     emb_grad_sort,
     emb_grad_workspace_bytes,
+    bce_logits,
+    linear_bwd,
+    linear_bwd_workspace_bytes,
+    linear_fwd,
+    relu_bwd,
+    sgd_dense,
 )

@@ -256,7 +256,7 @@ el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t f
 
 const char* el_last_error(void) { return g_last_error.c_str(); }
 
-int el_version(void) { return 100; }
+int el_version(void) { return 200; }
 
 }  // extern "C"
 

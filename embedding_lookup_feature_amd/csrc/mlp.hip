@@ -1,0 +1,702 @@
+// mlp.hip -- the dense layers of the bottom and top MLPs on gfx950 MFMA, the logistic loss
+// on the final logit, and plain SGD on the dense parameters.
+//
+// Page "DLRM For PyTorch", §Model architecture: the dense features pass through the bottom
+// MLP (linear layers, each followed by a ReLU); the interaction output, concatenated with
+// the bottom-MLP output, passes through the top MLP, which ends in one number read as a
+// click likelihood.  §Command-line options gives the widths (--bottom_mlp_sizes 512,256,128,
+// --top_mlp_sizes 1024,1024,512,256,1) and the page trains the MLPs in mixed precision:
+// 16-bit operands with fp32 master weights.
+//
+// One tiled MFMA kernel serves the three products of a layer.  With weights w[n][k]:
+//   forward   y[m][n]  = sum_k x[m][k]  w[n][k]   rows operand x  (reduction contiguous),
+//                                                  cols operand w  (reduction contiguous)
+//   data grad dx[m][k] = sum_n dz[m][n] w[n][k]   rows operand dz (reduction contiguous),
+//                                                  cols operand w  (output contiguous)
+//   weight    dw[n][k] = sum_m dz[m][n] x[m][k]   rows operand dz (output contiguous),
+//                                                  cols operand x  (output contiguous)
+// Both operands are staged through LDS as [row][reduction] tiles (an 8 x 8 register
+// transpose for operands whose output index is the contiguous one), then read as
+// v_mfma_f32_32x32x16 fragments.  The MFMA "A" operand is the cols operand, so each lane's
+// accumulator registers hold 4 consecutive output columns of one output row: the epilogue
+// stores 8 (16-bit) or 16 (fp32) contiguous bytes per lane.
+#include <algorithm>
+#include <cstdio>
+#include <string>
+
+#include "el_internal.hpp"
+#include "el_mfma.hpp"
+
+namespace el {
+namespace {
+
+constexpr int kBR = 128;          // output rows per workgroup
+constexpr int kBC = 128;          // output cols per workgroup
+constexpr int kBK = 64;           // reduction per LDS stage
+constexpr int kPitch = kBK + 8;   // LDS row pitch in elements (144 B: 16-B reads conflict-free)
+constexpr int kTile = 128 * kPitch;  // elements of one operand tile
+constexpr int kThreads = 256;
+
+enum Epi { EPI_FWD = 0, EPI_DGRAD = 1, EPI_WGRAD = 2 };
+
+struct GemmArgs {
+  const uint16_t* P;  // rows operand
+  long ldp;
+  const uint16_t* Q;  // cols operand
+  long ldq;
+  int R, C;           // output rows, cols
+  int red;            // reduction length
+  int red_per_split;  // reduction per blockIdx.y (multiple of kBK)
+  int tiles_c, tiles;  // column tiles, tiles per split
+  void* out;          // fwd / dgrad: [R][ldo] 16-bit; wgrad: fp32 [split][R][ldo]
+  long ldo;
+  long split_stride;  // wgrad: elements between the partial planes of two splits
+  const float* bias;  // fwd: [C] or null
+  int relu;           // fwd: ReLU; dgrad: multiply by 1[mask > 0]
+  const uint16_t* mask;  // dgrad: [R][ldm]
+  long ldm;
+  float* dbp;         // wgrad: [split][R] row sums of the rows operand (bias gradient)
+};
+
+// 16 bytes from global memory or zeros.
+__device__ inline u32x4 ld16(const uint16_t* p, bool ok) {
+  return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+}
+
+// Global -> registers for one operand tile.
+//  RC (reduction contiguous): 128 rows x 64 reduction; all 256 threads, 4 vectors each
+//    (thread t: row t/8 + 32 i, reduction 8 (t%8) .. +8).
+//  OC (output contiguous): global [red][rows]; 128 threads, an 8 x 8 block each
+//    (thread s: reduction block s%8, row block s/8; 8 vectors of 8 rows at 8 reductions).
+template <bool RC>
+struct TileLoader {
+  static constexpr int N = RC ? 4 : 8;
+  u32x4 v[N];
+  __device__ inline void load(const uint16_t* base, long ld, int row0, int nrows, int k0, int kend,
+                              int sub) {
+    if constexpr (RC) {
+      const int kk = k0 + (sub & 7) * 8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + (sub >> 3) + 32 * i;
+        v[i] = ld16(base + static_cast<long>(r) * ld + kk, r < nrows && kk < kend);
+      }
+    } else {
+      const int kb = sub & 7, rb = sub >> 3;
+      const int r = row0 + rb * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = k0 + kb * 8 + i;
+        v[i] = ld16(base + static_cast<long>(k) * ld + r, r < nrows && k < kend);
+      }
+    }
+  }
+  __device__ inline void store(uint16_t* lds, int sub) const {
+    if constexpr (RC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + 32 * i) * kPitch + (sub & 7) * 8) = v[i];
+    } else {
+      const int kb = sub & 7, rb = sub >> 3;
+      // 8 x 8 transpose: out[j] holds row rb*8 + j at reductions kb*8 .. +8.
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int w = j >> 1;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t a = v[2 * q][w], b = v[2 * q + 1][w];
+          o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+        *reinterpret_cast<u32x4*>(lds + (rb * 8 + j) * kPitch + kb * 8) = o;
+      }
+    }
+  }
+};
+
+template <class T, bool P_RC, bool Q_RC, int EPI>
+__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nb = a.tiles;
+  const int bid = (nb & 7) == 0 ? xcd_remap(blockIdx.x, nb) : static_cast<int>(blockIdx.x);
+  const int tr = bid / a.tiles_c, tc = bid - tr * a.tiles_c;
+  const int row0 = tr * kBR, col0 = tc * kBC;
+  const int split = blockIdx.y;
+  const int kbeg = split * a.red_per_split;
+  const int kend = min(a.red, kbeg + a.red_per_split);
+  const int nk = (kend - kbeg + kBK - 1) / kBK;
+
+  // Which threads load which operand: an RC operand uses all threads; an OC operand uses
+  // threads 0..127 (rows operand) or 128..255 (cols operand).
+  const bool p_me = P_RC || tid < 128;
+  const bool q_me = Q_RC || tid >= 128;
+  const int p_sub = P_RC ? tid : tid;
+  const int q_sub = Q_RC ? tid : tid - 128;
+
+  TileLoader<P_RC> lp;
+  TileLoader<Q_RC> lq;
+  if (p_me) lp.load(a.P, a.ldp, row0, a.R, kbeg, kend, p_sub);
+  if (q_me) lq.load(a.Q, a.ldq, col0, a.C, kbeg, kend, q_sub);
+  if (p_me) lp.store(sP[0], p_sub);
+  if (q_me) lq.store(sQ[0], q_sub);
+  __syncthreads();
+
+  const int wr = wave >> 1, wc = wave & 1;  // 64 x 64 output block of this wavefront
+  const int half = lane >> 5, l32 = lane & 31;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  // bias gradient (weight-gradient launch): the first column tile sums its rows operand
+  const bool do_db = (EPI == EPI_WGRAD) && tc == 0 && tid < 128;
+  float dbsum = 0.f;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = kbeg + (kt + 1) * kBK;
+      if (p_me) lp.load(a.P, a.ldp, row0, a.R, k0, kend, p_sub);
+      if (q_me) lq.load(a.Q, a.ldq, col0, a.C, k0, kend, q_sub);
+    }
+    const uint16_t* P = sP[cur];
+    const uint16_t* Q = sQ[cur];
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int ko = ks * 16 + half * 8;
+      u32x4 qa[2], pb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        qa[i] = *reinterpret_cast<const u32x4*>(Q + (wc * 64 + i * 32 + l32) * kPitch + ko);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        pb[j] = *reinterpret_cast<const u32x4*>(P + (wr * 64 + j * 32 + l32) * kPitch + ko);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(qa[i], pb[j], acc[i][j]);
+    }
+    if (do_db) {
+      const uint16_t* row = P + tid * kPitch;
+#pragma unroll
+      for (int v = 0; v < kBK / 8; ++v) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(row + v * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dbsum += T::to_f(static_cast<uint16_t>(x[q] & 0xffffu)) + T::to_f(static_cast<uint16_t>(x[q] >> 16));
+      }
+    }
+    if (more) {
+      if (p_me) lp.store(sP[cur ^ 1], p_sub);
+      if (q_me) lq.store(sQ[cur ^ 1], q_sub);
+    }
+    __syncthreads();
+  }
+
+  if (EPI == EPI_WGRAD && do_db && row0 + tid < a.R) a.dbp[static_cast<long>(split) * a.R + row0 + tid] = dbsum;
+
+  // Epilogue: register rr of acc[i][j] is output column col0 + wc*64 + i*32 + 8(rr/4) +
+  // 4 half + rr%4 of output row row0 + wr*64 + j*32 + l32.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = row0 + wr * 64 + j * 32 + l32;
+    if (r >= a.R) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = col0 + wc * 64 + i * 32 + g * 8 + half * 4;
+        if (c >= a.C) continue;
+        float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+        if constexpr (EPI == EPI_WGRAD) {
+          float* o = static_cast<float*>(a.out) + static_cast<long>(split) * a.split_stride +
+                     static_cast<long>(r) * a.ldo + c;
+          *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+          if constexpr (EPI == EPI_FWD) {
+            if (a.bias) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] += a.bias[c + q];
+            }
+            if (a.relu) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = v[q] > 0.f ? v[q] : 0.f;
+            }
+          } else {
+            if (a.relu) {
+              const uint2 m = *reinterpret_cast<const uint2*>(a.mask + static_cast<long>(r) * a.ldm + c);
+              const uint32_t mw[2] = {m.x, m.y};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float x = T::to_f(static_cast<uint16_t>((mw[q >> 1] >> (16 * (q & 1))) & 0xffffu));
+                if (!(x > 0.f)) v[q] = 0.f;
+              }
+            }
+          }
+          store_n<T, 4>(static_cast<uint16_t*>(a.out) + static_cast<long>(r) * a.ldo + c, v);
+        }
+      }
+    }
+  }
+}
+
+// Ordered sum of the split partials: out[i] = sum_s part[s][i] (i < n), and the bias
+// gradient db[i] = sum_s dbp[s][i] (i < nb).
+__global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, int splits, float* out,
+                                                   const float* dbp, int nb, float* db) {
+  const long i4 = (static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i4 < n) {
+    float4 s = *reinterpret_cast<const float4*>(part + i4);
+    for (int p = 1; p < splits; ++p) {
+      const float4 v = *reinterpret_cast<const float4*>(part + p * n + i4);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + i4) = s;
+  }
+  const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g < nb) {
+    float s = dbp[g];
+    for (int p = 1; p < splits; ++p) s += dbp[static_cast<long>(p) * nb + g];
+    db[g] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// One-output layers (the logit): y[m] = act(sum_k x[m][k] w[k] + b).  A group of L lanes
+// (L = power of two, 8 elements per lane and step) per row; rows per wavefront 64 / L.
+// ---------------------------------------------------------------------------------------
+template <class T, int L>
+__global__ __launch_bounds__(256) void k_gemv_fwd(const uint16_t* x, long ldx, int M, int K,
+                                                 const uint16_t* w, const float* bias, int relu,
+                                                 uint16_t* y, long ldy) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % L;
+  const long rows_per_block = (blockDim.x / 64) * (64 / L);
+  const long m = blockIdx.x * rows_per_block + (threadIdx.x / 64) * (64 / L) + lane / L;
+  float s = 0.f;
+  if (m < M) {
+    for (int k = sub * 8; k < K; k += L * 8) {
+      float xf[8], wf[8];
+      unpack16<T>(*reinterpret_cast<const uint4*>(x + m * ldx + k), xf);
+      unpack16<T>(*reinterpret_cast<const uint4*>(w + k), wf);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += xf[q] * wf[q];
+    }
+  }
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (m < M && sub == 0) {
+    if (bias) s += bias[0];
+    if (relu && !(s > 0.f)) s = 0.f;
+    y[m * ldy] = T::from_f(s);
+  }
+}
+
+// dx[m][k] = dz[m] * w[k] (times 1[x[m][k] > 0] with the mask), 8 elements per thread.
+template <class T>
+__global__ __launch_bounds__(256) void k_gemv_dgrad(const uint16_t* dz, long ldz, int M, int K,
+                                                   const uint16_t* w, const uint16_t* mask, long ldm,
+                                                   uint16_t* dx, long lddx) {
+  const int kv = K / 8;
+  const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= static_cast<long>(M) * kv) return;
+  const long m = g / kv;
+  const int k = static_cast<int>(g - m * kv) * 8;
+  const float d = T::to_f(dz[m * ldz]);
+  float wf[8], v[8];
+  unpack16<T>(*reinterpret_cast<const uint4*>(w + k), wf);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = d * wf[q];
+  if (mask) {
+    float xf[8];
+    unpack16<T>(*reinterpret_cast<const uint4*>(mask + m * ldm + k), xf);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (!(xf[q] > 0.f)) v[q] = 0.f;
+  }
+  store_n<T, 8>(dx + m * lddx + k, v);
+}
+
+// Weight / bias gradient of a one-output layer over the rows of one split:
+//   part[split][k] = sum_m dz[m] x[m][k],  dbp[split] = sum_m dz[m]
+// Threads: K/8 lanes per row group, G = 256 / (K/8) row groups striding over the rows; the
+// groups are combined in LDS in fixed order.
+template <class T>
+__global__ __launch_bounds__(256) void k_gemv_wgrad(const uint16_t* x, long ldx, int M, int K,
+                                                   const uint16_t* dz, long ldz, int rows_per_split,
+                                                   float* part, float* dbp) {
+  __shared__ float red[256 * 8 + 256];
+  const int kv = K / 8;
+  const int G = 256 / kv;
+  const int t = threadIdx.x, grp = t / kv, kk = (t % kv) * 8;
+  const int m0 = blockIdx.x * rows_per_split;
+  const int m1 = min(M, m0 + rows_per_split);
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float sd = 0.f;
+  if (grp < G) {
+    for (int m = m0 + grp; m < m1; m += G) {
+      const float d = T::to_f(dz[static_cast<long>(m) * ldz]);
+      float xf[8];
+      unpack16<T>(*reinterpret_cast<const uint4*>(x + static_cast<long>(m) * ldx + kk), xf);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] += d * xf[q];
+      sd += d;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[t * 8 + q] = s[q];
+  red[256 * 8 + t] = sd;
+  __syncthreads();
+  if (t < kv) {
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int g2 = 0; g2 < G; ++g2)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o[q] += red[(g2 * kv + t) * 8 + q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) part[static_cast<long>(blockIdx.x) * K + kk + q] = o[q];
+  }
+  if (t == 0) {
+    float o = 0.f;
+    for (int g2 = 0; g2 < G; ++g2) o += red[256 * 8 + g2 * kv];
+    dbp[blockIdx.x] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Logistic loss on logits z [M] with labels in {0,1}: dz[m] = (sigmoid(z_m) - y_m) / M and
+// loss = (1/M) sum_m [max(z,0) - z y + log(1 + exp(-|z|))].  One workgroup; each thread
+// sums a strided subset, then a fixed-order tree in LDS (bitwise reproducible).
+// ---------------------------------------------------------------------------------------
+template <class T>
+__global__ __launch_bounds__(1024) void k_bce(const uint16_t* z, long ldz, const float* labels, int M,
+                                             float* loss, uint16_t* dz, long lddz) {
+  __shared__ double red[1024];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  const float inv = 1.0f / static_cast<float>(M);
+  for (int m = t; m < M; m += 1024) {
+    const float v = T::to_f(z[static_cast<long>(m) * ldz]);
+    const float y = labels[m];
+    s += static_cast<double>(fmaxf(v, 0.f) - v * y + log1pf(expf(-fabsf(v))));
+    const float p = 1.f / (1.f + expf(-v));
+    dz[static_cast<long>(m) * lddz] = T::from_f((p - y) * inv);
+  }
+  red[t] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) loss[0] = static_cast<float>(red[0] / M);
+}
+
+// dz = dy * 1[y > 0], 8 elements per thread ([M] rows of stride ld, N % 8 == 0).
+template <class T>
+__global__ __launch_bounds__(256) void k_relu_bwd(const uint16_t* dy, const uint16_t* y, uint16_t* dz,
+                                                 int M, int N, long ld) {
+  const int nv = N / 8;
+  const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= static_cast<long>(M) * nv) return;
+  const long m = g / nv;
+  const long off = m * ld + (g - m * nv) * 8;
+  const uint4 d = *reinterpret_cast<const uint4*>(dy + off);
+  const uint4 v = *reinterpret_cast<const uint4*>(y + off);
+  const uint32_t dw[4] = {d.x, d.y, d.z, d.w}, vw[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const bool lo = T::to_f(static_cast<uint16_t>(vw[q] & 0xffffu)) > 0.f;
+    const bool hi = T::to_f(static_cast<uint16_t>(vw[q] >> 16)) > 0.f;
+    o[q] = (lo ? (dw[q] & 0xffffu) : 0u) | (hi ? (dw[q] & 0xffff0000u) : 0u);
+  }
+  *reinterpret_cast<uint4*>(dz + off) = uint4{o[0], o[1], o[2], o[3]};
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* p, long n) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+// master[i] -= lr * grad[i] (one fp32 rounding); copy[i] = master[i] in the copy's dtype.
+template <class T>
+__global__ __launch_bounds__(256) void k_sgd_dense(float* master, uint16_t* copy, const float* grad,
+                                                  long n, float lr) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = fmaf(-lr, grad[i], master[i]);
+  master[i] = v;
+  if (copy) copy[i] = T::from_f(v);
+}
+
+__global__ __launch_bounds__(256) void k_sgd_dense_f32(float* master, const float* grad, long n, float lr) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  master[i] = fmaf(-lr, grad[i], master[i]);
+}
+
+// ---------------------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------------------
+el_status bad(const char* fn, const std::string& what) {
+  return set_error(EL_ERR_INVALID_ARG, std::string(fn) + ": " + what);
+}
+bool al(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+struct WgradPlan {
+  int splits = 1;
+  int per = 0;     // reduction rows per split
+  size_t bytes = 0;
+};
+
+// Splits of the weight-gradient reduction over the batch: enough workgroups to cover the
+// chip about twice (output tiles x splits >= 512), each split at least 4 LDS stages long.
+WgradPlan plan_wgrad(int M, int K, int N) {
+  WgradPlan p;
+  if (M <= 0) return p;
+  if (N == 1) {
+    const int per = std::max(256, (M + 1023) / 1024);
+    p.splits = (M + per - 1) / per;
+    p.per = per;
+    p.bytes = static_cast<size_t>(p.splits) * (K + 1) * sizeof(float);
+    return p;
+  }
+  const int tiles = ((N + kBR - 1) / kBR) * ((K + kBC - 1) / kBC);
+  int s = std::max(1, (512 + tiles - 1) / tiles);
+  const int max_s = std::max(1, M / (4 * kBK));
+  s = std::min(std::min(s, max_s), 64);
+  int per = (M + s - 1) / s;
+  per = (per + kBK - 1) / kBK * kBK;
+  p.splits = (M + per - 1) / per;
+  p.per = per;
+  p.bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * (static_cast<size_t>(N) * K + N) * sizeof(float) : 0;
+  return p;
+}
+
+template <class T>
+el_status run_linear_fwd(const uint16_t* x, long ldx, int M, int K, const uint16_t* w, const float* bias,
+                         int N, int relu, uint16_t* y, long ldy, hipStream_t st) {
+  if (M == 0) return EL_OK;
+  if (N == 1) {
+    int L = 1;
+    while (L < 64 && L * 8 < K) L *= 2;
+    const int rows_per_block = 4 * (64 / L);
+    const dim3 grid((M + rows_per_block - 1) / rows_per_block);
+    switch (L) {
+#define EL_GEMV_CASE(LL) \
+  case LL: hipLaunchKernelGGL((k_gemv_fwd<T, LL>), grid, dim3(256), 0, st, x, ldx, M, K, w, bias, relu, y, ldy); break;
+      EL_GEMV_CASE(1) EL_GEMV_CASE(2) EL_GEMV_CASE(4) EL_GEMV_CASE(8) EL_GEMV_CASE(16) EL_GEMV_CASE(32)
+      EL_GEMV_CASE(64)
+#undef EL_GEMV_CASE
+    }
+    return check_launch("el_linear_fwd");
+  }
+  GemmArgs a{};
+  a.P = x; a.ldp = ldx; a.Q = w; a.ldq = K;
+  a.R = M; a.C = N; a.red = K; a.red_per_split = (K + kBK - 1) / kBK * kBK;
+  a.tiles_c = (N + kBC - 1) / kBC;
+  a.tiles = ((M + kBR - 1) / kBR) * a.tiles_c;
+  a.out = y; a.ldo = ldy; a.bias = bias; a.relu = relu;
+  hipLaunchKernelGGL((k_gemm<T, true, true, EPI_FWD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
+  return check_launch("el_linear_fwd");
+}
+
+template <class T>
+el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16_t* w, int N,
+                         const uint16_t* dz, long ldz, uint16_t* dx, long lddx, int mask,
+                         float* dw, float* db, void* ws, hipStream_t st) {
+  const WgradPlan pl = plan_wgrad(M, K, N);
+  if (M == 0) {  // empty batch: zero gradients (a fill kernel, so the call stays capturable)
+    const long n = static_cast<long>(N) * K;
+    hipLaunchKernelGGL(k_fill_zero, dim3((n + 255) / 256), dim3(256), 0, st, dw, n);
+    hipLaunchKernelGGL(k_fill_zero, dim3((N + 255) / 256), dim3(256), 0, st, db, static_cast<long>(N));
+    return check_launch("el_linear_bwd");
+  }
+  if (N == 1) {
+    if (dx) {
+      const long nthr = static_cast<long>(M) * (K / 8);
+      hipLaunchKernelGGL((k_gemv_dgrad<T>), dim3((nthr + 255) / 256), dim3(256), 0, st, dz, ldz, M, K, w,
+                         mask ? x : nullptr, ldx, dx, lddx);
+    }
+    float* part = static_cast<float*>(ws);
+    float* dbp = part + static_cast<size_t>(pl.splits) * K;
+    hipLaunchKernelGGL((k_gemv_wgrad<T>), dim3(pl.splits), dim3(256), 0, st, x, ldx, M, K, dz, ldz, pl.per,
+                       part, dbp);
+    const long n4 = (K + 3) / 4;
+    const long nthr = std::max<long>(n4, 1);
+    hipLaunchKernelGGL(k_split_sum, dim3((nthr + 255) / 256), dim3(256), 0, st, part, static_cast<long>(K),
+                       pl.splits, dw, dbp, 1, db);
+    return check_launch("el_linear_bwd");
+  }
+  if (dx) {
+    GemmArgs a{};
+    a.P = dz; a.ldp = ldz; a.Q = w; a.ldq = K;
+    a.R = M; a.C = K; a.red = N; a.red_per_split = (N + kBK - 1) / kBK * kBK;
+    a.tiles_c = (K + kBC - 1) / kBC;
+    a.tiles = ((M + kBR - 1) / kBR) * a.tiles_c;
+    a.out = dx; a.ldo = lddx; a.relu = mask; a.mask = x; a.ldm = ldx;
+    hipLaunchKernelGGL((k_gemm<T, true, false, EPI_DGRAD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
+  }
+  GemmArgs b{};
+  b.P = dz; b.ldp = ldz; b.Q = x; b.ldq = ldx;
+  b.R = N; b.C = K; b.red = M; b.red_per_split = pl.per;
+  b.tiles_c = (K + kBC - 1) / kBC;
+  b.tiles = ((N + kBR - 1) / kBR) * b.tiles_c;
+  if (pl.splits == 1) {
+    b.out = dw; b.ldo = K; b.split_stride = 0; b.dbp = db;
+    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles, 1), dim3(kThreads), 0, st, b);
+  } else {
+    float* part = static_cast<float*>(ws);
+    float* dbp = part + static_cast<size_t>(pl.splits) * N * K;
+    b.out = part; b.ldo = K; b.split_stride = static_cast<long>(N) * K; b.dbp = dbp;
+    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles, pl.splits), dim3(kThreads), 0, st, b);
+    const long n = static_cast<long>(N) * K;
+    const long nthr = std::max<long>((n + 3) / 4, N);
+    hipLaunchKernelGGL(k_split_sum, dim3((nthr + 255) / 256), dim3(256), 0, st, part, n, pl.splits, dw, dbp,
+                       N, db);
+  }
+  return check_launch("el_linear_bwd");
+}
+
+el_status check_linear(const char* fn, const void* x, int32_t ldx, int32_t M, int32_t K, const void* w,
+                       int32_t N, el_dtype dtype) {
+  if (dtype != EL_BF16 && dtype != EL_F16)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be EL_BF16 or EL_F16");
+  if (M < 0) return bad(fn, "M must be >= 0");
+  if (K < 8 || K % 8 != 0) return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": K must be a positive multiple of 8");
+  if (N < 1) return bad(fn, "N must be >= 1");
+  if (N != 1 && N % 8 != 0) return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": N must be 1 or a multiple of 8");
+  if (N == 1 && K > 2048) return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": one-output layers take K <= 2048");
+  if (ldx < K || ldx % 8 != 0) return bad(fn, "ldx must be >= K and a multiple of 8");
+  if (!w || !al(w, 16)) return bad(fn, "w must be non-null and 16-byte aligned");
+  if (M > 0 && (!x || !al(x, 16))) return bad(fn, "x must be non-null and 16-byte aligned");
+  return EL_OK;
+}
+
+}  // namespace
+}  // namespace el
+
+using namespace el;
+
+extern "C" {
+
+EL_API el_status el_linear_fwd(const void* x, int32_t ldx, int32_t M, int32_t K, const void* w,
+                               const float* bias, int32_t N, uint32_t act, void* y, int32_t ldy,
+                               el_dtype dtype, hipStream_t stream) {
+  const char* fn = "el_linear_fwd";
+  const el_status s = check_linear(fn, x, ldx, M, K, w, N, dtype);
+  if (s != EL_OK) return s;
+  if (act != EL_ACT_NONE && act != EL_ACT_RELU) return bad(fn, "unknown activation");
+  if (bias && !al(bias, 16)) return bad(fn, "bias must be 16-byte aligned");
+  if (ldy < N || (N != 1 && ldy % 8 != 0)) return bad(fn, "ldy must be >= N (and a multiple of 8 when N > 1)");
+  if (M > 0 && (!y || !al(y, N == 1 ? 2 : 16))) return bad(fn, "y must be non-null and aligned");
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* ws = static_cast<const uint16_t*>(w);
+  uint16_t* ys = static_cast<uint16_t*>(y);
+  const int relu = act == EL_ACT_RELU;
+  return dtype == EL_BF16 ? run_linear_fwd<BF16T>(xs, ldx, M, K, ws, bias, N, relu, ys, ldy, stream)
+                          : run_linear_fwd<F16T>(xs, ldx, M, K, ws, bias, N, relu, ys, ldy, stream);
+}
+
+EL_API size_t el_linear_bwd_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+  if (M < 0 || K < 1 || N < 1) return 0;
+  return plan_wgrad(M, K, N).bytes;
+}
+
+EL_API el_status el_linear_bwd(const void* x, int32_t ldx, int32_t M, int32_t K, const void* w,
+                               int32_t N, const void* dz, int32_t ldz, void* dx, int32_t lddx,
+                               uint32_t flags, float* dw, float* db, el_dtype dtype,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "el_linear_bwd";
+  const el_status s = check_linear(fn, x, ldx, M, K, w, N, dtype);
+  if (s != EL_OK) return s;
+  if (flags & ~static_cast<uint32_t>(EL_LINEAR_DX_RELU_MASK)) return bad(fn, "unknown flags");
+  if (ldz < N || (N != 1 && ldz % 8 != 0)) return bad(fn, "ldz must be >= N (and a multiple of 8 when N > 1)");
+  if (M > 0 && (!dz || !al(dz, N == 1 ? 2 : 16))) return bad(fn, "dz must be non-null and aligned");
+  if (dx && (lddx < K || lddx % 8 != 0 || !al(dx, 16))) return bad(fn, "dx: lddx must be >= K, a multiple of 8, dx 16-byte aligned");
+  if (!dx && (flags & EL_LINEAR_DX_RELU_MASK)) return bad(fn, "the ReLU mask flag needs dx");
+  if (!dw || !db || !al(dw, 16) || !al(db, 4)) return bad(fn, "dw (16-byte aligned) and db must be non-null");
+  const size_t need = plan_wgrad(M, K, N).bytes;
+  if (need > 0 && (!workspace || !al(workspace, 256)))
+    return set_error(EL_ERR_WORKSPACE, std::string(fn) + ": workspace must be non-null and 256-byte aligned");
+  if (workspace_bytes < need) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+    return set_error(EL_ERR_WORKSPACE, buf);
+  }
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* ws = static_cast<const uint16_t*>(w);
+  const uint16_t* dzs = static_cast<const uint16_t*>(dz);
+  uint16_t* dxs = static_cast<uint16_t*>(dx);
+  const int mask = (flags & EL_LINEAR_DX_RELU_MASK) ? 1 : 0;
+  return dtype == EL_BF16
+             ? run_linear_bwd<BF16T>(xs, ldx, M, K, ws, N, dzs, ldz, dxs, lddx, mask, dw, db, workspace, stream)
+             : run_linear_bwd<F16T>(xs, ldx, M, K, ws, N, dzs, ldz, dxs, lddx, mask, dw, db, workspace, stream);
+}
+
+EL_API el_status el_relu_bwd(const void* dy, const void* y, void* dz, int32_t M, int32_t N,
+                             int32_t ld, el_dtype dtype, hipStream_t stream) {
+  const char* fn = "el_relu_bwd";
+  if (dtype != EL_BF16 && dtype != EL_F16)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be EL_BF16 or EL_F16");
+  if (M < 0 || N < 1) return bad(fn, "M must be >= 0 and N >= 1");
+  if (N % 8 != 0 || ld < N || ld % 8 != 0)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": N and ld must be multiples of 8, ld >= N");
+  if (M == 0) return EL_OK;
+  if (!dy || !y || !dz || !al(dy, 16) || !al(y, 16) || !al(dz, 16)) return bad(fn, "null or misaligned pointer");
+  const long n = static_cast<long>(M) * (N / 8);
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  const uint16_t* a = static_cast<const uint16_t*>(dy);
+  const uint16_t* b = static_cast<const uint16_t*>(y);
+  uint16_t* c = static_cast<uint16_t*>(dz);
+  if (dtype == EL_BF16)
+    hipLaunchKernelGGL((k_relu_bwd<BF16T>), grid, dim3(256), 0, stream, a, b, c, M, N, static_cast<long>(ld));
+  else
+    hipLaunchKernelGGL((k_relu_bwd<F16T>), grid, dim3(256), 0, stream, a, b, c, M, N, static_cast<long>(ld));
+  return check_launch(fn);
+}
+
+EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, int32_t M,
+                               el_dtype dtype, float* loss, void* dz, int32_t lddz,
+                               hipStream_t stream) {
+  const char* fn = "el_bce_logits";
+  if (dtype != EL_BF16 && dtype != EL_F16)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be EL_BF16 or EL_F16");
+  if (M < 1) return bad(fn, "M must be >= 1");
+  if (ldz < 1 || lddz < 1) return bad(fn, "ldz and lddz must be >= 1");
+  if (!z || !labels || !loss || !dz || !al(z, 2) || !al(dz, 2) || !al(labels, 4) || !al(loss, 4))
+    return bad(fn, "null or misaligned pointer");
+  const uint16_t* zs = static_cast<const uint16_t*>(z);
+  uint16_t* dzs = static_cast<uint16_t*>(dz);
+  if (dtype == EL_BF16)
+    hipLaunchKernelGGL((k_bce<BF16T>), dim3(1), dim3(1024), 0, stream, zs, ldz, labels, M, loss, dzs, lddz);
+  else
+    hipLaunchKernelGGL((k_bce<F16T>), dim3(1), dim3(1024), 0, stream, zs, ldz, labels, M, loss, dzs, lddz);
+  return check_launch(fn);
+}
+
+EL_API el_status el_sgd_dense(float* master, void* copy, el_dtype copy_dtype, const float* grad,
+                              int64_t n, float lr, hipStream_t stream) {
+  const char* fn = "el_sgd_dense";
+  if (n < 0) return bad(fn, "n must be >= 0");
+  if (n == 0) return EL_OK;
+  if (!master || !grad || !al(master, 4) || !al(grad, 4)) return bad(fn, "master and grad must be non-null");
+  if (copy && copy_dtype != EL_BF16 && copy_dtype != EL_F16)
+    return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": copy dtype must be EL_BF16 or EL_F16");
+  if (copy && !al(copy, 2)) return bad(fn, "copy must be 2-byte aligned");
+  const dim3 grid(static_cast<unsigned>((n + 255) / 256));
+  uint16_t* cs = static_cast<uint16_t*>(copy);
+  if (!copy)
+    hipLaunchKernelGGL(k_sgd_dense_f32, grid, dim3(256), 0, stream, master, grad, static_cast<long>(n), lr);
+  else if (copy_dtype == EL_BF16)
+    hipLaunchKernelGGL((k_sgd_dense<BF16T>), grid, dim3(256), 0, stream, master, cs, grad, static_cast<long>(n), lr);
+  else
+    hipLaunchKernelGGL((k_sgd_dense<F16T>), grid, dim3(256), 0, stream, master, cs, grad, static_cast<long>(n), lr);
+  return check_launch(fn);
+}
+
+}  // extern "C"

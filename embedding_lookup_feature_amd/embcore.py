@@ -18,6 +18,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "embcore.h")
 EL_OK, EL_ERR_INVALID_ARG, EL_ERR_UNSUPPORTED, EL_ERR_WORKSPACE, EL_ERR_HIP = range(5)
 EL_F32, EL_F16, EL_BF16 = 0, 1, 2
 EL_FLAG_HASH_INDICES = 1
+EL_ACT_NONE, EL_ACT_RELU = 0, 1
+EL_LINEAR_DX_RELU_MASK = 1
 
 _DTYPE = {torch.float32: EL_F32, torch.float16: EL_F16, torch.bfloat16: EL_BF16}
 
@@ -63,11 +65,21 @@ def lib() -> ctypes.CDLL:
         L.emb_grad_apply.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.emb_grad_sort.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp]
         L.el_validate_bags.argtypes = [T, Bg, u32, vp, vp]
+        sz = ctypes.c_size_t
+        L.el_linear_fwd.argtypes = [vp, i32, i32, i32, vp, vp, i32, u32, vp, i32, ctypes.c_int, vp]
+        L.el_linear_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+        L.el_linear_bwd_workspace_bytes.restype = sz
+        L.el_linear_bwd.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, i32, u32, vp, vp,
+                                    ctypes.c_int, vp, sz, vp]
+        L.el_relu_bwd.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
+        L.el_bce_logits.argtypes = [vp, i32, vp, i32, ctypes.c_int, vp, vp, i32, vp]
+        L.el_sgd_dense.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, f32, vp]
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
         for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
                      "emb_grad_reduce_update", "emb_grad_prepare", "emb_grad_apply",
-                     "emb_grad_sort", "el_validate_bags"):
+                     "emb_grad_sort", "el_validate_bags", "el_linear_fwd", "el_linear_bwd",
+                     "el_relu_bwd", "el_bce_logits", "el_sgd_dense"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -243,3 +255,92 @@ def el_validate_bags(tables: Tables, bags: Bags, bad_count: torch.Tensor, hash_i
     _check(lib().el_validate_bags(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
                                   _dev(bad_count, "bad_count"), _stream(stream)))
     return bad_count
+
+
+# ----------------------------------------------------------------------------------------
+# dense layers, logistic loss, dense SGD
+# ----------------------------------------------------------------------------------------
+
+def _rows(t: torch.Tensor, name: str):
+    """(pointer, rows, row stride) of a 2-D tensor whose rows may be strided (last dim dense)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.data_ptr(), t.shape[0], t.stride(0)
+
+
+def linear_fwd(x: torch.Tensor, w: torch.Tensor, bias, y: torch.Tensor, relu: bool, stream=None):
+    """y[:, :N] = act(x[:, :K] @ w.T + bias) with w [N, K]; x, y may be row-strided views."""
+    xp, M, ldx = _rows(x, "x")
+    N, K = w.shape
+    yp, My, ldy = _rows(y, "y")
+    if My != M or y.dtype != x.dtype or w.dtype != x.dtype:
+        raise ValueError("x, w, y must share the dtype; y must have M rows")
+    bp = _dev(bias, "bias") if bias is not None else None
+    _check(lib().el_linear_fwd(xp, ldx, M, K, _dev(w, "w"), bp, N,
+                               EL_ACT_RELU if relu else EL_ACT_NONE, yp, ldy, _dtype(x, "x"),
+                               _stream(stream)))
+    return y
+
+
+def linear_bwd_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(lib().el_linear_bwd_workspace_bytes(M, K, N))
+
+
+def linear_bwd(x: torch.Tensor, w: torch.Tensor, dz: torch.Tensor, dw: torch.Tensor,
+               db: torch.Tensor, dx: torch.Tensor = None, relu_mask: bool = False,
+               workspace: torch.Tensor = None, stream=None):
+    """dw = dz^T x, db = dz.sum(0) (fp32) and, when dx is given, dx = dz @ w (times
+    1[x > 0] with relu_mask).  workspace: bytes >= linear_bwd_workspace_bytes(M, K, N)."""
+    xp, M, ldx = _rows(x, "x")
+    N, K = w.shape
+    zp, Mz, ldz = _rows(dz, "dz")
+    if Mz != M:
+        raise ValueError("dz must have M rows")
+    dxp, lddx = (None, K)
+    if dx is not None:
+        dxp, Mx, lddx = _rows(dx, "dx")
+        if Mx != M:
+            raise ValueError("dx must have M rows")
+    need = linear_bwd_workspace_bytes(M, K, N)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wp = _dev(workspace, "workspace") if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
+    _check(lib().el_linear_bwd(xp, ldx, M, K, _dev(w, "w"), N, zp, ldz, dxp, lddx,
+                               EL_LINEAR_DX_RELU_MASK if relu_mask else 0, _dev(dw, "dw"),
+                               _dev(db, "db"), _dtype(x, "x"), wp, wn, _stream(stream)))
+    return dx, dw, db
+
+
+def relu_bwd(dy: torch.Tensor, y: torch.Tensor, dz: torch.Tensor, stream=None):
+    """dz = dy * 1[y > 0] (the ReLU derivative from its output)."""
+    M, N = dy.shape
+    if y.shape != dy.shape or dz.shape != dy.shape:
+        raise ValueError("dy, y, dz must have one shape")
+    _check(lib().el_relu_bwd(_dev(dy, "dy"), _dev(y, "y"), _dev(dz, "dz"), M, N, N,
+                             _dtype(dy, "dy"), _stream(stream)))
+    return dz
+
+
+def bce_logits(z: torch.Tensor, labels: torch.Tensor, loss: torch.Tensor, dz: torch.Tensor,
+               stream=None):
+    """loss[0] = batch-mean logistic loss of logits z ([M] or [M, 1] view), dz = dloss/dz."""
+    M = labels.numel()
+    ldz = z.stride(0) if z.dim() >= 1 else 1
+    lddz = dz.stride(0) if dz.dim() >= 1 else 1
+    if not (z.is_cuda and dz.is_cuda):
+        raise ValueError("z and dz must be device tensors")
+    _check(lib().el_bce_logits(z.data_ptr(), ldz, _dev(labels, "labels"), M, _dtype(z, "z"),
+                               _dev(loss, "loss"), dz.data_ptr(), lddz, _stream(stream)))
+    return loss, dz
+
+
+def sgd_dense(master: torch.Tensor, grad: torch.Tensor, lr: float, copy: torch.Tensor = None,
+              stream=None):
+    """master -= lr * grad (fp32); copy = master in the copy's 16-bit dtype."""
+    cp = _dev(copy, "copy") if copy is not None else None
+    cd = _dtype(copy, "copy") if copy is not None else EL_BF16
+    _check(lib().el_sgd_dense(_dev(master, "master"), cp, cd, _dev(grad, "grad"), master.numel(),
+                              float(lr), _stream(stream)))

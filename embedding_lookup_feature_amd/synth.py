@@ -228,6 +228,50 @@ def make_dout(wl: Workload, device, batch_id: int = 0) -> torch.Tensor:
     return G.to(_TORCH[wl.act_dtype]).contiguous()
 
 
+TOP_MLP = (1024, 1024, 512, 256, 1)  # --top_mlp_sizes default
+LABEL_RATE = 0.25  # clicks per sample of the synthetic labels (the page gives no rate)
+
+
+def make_dense(wl: Workload, device, batch_id: int = 0, k_pad: int = 16) -> torch.Tensor:
+    """The dense features of make_x0 (exp(N(0,1)), 13 per sample) in the activation dtype,
+    zero-padded to k_pad columns so that rows are 16-byte multiples."""
+    g = _gen(device, wl.name, "dense", batch_id)
+    h = torch.exp(torch.randn((wl.batch, wl.bottom_mlp[0]), generator=g, device=device))
+    out = torch.zeros((wl.batch, k_pad), dtype=_TORCH[wl.act_dtype], device=device)
+    out[:, :wl.bottom_mlp[0]] = h.to(out.dtype)
+    return out
+
+
+def make_mlp_params(wl: Workload, which: str, sizes, k_pad: int, device):
+    """Dense-layer parameters [(w [N][K'] fp32, b [N] fp32)], w and b ~ U(+-1/sqrt(fan_in));
+    the first layer's input width is zero-padded from sizes[0] to k_pad columns."""
+    gw = _gen(device, wl.name, which + "_mlp")
+    params = []
+    for i, (fan_in, fan_out) in enumerate(zip(sizes[:-1], sizes[1:])):
+        bound = 1.0 / math.sqrt(fan_in)
+        k = k_pad if i == 0 else fan_in
+        w = torch.zeros((fan_out, k), dtype=torch.float32, device=device)
+        w[:, :fan_in] = (torch.rand((fan_out, fan_in), generator=gw, device=device) * 2 - 1) * bound
+        b = (torch.rand((fan_out,), generator=gw, device=device) * 2 - 1) * bound
+        params.append((w, b))
+    return params
+
+
+def make_labels(wl: Workload, device, batch_id: int = 0, rate: float = LABEL_RATE) -> torch.Tensor:
+    """Click labels in {0, 1} (fp32 [B]), Bernoulli(rate)."""
+    g = _gen(device, wl.name, "labels", batch_id)
+    return (torch.rand((wl.batch,), generator=g, device=device) < rate).to(torch.float32)
+
+
+def make_normal(shape, device, dtype: str, *tags, scale: float = 1.0, relu: bool = False) -> torch.Tensor:
+    """A seeded N(0, scale^2) tensor (optionally passed through max(., 0)) in `dtype`, for
+    testing a call on its own."""
+    x = torch.randn(shape, generator=_gen(device, *tags), device=device) * scale
+    if relu:
+        x = torch.clamp_min(x, 0.0)
+    return x.to(_TORCH[dtype]).contiguous()
+
+
 def torch_dtype(name: str) -> torch.dtype:
     return _TORCH[name]
 

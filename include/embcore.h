@@ -189,6 +189,81 @@ EL_API el_status emb_grad_sort(const el_tables* tab, const el_bags* bags, uint32
 EL_API el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t flags,
                            int64_t* bad_count, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Dense layers, logistic loss and dense SGD: the steps on either side of the core (same
+ * page, §Model architecture: the bottom MLP is a series of linear layers with ReLU
+ * activations; the top MLP is a series of dense layers ending in one number, the click
+ * likelihood; §Command-line options: --bottom_mlp_sizes 512,256,128 and --top_mlp_sizes
+ * 1024,1024,512,256,1; the MLPs train in mixed precision with fp32 master weights).
+ * Activations and weights are 16-bit (EL_BF16 or EL_F16, one dtype per call) and every
+ * product accumulates in fp32 (MFMA); weight / bias gradients are fp32.  Weights are
+ * w[n][k], row-major [N][K]: input feature k -> output feature n.
+ * ------------------------------------------------------------------------------------ */
+enum { EL_ACT_NONE = 0u, EL_ACT_RELU = 1u };
+enum { EL_LINEAR_DX_RELU_MASK = 1u };
+
+/*
+ * Dense layer forward:  y[m][n] = act( sum_k x[m][k] * w[n][k] + bias[n] ),  m < M, n < N.
+ * x: [M] rows of stride ldx (first K used); w: [N][K]; bias: fp32 [N] or NULL; y: [M] rows
+ * of stride ldy (first N written), one rounding per output.  act: EL_ACT_NONE or
+ * EL_ACT_RELU.  Shapes: K % 8 == 0, ldx % 8 == 0, N == 1 or N % 8 == 0 (then ldy % 8 == 0);
+ * N == 1 takes K <= 2048 (other shapes EL_ERR_UNSUPPORTED).  x, w, bias 16-byte aligned;
+ * y 16-byte aligned (2-byte when N == 1).  A K not divisible by 8 is served by zero-padding
+ * the inputs and the weight columns, which leaves every output unchanged.
+ */
+EL_API el_status el_linear_fwd(const void* x, int32_t ldx, int32_t M, int32_t K, const void* w,
+                               const float* bias, int32_t N, uint32_t act, void* y, int32_t ldy,
+                               el_dtype dtype, hipStream_t stream);
+
+/* [host, pure] Bytes of device workspace el_linear_bwd needs for these sizes (0 when the
+ * weight gradient needs no partial sums); 0 for invalid sizes. */
+EL_API size_t el_linear_bwd_workspace_bytes(int32_t M, int32_t K, int32_t N);
+
+/*
+ * Dense layer backward, from dz = dL/d(pre-activation) [M] rows of stride ldz:
+ *   dx[m][k] = sum_n dz[m][n] w[n][k]      (dx may be NULL: not computed)
+ *              times 1[x[m][k] > 0] with EL_LINEAR_DX_RELU_MASK (x is then the output of a
+ *              ReLU layer below, and dx is that layer's dz)
+ *   dw[n][k] = sum_m dz[m][n] x[m][k]      fp32 [N][K], overwritten
+ *   db[n]    = sum_m dz[m][n]              fp32 [N], overwritten
+ * The sums over m are split into fixed slices whose fp32 partials are added in slice order:
+ * bitwise reproducible.  dx: [M] rows of stride lddx (lddx % 8 == 0, 16-byte aligned); x,
+ * w, dz as for el_linear_fwd (dz has the shape of y).  workspace: >=
+ * el_linear_bwd_workspace_bytes(M, K, N), 256-byte aligned (may be NULL when that is 0).
+ */
+EL_API el_status el_linear_bwd(const void* x, int32_t ldx, int32_t M, int32_t K, const void* w,
+                               int32_t N, const void* dz, int32_t ldz, void* dx, int32_t lddx,
+                               uint32_t flags, float* dw, float* db, el_dtype dtype,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward of a ReLU from its output y:  dz[m][n] = dy[m][n] * 1[y[m][n] > 0]  (the bottom
+ * MLP's last ReLU, between the interaction gradient dx0 and the last bottom layer).
+ * dy, y, dz: [M] rows of stride ld, first N used; N % 8 == 0, ld % 8 == 0; 16-byte aligned.
+ */
+EL_API el_status el_relu_bwd(const void* dy, const void* y, void* dz, int32_t M, int32_t N,
+                             int32_t ld, el_dtype dtype, hipStream_t stream);
+
+/*
+ * Logistic loss of one logit per sample (the model's output read as a click likelihood;
+ * the page names no loss, binary cross-entropy is the plain reading), batch mean:
+ *   loss[0] = (1/M) sum_m [ max(z_m, 0) - z_m y_m + log(1 + exp(-|z_m|)) ]   (fp32)
+ *   dz[m]   = (sigmoid(z_m) - y_m) / M                                       (dtype)
+ * z: logits at z[m * ldz]; labels: fp32 [M] in {0, 1}; dz at dz[m * lddz].  The loss is
+ * summed in a fixed order (bitwise reproducible).
+ */
+EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, int32_t M,
+                               el_dtype dtype, float* loss, void* dz, int32_t lddz,
+                               hipStream_t stream);
+
+/*
+ * Plain SGD on dense parameters kept in fp32 (--lr, same page):
+ *   master[i] <- master[i] - lr * grad[i]   (one fp32 rounding),   copy[i] <- master[i]
+ * rounded to copy_dtype (EL_BF16 / EL_F16; copy may be NULL).  n elements.
+ */
+EL_API el_status el_sgd_dense(float* master, void* copy, el_dtype copy_dtype, const float* grad,
+                              int64_t n, float lr, hipStream_t stream);
+
 /* Text of the last non-OK status returned on the calling thread ("" if none). */
 EL_API const char* el_last_error(void);
 

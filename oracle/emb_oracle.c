@@ -506,6 +506,21 @@ int oracle_linear_bwd(const void* x, int x_dtype, int M, int K, int ldx, const v
 }
 
 /*
+ * Backward of a ReLU given its output y:  dz[m][n] = dy[m][n] * 1[y[m][n] > 0]  (all three
+ * [M] rows of stride ld, first N used).
+ */
+int oracle_relu_bwd(const void* dy, const void* y, int dtype, int M, int N, int ld, void* dz) {
+  if (!dtype_ok(dtype)) return OR_BAD_DTYPE;
+  if (M < 0 || N < 1 || ld < N) return OR_BAD_SHAPE;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) {
+      size_t i = (size_t)m * ld + n;
+      store_elem(dz, dtype, i, load_elem(y, dtype, i) > 0.0 ? load_elem(dy, dtype, i) : 0.0);
+    }
+  return OR_OK;
+}
+
+/*
  * Logistic loss on one logit per sample, label y in {0, 1} (fp32):
  *   loss = (1/M) sum_m [ max(z,0) - z*y + log(1 + exp(-|z|)) ]      (= -log p or -log(1-p),
  *                                                                     p = 1/(1+exp(-z)))

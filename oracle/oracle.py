@@ -53,11 +53,12 @@ def _configure(L):
     L.oracle_linear_fwd.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, i32]
     L.oracle_linear_bwd.argtypes = [vp, i32, i32, i32, i32, vp, i32, i32, vp, i32, i32, vp, vp,
                                     i32, vp, vp, i32]
+    L.oracle_relu_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     L.oracle_bce_logits.argtypes = [vp, i32, vp, i32, vp, vp, i32]
     L.oracle_sgd_dense.argtypes = [vp, vp, i64, ctypes.c_float, vp, i32]
     for name in ("oracle_emb_bag_fwd", "oracle_dot_interact_fwd", "oracle_dot_interact_bwd",
                  "oracle_grad_sort", "oracle_grad_reduce_update", "oracle_linear_fwd",
-                 "oracle_linear_bwd", "oracle_bce_logits", "oracle_sgd_dense", "oracle_version"):
+                 "oracle_linear_bwd", "oracle_relu_bwd", "oracle_bce_logits", "oracle_sgd_dense", "oracle_version"):
         getattr(L, name).restype = ctypes.c_int
     L.oracle_round_f64.restype = None
     L.oracle_widen.restype = None
@@ -222,6 +223,16 @@ def linear_bwd(x, x_dtype, w, w_dtype, dz, dz_dtype, dx_dtype=None, relu_mask=Fa
                                    _CODES[dx_dtype or "f32"], _ptr(dw), _ptr(db),
                                    _CODES[wgrad_dtype]))
     return dx, dw, db
+
+
+def relu_bwd(dy, y, dtype):
+    """dz = dy * 1[y > 0] for a ReLU with output y; returns dz with dy's shape."""
+    dy = _as(dy, dtype)
+    y = _as(y, dtype)
+    M, N = dy.shape
+    dz = empty((M, N), dtype)
+    _check(lib().oracle_relu_bwd(_ptr(dy), _ptr(y), _CODES[dtype], M, N, N, _ptr(dz)))
+    return dz
 
 
 def bce_logits(z, z_dtype, labels, dz_dtype):

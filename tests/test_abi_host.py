@@ -30,10 +30,12 @@ def test_library_loads_and_exports_every_declared_function():
     assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
                           "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_prepare",
                           "emb_grad_apply", "emb_grad_sort",
-                          "el_validate_bags", "el_last_error", "el_version"}
+                          "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
+                          "el_linear_bwd_workspace_bytes", "el_linear_bwd", "el_relu_bwd",
+                          "el_bce_logits", "el_sgd_dense"}
     for n in names:
         assert hasattr(L, n), n
-    assert ec.el_version() == 100
+    assert ec.el_version() == 200
 
 
 def test_workspace_bytes_is_host_pure_and_scales():
@@ -118,3 +120,51 @@ def test_table_row_limits():
     L = ec.lib()
     t = ec.ElTables(A, A, 1 << 32, 1, 128, ec.EL_F32)  # 2^32 rows: keys would not fit 32 bits
     assert L.emb_bag_fwd(ref(t), ref(bags(F=1)), 0, A, ec.EL_F32, None) == INVALID
+
+
+def test_dense_layer_calls_reject_on_the_host():
+    L = ec.lib()
+    f = L.el_linear_fwd
+    ok = dict(x=A, ldx=1024, M=65536, K=1024, w=A, bias=A, N=1024, act=ec.EL_ACT_RELU, y=A,
+              ldy=1024, dt=ec.EL_BF16)
+
+    def fwd(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["ldx"], a["M"], a["K"], a["w"], a["bias"], a["N"], a["act"], a["y"],
+                 a["ldy"], a["dt"], None)
+
+    assert fwd(K=13) == UNSUPPORTED                 # K not a multiple of 8
+    assert fwd(N=12, ldy=16) == UNSUPPORTED         # N neither 1 nor a multiple of 8
+    assert fwd(N=1, K=4096, ldx=4096) == UNSUPPORTED  # one-output layers take K <= 2048
+    assert fwd(dt=ec.EL_F32) == UNSUPPORTED
+    assert fwd(ldx=1000) == INVALID                 # ldx < K
+    assert fwd(x=A + 8) == INVALID                  # misaligned x
+    assert fwd(w=0) == INVALID
+    assert fwd(act=5) == INVALID
+    assert fwd(bias=A + 4) == INVALID
+    assert fwd(ldy=1000) == INVALID
+    assert "el_linear_fwd" in ec.el_last_error()
+    assert fwd(M=0, x=0, y=0) == ec.EL_OK           # empty batch: nothing enqueued
+
+    need = L.el_linear_bwd_workspace_bytes(65536, 1024, 1024)
+    assert need >= 8 * 1024 * 1024 * 4              # fp32 partial weight gradients of the splits
+    assert L.el_linear_bwd_workspace_bytes(65536, 1024, 1024) == need  # pure
+    assert L.el_linear_bwd_workspace_bytes(-1, 1024, 1024) == 0
+    b = L.el_linear_bwd
+    args = [A, 1024, 65536, 1024, A, 1024, A, 1024, A, 1024, 0, A, A, ec.EL_BF16]
+    assert b(*args, A, need - 1, None) == WORKSPACE
+    assert b(*args, 0, need, None) == WORKSPACE
+    assert b(*args[:10], 2, *args[11:], A, need, None) == INVALID        # unknown flag
+    assert b(*args[:8], None, 1024, ec.EL_LINEAR_DX_RELU_MASK, *args[11:], A, need, None) == INVALID
+    assert b(*args[:11], 0, *args[12:], A, need, None) == INVALID        # null dw
+    assert "el_linear_bwd" in ec.el_last_error()
+
+    assert L.el_relu_bwd(A, A, A, 100, 12, 16, ec.EL_BF16, None) == UNSUPPORTED
+    assert L.el_relu_bwd(A, A, A + 2, 100, 16, 16, ec.EL_BF16, None) == INVALID
+    assert L.el_relu_bwd(A, A, A, 0, 16, 16, ec.EL_BF16, None) == ec.EL_OK
+    assert L.el_bce_logits(A, 1, A, 0, ec.EL_BF16, A, A, 1, None) == INVALID
+    assert L.el_bce_logits(A, 1, A, 16, ec.EL_F32, A, A, 1, None) == UNSUPPORTED
+    assert L.el_bce_logits(A, 1, 0, 16, ec.EL_BF16, A, A, 1, None) == INVALID
+    assert L.el_sgd_dense(A, A, ec.EL_BF16, A, -1, ctypes.c_float(0.01), None) == INVALID
+    assert L.el_sgd_dense(A, A, 9, A, 10, ctypes.c_float(0.01), None) == UNSUPPORTED
+    assert L.el_sgd_dense(A, A, ec.EL_BF16, A, 0, ctypes.c_float(0.01), None) == ec.EL_OK

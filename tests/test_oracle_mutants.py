@@ -53,6 +53,9 @@ MUTANTS = [
      "for (int m = 0; m < M; ++m) s += load_elem(dz, dz_dtype, (size_t)m * ldz);"),
     ("logistic gradient sign", "store_elem(dz, dz_dtype, (size_t)m, (p - y) / (double)M);",
      "store_elem(dz, dz_dtype, (size_t)m, (y - p) / (double)M);"),
+    ("ReLU backward passes gradients at y = 0",
+     "store_elem(dz, dtype, i, load_elem(y, dtype, i) > 0.0 ? load_elem(dy, dtype, i) : 0.0);",
+     "store_elem(dz, dtype, i, load_elem(y, dtype, i) >= 0.0 ? load_elem(dy, dtype, i) : 0.0);"),
     ("loss not averaged", "*loss = s / (double)M;", "*loss = s;"),
     ("dense SGD sign", "master[i] = (float)((double)master[i] - (double)lr * (double)grad[i]);",
      "master[i] = (float)((double)master[i] + (double)lr * (double)grad[i]);"),
@@ -93,6 +96,7 @@ def battery():
         pins.test_bce_gradient_central_differences,
         pins.test_sgd_dense_special_cases,
         pins.test_mlp_chain_gradient_central_differences,
+        pins.test_relu_bwd_is_the_relu_derivative,
     ]
 
 

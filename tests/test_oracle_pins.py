@@ -791,3 +791,16 @@ def test_mlp_chain_gradient_central_differences():
             fd = (loss(p, w1) - loss(q, w1)) / (2 * h) if which == 0 else \
                 (loss(x, p) - loss(x, q)) / (2 * h)
             assert abs(fd - grad[idx]) < 1e-7
+
+
+def test_relu_bwd_is_the_relu_derivative():
+    """dz = dy where y > 0, else 0 (y = 0 at the kink, negative zero and NaN give 0): the
+    derivative of the ReLU, written out element by element."""
+    rng = np.random.default_rng(15)
+    dy = rng.standard_normal((3, 5))
+    y = np.maximum(rng.standard_normal((3, 5)), 0.0)
+    y[0, 0], y[0, 1], y[0, 2] = 0.0, -0.0, np.nan
+    dz = orc.relu_bwd(dy, y, "f64")
+    for idx in np.ndindex(y.shape):
+        assert dz[idx] == (dy[idx] if y[idx] > 0 else 0.0)
+    assert np.count_nonzero(dz) == np.count_nonzero(y > 0)
