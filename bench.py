@@ -163,6 +163,9 @@ def main():
     if args.inference_sweep:
         inference_sweep(dev, args.workload if args.workload != "train_step" else "large_table")
         return
+    if args.workload == "dlrm_step":
+        dlrm_bench(args, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     B, F, D = wl.batch, wl.num_tables, wl.dim
     act = synth.act_dtype(wl)
@@ -349,6 +352,183 @@ def main():
         if omp:
             result["cpu_baseline_openmp"] = omp
     print(json.dumps(result), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def dlrm_bench(args, dev):
+    """The whole DLRM training step on the train_step shapes: bottom MLP 13-512-256-128,
+    emb-bag + dot interaction, top MLP 479-1024-1024-512-256-1, logistic loss, backward of
+    every stage, SGD (lr 0.01) on the dense parameters and the embedding rows; the sort of
+    the lookups on a side stream from the start of the step.  Reports samples/s, per-stage
+    HIP-event times, and each dense layer's forward / backward timed on its own (TFLOP/s vs
+    the bf16 MFMA peak); the roofline object is the dominant dense-layer product."""
+    import embedding_lookup_feature_amd as elf
+    from embedding_lookup_feature_amd import dlrm, synth
+
+    wl = synth.WORKLOADS["train_step"]
+    B = wl.batch
+    W, ro = synth.make_tables(wl, dev)
+    tab = elf.Tables(W, ro)
+    batches = []
+    for i in range(args.batches):
+        idx, off = synth.make_indices(wl, dev, batch_id=i)
+        batches.append((elf.Bags(idx, off, B), synth.make_dense(wl, dev, i), synth.make_labels(wl, dev, i)))
+    step = dlrm.DLRMStep(wl, tab, dev)
+    ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches), dtype=torch.uint8, device=dev)
+    side = torch.cuda.Stream()  # default priority
+
+    def run(i, mark=None):
+        bags, dense, labels = batches[i % len(batches)]
+        step.train_step(dense, bags, labels, ws, side=side, mark=mark)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    side.wait_stream(torch.cuda.current_stream())
+    for i in range(args.steps):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # per-stage HIP events on the main stream (the sort runs beside them on the side stream)
+    stage = {}
+    for i in range(args.steps):
+        marks = [("start", torch.cuda.Event(enable_timing=True))]
+        marks[0][1].record()
+
+        def mark(name, marks=marks):
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append((name, e))
+        run(i, mark)
+        torch.cuda.synchronize()
+        for (_, a), (n, b) in zip(marks[:-1], marks[1:]):
+            stage.setdefault(n, []).append(a.elapsed_time(b))
+    stages = {n: {"median_ms": round(pct(v, 50), 4), "p10_ms": round(pct(v, 10), 4),
+                  "p90_ms": round(pct(v, 90), 4)} for n, v in stage.items()}
+
+    # each dense layer on its own: forward, and backward (data + weight gradients)
+    layers = []
+    reps = max(10, args.steps // 5)
+    shapes = [("bottom", i, s) for i, s in enumerate(step.bottom.shapes)] + \
+             [("top", i, s) for i, s in enumerate(step.top.shapes)]
+    real_k = dict(zip(range(len(shapes)), [wl.bottom_mlp[0]] + [k for (_, k) in step.bottom.shapes[1:]] +
+                      [wl.out_width] + [k for (_, k) in step.top.shapes[1:]]))
+    for li, (which, i, (N, K)) in enumerate(shapes):
+        mlp = step.bottom if which == "bottom" else step.top
+        acts = step.h_bot if which == "bottom" else step.h_top
+        x = (batches[0][1] if i == 0 else acts[i - 1]) if which == "bottom" else (step.inter if i == 0 else acts[i - 1])
+        y = acts[i]
+        relu = which == "bottom" or i < len(mlp.w) - 1
+        dz = torch.zeros_like(y)
+        dx = torch.empty_like(x) if not (which == "bottom" and i == 0) else None
+        res = {}
+        for kind in ("fwd", "bwd"):
+            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for e0, e1 in es:
+                e0.record()
+                if kind == "fwd":
+                    elf.linear_fwd(x, mlp.w[i], mlp.b[i], y, relu=relu)
+                else:
+                    elf.linear_bwd(x, mlp.w[i], dz, mlp.dw[i], mlp.db[i], dx=dx, relu_mask=dx is not None and i > 0,
+                                   workspace=step.lin_ws)
+                e1.record()
+            torch.cuda.synchronize()
+            ms = float(np.mean([a.elapsed_time(b) for a, b in es]))
+            flops = 2 * B * N * real_k[li] * (1 if kind == "fwd" else (2 if dx is not None else 1))
+            res[kind] = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1)}
+        layers.append({"layer": f"{which}{i}", "K": real_k[li], "N": N, **res})
+    dom = max(layers, key=lambda l: l["fwd"]["ms"] + l["bwd"]["ms"])
+    achieved = dom["fwd"]["tflops"]
+    flops = step.dense_flops()
+    total_dense = sum(flops.values())
+    dense_ms = sum(l["fwd"]["ms"] + l["bwd"]["ms"] for l in layers)
+    result = {
+        "metric": f"samples/s fwd+bwd, whole DLRM step (bottom MLP + emb-bag + dot interaction + top MLP "
+                  f"+ logistic loss, SGD) at batch {B}",
+        "value": round(B / (ms_per_step * 1e-3), 1),
+        "unit": "samples/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dlrm_step: train_step shapes (26 fp32 tables x 100,000 x 128, Zipf(1.05) "
+                               "hotness 1) + bottom MLP 13-512-256-128 + top MLP 479-1024-1024-512-256-1 "
+                               "+ logistic loss on Bernoulli(0.25) labels, SGD lr 0.01 everywhere",
+                   "global_batch": B, "parallelism": "single-gpu"},
+        "dense_gflop_per_step": round(total_dense / 1e9, 1),
+        "dense_tflops_in_isolation": round(total_dense / (dense_ms * 1e-3) / 1e12, 1),
+        "stages": stages,
+        "dense_layers": layers,
+        "roofline": {"bound": "mfma", "kernel": f"k_gemm forward, {dom['layer']} ({dom['K']} -> {dom['N']})",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = dlrm_cpu_baseline(wl, W, ro, step, batches[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def dlrm_cpu_baseline(wl, W, ro, step, batch, seconds):
+    """The oracle's whole DLRM step (forward, loss, backward, SGD of the dense layers and of
+    the touched embedding rows) over the first n samples of batch 0, single-threaded and
+    pinned to one core; n sized for about `seconds`."""
+    from oracle import oracle as orc
+    from tests.helpers import sub_batch, to_np
+
+    bags, dense, labels = batch
+    F, B, D, dt = wl.num_tables, wl.batch, wl.dim, wl.act_dtype
+    W_h, ro_h = to_np(W), to_np(ro)
+    idx_h, off_h = to_np(bags.indices), to_np(bags.offsets)
+    dense_h, lab_h = to_np(dense), to_np(labels)
+    bw = [to_np(w) for w in step.bottom.w]
+    bb = [to_np(b) for b in step.bottom.b]
+    tw = [to_np(w) for w in step.top.w]
+    tb = [to_np(b) for b in step.top.b]
+    bm, tm = to_np(step.bottom.master), to_np(step.top.master)
+
+    def run(n):
+        si, so, nb = sub_batch(idx_h, off_h, F, B, np.arange(n))
+        t = time.perf_counter()
+        hs = [dense_h[:n]]
+        for w, b in zip(bw, bb):
+            hs.append(orc.linear_fwd(hs[-1], dt, w, dt, b, True, dt))
+        emb = orc.emb_bag_fwd(W_h, wl.table_dtype, ro_h, si, so, nb, D, dt)
+        ts = [orc.dot_interact_fwd(hs[-1], emb, dt, dt, wl.out_stride)]
+        for j, (w, b) in enumerate(zip(tw, tb)):
+            ts.append(orc.linear_fwd(ts[-1], dt, w, dt, b, j < len(tw) - 1, dt))
+        _, dz = orc.bce_logits(ts[-1], dt, lab_h[:n], dt)
+        dz = dz.reshape(n, 1)
+        for j in reversed(range(len(tw))):
+            dz, _, _ = orc.linear_bwd(ts[j], dt, tw[j], dt, dz, dt, dx_dtype=dt, relu_mask=j > 0)
+        dx0, demb = orc.dot_interact_bwd(hs[-1], emb, dt, dz, dt, dt)
+        dz = orc.relu_bwd(dx0, hs[-1], dt)
+        for j in reversed(range(len(bw))):
+            dz, _, _ = orc.linear_bwd(hs[j], dt, bw[j], dt, dz, dt, dx_dtype=dt if j > 0 else None,
+                                      relu_mask=j > 0)
+        orc.sgd_dense(bm, np.zeros_like(bm), wl.lr)
+        orc.sgd_dense(tm, np.zeros_like(tm), wl.lr)
+        orc.grad_reduce_update(W_h, wl.table_dtype, ro_h, si, so, nb, demb, dt, wl.lr)
+        return time.perf_counter() - t
+
+    model, nproc = cpu_info()
+    old = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old)})
+    try:
+        probe = 16
+        dt_probe = run(probe)
+        n = int(min(B, max(probe, probe * seconds / max(dt_probe, 1e-6))))
+        dt_run = run(n)
+    finally:
+        os.sched_setaffinity(0, old)
+    return {"value": round(n / dt_run, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {B} samples of batch 0: the whole step (dense layers, full tables, "
+                      f"SGD of all dense parameters and a full-table copy for the row update), "
+                      f"single-threaded C oracle pinned to one core, {dt_run:.1f} s",
+            "host_cpu": model, "host_cpus_visible": nproc}
 
 
 def inference_sweep(dev, workload, sizes=(1, 16, 256, 4096, 65536, 262144, 1048576), iters=100):

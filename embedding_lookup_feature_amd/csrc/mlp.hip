@@ -46,7 +46,7 @@ struct GemmArgs {
   long ldq;
   int R, C;           // output rows, cols
   int red;            // reduction length
-  int red_per_split;  // reduction per blockIdx.y (multiple of kBK)
+  int red_per_split;  // reduction per split (multiple of kBK)
   int tiles_c, tiles;  // column tiles, tiles per split
   void* out;          // fwd / dgrad: [R][ldo] 16-bit; wgrad: fp32 [split][R][ldo]
   long ldo;
@@ -58,91 +58,142 @@ struct GemmArgs {
   float* dbp;         // wgrad: [split][R] row sums of the rows operand (bias gradient)
 };
 
-// 16 bytes from global memory or zeros.
-__device__ inline u32x4 ld16(const uint16_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+// 16 bytes from global memory.  The load is unconditional (from `safe`, the operand's base,
+// for a vector outside the operand) so that no branch splits the stream of loads; the caller
+// zeroes such vectors only when it writes them to LDS, so nothing waits for a load before
+// its stage needs it.
+__device__ inline u32x4 ld16(const uint16_t* p, const uint16_t* safe, bool ok) {
+  return *reinterpret_cast<const u32x4*>(ok ? p : safe);
+}
+__device__ inline u32x4 keep_if(const u32x4& v, uint32_t mask, int i) {
+  return ((mask >> i) & 1u) ? v : u32x4{0, 0, 0, 0};
 }
 
-// Global -> registers for one operand tile.
-//  RC (reduction contiguous): 128 rows x 64 reduction; all 256 threads, 4 vectors each
-//    (thread t: row t/8 + 32 i, reduction 8 (t%8) .. +8).
-//  OC (output contiguous): global [red][rows]; 128 threads, an 8 x 8 block each
-//    (thread s: reduction block s%8, row block s/8; 8 vectors of 8 rows at 8 reductions).
-template <bool RC>
-struct TileLoader {
-  static constexpr int N = RC ? 4 : 8;
-  u32x4 v[N];
+// Global -> registers for one reduction-contiguous operand tile: 128 rows x 64 reduction;
+// all 256 threads, 4 vectors each (thread t: row t/8 + 32 i, reduction 8 (t%8) .. +8).
+struct TileLoaderRC {
+  u32x4 v[4];
+  uint32_t ok = 0;  // bit i: vector i lies inside the operand
   __device__ inline void load(const uint16_t* base, long ld, int row0, int nrows, int k0, int kend,
                               int sub) {
-    if constexpr (RC) {
-      const int kk = k0 + (sub & 7) * 8;
+    const int kk = k0 + (sub & 7) * 8;
+    ok = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = row0 + (sub >> 3) + 32 * i;
-        v[i] = ld16(base + static_cast<long>(r) * ld + kk, r < nrows && kk < kend);
-      }
-    } else {
-      const int kb = sub & 7, rb = sub >> 3;
-      const int r = row0 + rb * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kb * 8 + i;
-        v[i] = ld16(base + static_cast<long>(k) * ld + r, r < nrows && k < kend);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + (sub >> 3) + 32 * i;
+      const bool in = r < nrows && kk < kend;
+      v[i] = ld16(base + static_cast<long>(r) * ld + kk, base, in);
+      ok |= static_cast<uint32_t>(in) << i;
     }
   }
   __device__ inline void store(uint16_t* lds, int sub) const {
-    if constexpr (RC) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + 32 * i) * kPitch + (sub & 7) * 8) = v[i];
-    } else {
-      const int kb = sub & 7, rb = sub >> 3;
-      // 8 x 8 transpose: out[j] holds row rb*8 + j at reductions kb*8 .. +8.
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + 32 * i) * kPitch + (sub & 7) * 8) = keep_if(v[i], ok, i);
+  }
+};
+
+// One LDS stage of the product: this wavefront's 64 x 64 block accumulates the kBK-long
+// slice held in P (rows operand) and Q (cols operand); with DB, threads 0..127 also add up
+// their row of P (the bias gradient of the weight-gradient launch).
+// Both operands output-contiguous (the weight gradient, global [red][rows]): threads 0..127
+// fetch the rows operand's 128 blocks of 8 rows x 8 reductions and threads 128..255 the
+// cols operand's, through one code path (operand chosen by per-thread selects, no branch
+// between the two sets of loads); each block is transposed in registers on its way to LDS.
+struct PairLoaderOC {
+  u32x4 v[8];
+  uint32_t ok = 0;
+  const uint16_t* base;
+  long ld;
+  int row0, nrows, sub;
+  __device__ inline PairLoaderOC(const GemmArgs& a, int tid, int prow0, int qcol0) {
+    const bool q = tid >= 128;
+    base = q ? a.Q : a.P;
+    ld = q ? a.ldq : a.ldp;
+    row0 = q ? qcol0 : prow0;
+    nrows = q ? a.C : a.R;
+    sub = tid & 127;
+  }
+  __device__ inline void load(int k0, int kend) {
+    const int kb = sub & 7, rb = sub >> 3;
+    const int r = row0 + rb * 8;
+    ok = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int w = j >> 1;
-        u32x4 o;
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + kb * 8 + i;
+      const bool in = r < nrows && k < kend;
+      v[i] = ld16(base + static_cast<long>(k) * ld + r, base, in);
+      ok |= static_cast<uint32_t>(in) << i;
+    }
+  }
+  __device__ inline void store(uint16_t* lds) const {
+    const int kb = sub & 7, rb = sub >> 3;
+    u32x4 z[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t a = v[2 * q][w], b = v[2 * q + 1][w];
-          o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-        }
-        *reinterpret_cast<u32x4*>(lds + (rb * 8 + j) * kPitch + kb * 8) = o;
+    for (int i = 0; i < 8; ++i) z[i] = keep_if(v[i], ok, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = j >> 1;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t a = z[2 * q][w], b = z[2 * q + 1][w];
+        o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
       }
+      *reinterpret_cast<u32x4*>(lds + (rb * 8 + j) * kPitch + kb * 8) = o;
     }
   }
 };
 
+template <class T, bool DB>
+__device__ __forceinline__ void gemm_stage(const uint16_t* P, const uint16_t* Q, int wr, int wc, int half,
+                                           int l32, f32x16 (&acc)[2][2], bool do_db, int tid, float& dbsum) {
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    const int ko = ks * 16 + half * 8;
+    u32x4 qa[2], pb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      qa[i] = *reinterpret_cast<const u32x4*>(Q + (wc * 64 + i * 32 + l32) * kPitch + ko);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      pb[j] = *reinterpret_cast<const u32x4*>(P + (wr * 64 + j * 32 + l32) * kPitch + ko);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(qa[i], pb[j], acc[i][j]);
+  }
+  if (DB && do_db) {
+    const uint16_t* row = P + tid * kPitch;
+#pragma unroll
+    for (int v = 0; v < kBK / 8; ++v) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(row + v * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dbsum += T::to_f(static_cast<uint16_t>(x[q] & 0xffffu)) + T::to_f(static_cast<uint16_t>(x[q] >> 16));
+    }
+  }
+}
+
 template <class T, bool P_RC, bool Q_RC, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][kTile];
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nb = a.tiles;
-  const int bid = (nb & 7) == 0 ? xcd_remap(blockIdx.x, nb) : static_cast<int>(blockIdx.x);
+  // One flat grid of tiles x splits, in split-major logical order, handed to the XCDs in
+  // contiguous runs: the workgroups of one split (which share its batch slice of both
+  // operands) and the neighbouring tiles of one output row (which share a panel) meet in
+  // the same L2.
+  const int nb = static_cast<int>(gridDim.x);
+  const int lid = (nb & 7) == 0 ? xcd_remap(blockIdx.x, nb) : static_cast<int>(blockIdx.x);
+  const int split = lid / a.tiles;
+  const int bid = lid - split * a.tiles;
   const int tr = bid / a.tiles_c, tc = bid - tr * a.tiles_c;
   const int row0 = tr * kBR, col0 = tc * kBC;
-  const int split = blockIdx.y;
   const int kbeg = split * a.red_per_split;
   const int kend = min(a.red, kbeg + a.red_per_split);
   const int nk = (kend - kbeg + kBK - 1) / kBK;
-
-  // Which threads load which operand: an RC operand uses all threads; an OC operand uses
-  // threads 0..127 (rows operand) or 128..255 (cols operand).
-  const bool p_me = P_RC || tid < 128;
-  const bool q_me = Q_RC || tid >= 128;
-  const int p_sub = P_RC ? tid : tid;
-  const int q_sub = Q_RC ? tid : tid - 128;
-
-  TileLoader<P_RC> lp;
-  TileLoader<Q_RC> lq;
-  if (p_me) lp.load(a.P, a.ldp, row0, a.R, kbeg, kend, p_sub);
-  if (q_me) lq.load(a.Q, a.ldq, col0, a.C, kbeg, kend, q_sub);
-  if (p_me) lp.store(sP[0], p_sub);
-  if (q_me) lq.store(sQ[0], q_sub);
-  __syncthreads();
 
   const int wr = wave >> 1, wc = wave & 1;  // 64 x 64 output block of this wavefront
   const int half = lane >> 5, l32 = lane & 31;
@@ -156,46 +207,46 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
   const bool do_db = (EPI == EPI_WGRAD) && tc == 0 && tid < 128;
   float dbsum = 0.f;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = kbeg + (kt + 1) * kBK;
-      if (p_me) lp.load(a.P, a.ldp, row0, a.R, k0, kend, p_sub);
-      if (q_me) lq.load(a.Q, a.ldq, col0, a.C, k0, kend, q_sub);
-    }
-    const uint16_t* P = sP[cur];
-    const uint16_t* Q = sQ[cur];
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int ko = ks * 16 + half * 8;
-      u32x4 qa[2], pb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        qa[i] = *reinterpret_cast<const u32x4*>(Q + (wc * 64 + i * 32 + l32) * kPitch + ko);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        pb[j] = *reinterpret_cast<const u32x4*>(P + (wr * 64 + j * 32 + l32) * kPitch + ko);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(qa[i], pb[j], acc[i][j]);
-    }
-    if (do_db) {
-      const uint16_t* row = P + tid * kPitch;
-#pragma unroll
-      for (int v = 0; v < kBK / 8; ++v) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(row + v * 8);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dbsum += T::to_f(static_cast<uint16_t>(x[q] & 0xffffu)) + T::to_f(static_cast<uint16_t>(x[q] >> 16));
-      }
-    }
-    if (more) {
-      if (p_me) lp.store(sP[cur ^ 1], p_sub);
-      if (q_me) lq.store(sQ[cur ^ 1], q_sub);
-    }
+  // One register set: stage kt+1's loads are issued before stage kt is multiplied out of
+  // LDS and written to the other LDS buffer after it; several workgroups per CU hide the
+  // rest of the load latency.  Loads past the last stage re-read it (never written), so
+  // every stage issues the same unconditional loads.
+  if constexpr (P_RC && Q_RC) {
+    TileLoaderRC lp, lq;
+    lp.load(a.P, a.ldp, row0, a.R, kbeg, kend, tid);
+    lq.load(a.Q, a.ldq, col0, a.C, kbeg, kend, tid);
+    lp.store(sP[0], tid);
+    lq.store(sQ[0], tid);
     __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const int k1 = kbeg + min(kt + 1, nk - 1) * kBK;
+      lp.load(a.P, a.ldp, row0, a.R, k1, kend, tid);
+      lq.load(a.Q, a.ldq, col0, a.C, k1, kend, tid);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's products
+      gemm_stage<T, false>(sP[cur], sQ[cur], wr, wc, half, l32, acc, false, tid, dbsum);
+      if (kt + 1 < nk) {
+        lp.store(sP[cur ^ 1], tid);
+        lq.store(sQ[cur ^ 1], tid);
+      }
+      __syncthreads();
+    }
+  } else {
+    static_assert(!P_RC && !Q_RC, "mixed operand layouts are not instantiated");
+    PairLoaderOC l(a, tid, row0, col0);
+    uint16_t* dst[2] = {tid >= 128 ? sQ[0] : sP[0], tid >= 128 ? sQ[1] : sP[1]};
+    l.load(kbeg, kend);
+    l.store(dst[0]);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const int k1 = kbeg + min(kt + 1, nk - 1) * kBK;
+      l.load(k1, kend);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's products
+      gemm_stage<T, EPI == EPI_WGRAD>(sP[cur], sQ[cur], wr, wc, half, l32, acc, do_db, tid, dbsum);
+      if (kt + 1 < nk) l.store(dst[cur ^ 1]);
+      __syncthreads();
+    }
   }
 
   if (EPI == EPI_WGRAD && do_db && row0 + tid < a.R) a.dbp[static_cast<long>(split) * a.R + row0 + tid] = dbsum;
@@ -245,23 +296,63 @@ __global__ __launch_bounds__(kThreads) void k_gemm(GemmArgs a) {
   }
 }
 
+// wt[k][n] = w[n][k] for a [N][K] 16-bit matrix (N, K multiples of 8): one 8 x 8 block
+// per thread, transposed in registers.
+__global__ __launch_bounds__(256) void k_transpose16(const uint16_t* w, uint16_t* wt, int N, int K) {
+  const int kv = K / 8;
+  const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= static_cast<long>(N / 8) * kv) return;
+  const int nb = static_cast<int>(g / kv), kb = static_cast<int>(g - static_cast<long>(nb) * kv);
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const u32x4*>(w + static_cast<long>(nb * 8 + i) * K + kb * 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q2 = j >> 1;
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = v[2 * q][q2], b = v[2 * q + 1][q2];
+      o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+    *reinterpret_cast<u32x4*>(wt + static_cast<long>(kb * 8 + j) * N + nb * 8) = o;
+  }
+}
+
 // Ordered sum of the split partials: out[i] = sum_s part[s][i] (i < n), and the bias
 // gradient db[i] = sum_s dbp[s][i] (i < nb).
 __global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, int splits, float* out,
                                                    const float* dbp, int nb, float* db) {
+  // loads are issued in groups of 8 splits before they are added (in split order)
   const long i4 = (static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i4 < n) {
-    float4 s = *reinterpret_cast<const float4*>(part + i4);
-    for (int p = 1; p < splits; ++p) {
-      const float4 v = *reinterpret_cast<const float4*>(part + p * n + i4);
-      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < splits; p0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < splits) v[q] = *reinterpret_cast<const float4*>(part + (p0 + q) * n + i4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < splits) {
+          s.x += v[q].x; s.y += v[q].y; s.z += v[q].z; s.w += v[q].w;
+        }
     }
     *reinterpret_cast<float4*>(out + i4) = s;
   }
   const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (g < nb) {
-    float s = dbp[g];
-    for (int p = 1; p < splits; ++p) s += dbp[static_cast<long>(p) * nb + g];
+    float s = 0.f;
+    for (int p0 = 0; p0 < splits; p0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < splits) v[q] = dbp[static_cast<long>(p0 + q) * nb + g];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < splits) s += v[q];
+    }
     db[g] = s;
   }
 }
@@ -379,12 +470,23 @@ __global__ __launch_bounds__(1024) void k_bce(const uint16_t* z, long ldz, const
   const int t = threadIdx.x;
   double s = 0.0;
   const float inv = 1.0f / static_cast<float>(M);
-  for (int m = t; m < M; m += 1024) {
-    const float v = T::to_f(z[static_cast<long>(m) * ldz]);
-    const float y = labels[m];
-    s += static_cast<double>(fmaxf(v, 0.f) - v * y + log1pf(expf(-fabsf(v))));
-    const float p = 1.f / (1.f + expf(-v));
-    dz[static_cast<long>(m) * lddz] = T::from_f((p - y) * inv);
+  // 8 samples per thread and round: their loads are issued before any of them is used
+  for (int m0 = t; m0 < M; m0 += 8 * 1024) {
+    float v[8], y[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int m = m0 + q * 1024;
+      v[q] = m < M ? T::to_f(z[static_cast<long>(m) * ldz]) : 0.f;
+      y[q] = m < M ? labels[m] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int m = m0 + q * 1024;
+      if (m >= M) break;
+      s += static_cast<double>(fmaxf(v[q], 0.f) - v[q] * y[q] + log1pf(expf(-fabsf(v[q]))));
+      const float p = 1.f / (1.f + expf(-v[q]));
+      dz[static_cast<long>(m) * lddz] = T::from_f((p - y[q]) * inv);
+    }
   }
   red[t] = s;
   __syncthreads();
@@ -449,8 +551,9 @@ bool al(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 
 
 struct WgradPlan {
   int splits = 1;
-  int per = 0;     // reduction rows per split
-  size_t bytes = 0;
+  int per = 0;        // reduction rows per split
+  size_t wt_bytes = 0;  // transposed weights for the data gradient (256-byte multiple)
+  size_t bytes = 0;     // total
 };
 
 // Splits of the weight-gradient reduction over the batch: enough workgroups to cover the
@@ -468,12 +571,14 @@ WgradPlan plan_wgrad(int M, int K, int N) {
   const int tiles = ((N + kBR - 1) / kBR) * ((K + kBC - 1) / kBC);
   int s = std::max(1, (512 + tiles - 1) / tiles);
   const int max_s = std::max(1, M / (4 * kBK));
-  s = std::min(std::min(s, max_s), 64);
+  s = std::min(std::min(s, max_s), 256);
   int per = (M + s - 1) / s;
   per = (per + kBK - 1) / kBK * kBK;
   p.splits = (M + per - 1) / per;
   p.per = per;
-  p.bytes = p.splits > 1 ? static_cast<size_t>(p.splits) * (static_cast<size_t>(N) * K + N) * sizeof(float) : 0;
+  p.wt_bytes = (static_cast<size_t>(N) * K * 2 + 255) / 256 * 256;
+  p.bytes = p.wt_bytes +
+            (p.splits > 1 ? static_cast<size_t>(p.splits) * (static_cast<size_t>(N) * K + N) * sizeof(float) : 0);
   return p;
 }
 
@@ -532,14 +637,18 @@ el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16
                        pl.splits, dw, dbp, 1, db);
     return check_launch("el_linear_bwd");
   }
-  if (dx) {
+  if (dx) {  // dx = dz w: with w transposed once into the workspace, both operands are
+             // reduction-contiguous, as in the forward
+    uint16_t* wt = static_cast<uint16_t*>(ws);
+    const long nblk = static_cast<long>(N / 8) * (K / 8);
+    hipLaunchKernelGGL(k_transpose16, dim3((nblk + 255) / 256), dim3(256), 0, st, w, wt, N, K);
     GemmArgs a{};
-    a.P = dz; a.ldp = ldz; a.Q = w; a.ldq = K;
+    a.P = dz; a.ldp = ldz; a.Q = wt; a.ldq = N;
     a.R = M; a.C = K; a.red = N; a.red_per_split = (N + kBK - 1) / kBK * kBK;
     a.tiles_c = (K + kBC - 1) / kBC;
     a.tiles = ((M + kBR - 1) / kBR) * a.tiles_c;
     a.out = dx; a.ldo = lddx; a.relu = mask; a.mask = x; a.ldm = ldx;
-    hipLaunchKernelGGL((k_gemm<T, true, false, EPI_DGRAD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((k_gemm<T, true, true, EPI_DGRAD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
   }
   GemmArgs b{};
   b.P = dz; b.ldp = ldz; b.Q = x; b.ldq = ldx;
@@ -550,10 +659,10 @@ el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16
     b.out = dw; b.ldo = K; b.split_stride = 0; b.dbp = db;
     hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles, 1), dim3(kThreads), 0, st, b);
   } else {
-    float* part = static_cast<float*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.wt_bytes);
     float* dbp = part + static_cast<size_t>(pl.splits) * N * K;
     b.out = part; b.ldo = K; b.split_stride = static_cast<long>(N) * K; b.dbp = dbp;
-    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles, pl.splits), dim3(kThreads), 0, st, b);
+    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles * pl.splits), dim3(kThreads), 0, st, b);
     const long n = static_cast<long>(N) * K;
     const long nthr = std::max<long>((n + 3) / 4, N);
     hipLaunchKernelGGL(k_split_sum, dim3((nthr + 255) / 256), dim3(256), 0, st, part, n, pl.splits, dw, dbp,

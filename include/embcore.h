@@ -215,8 +215,9 @@ EL_API el_status el_linear_fwd(const void* x, int32_t ldx, int32_t M, int32_t K,
                                const float* bias, int32_t N, uint32_t act, void* y, int32_t ldy,
                                el_dtype dtype, hipStream_t stream);
 
-/* [host, pure] Bytes of device workspace el_linear_bwd needs for these sizes (0 when the
- * weight gradient needs no partial sums); 0 for invalid sizes. */
+/* [host, pure] Bytes of device workspace el_linear_bwd needs for these sizes (a transposed
+ * copy of w for the data gradient, and the fp32 partial sums of the weight gradient's
+ * batch slices); 0 for invalid sizes or M == 0. */
 EL_API size_t el_linear_bwd_workspace_bytes(int32_t M, int32_t K, int32_t N);
 
 /*
