@@ -22,6 +22,7 @@ from .embcore import (  # noqa: F401
     emb_grad_sort,
     emb_grad_workspace_bytes,
     bce_logits,
+    bce_workspace_bytes,
     linear_bwd,
     linear_bwd_workspace_bytes,
     linear_fwd,

@@ -242,7 +242,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs a) {
       const int cur = kt & 1;
       const int k1 = kbeg + min(kt + 1, nk - 1) * kBK;
       l.load(k1, kend);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's products
       gemm_stage<T, EPI == EPI_WGRAD>(sP[cur], sQ[cur], wr, wc, half, l32, acc, do_db, tid, dbsum);
       if (kt + 1 < nk) l.store(dst[cur ^ 1]);
       __syncthreads();
@@ -320,41 +319,66 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* w, uint16_t
   }
 }
 
-// Ordered sum of the split partials: out[i] = sum_s part[s][i] (i < n), and the bias
-// gradient db[i] = sum_s dbp[s][i] (i < nb).
-__global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, int splits, float* out,
-                                                   const float* dbp, int nb, float* db) {
-  // loads are issued in groups of 8 splits before they are added (in split order)
-  const long i4 = (static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
-  if (i4 < n) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < splits; p0 += 8) {
-      float4 v[8];
+// Ordered sum of the split partials: out[c] = sum_s part[s][c] (c < n; VEC consecutive
+// columns per thread, n % VEC == 0).  Each workgroup covers 16 column vectors with 16
+// split groups: group g adds splits g, g+16, g+32, ... in order (loads issued 8 at a time),
+// then the 16 group sums are added in group order.  Bitwise reproducible.
+template <int VEC>
+__global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, int splits, float* out) {
+  constexpr int SG = 16, CV = 256 / SG;
+  __shared__ float red[SG][CV * VEC];
+  const int t = threadIdx.x, cv = t % CV, sg = t / CV;
+  const long c = (static_cast<long>(blockIdx.x) * CV + cv) * VEC;
+  float s[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s[e] = 0.f;
+  if (c < n) {
+    for (int p0 = sg; p0 < splits; p0 += SG * 8) {
+      float v[8][VEC];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int p = p0 + q * SG;
+        if (p < splits) {
+          if constexpr (VEC == 4) {
+            const float4 x = *reinterpret_cast<const float4*>(part + p * n + c);
+            v[q][0] = x.x; v[q][1] = x.y; v[q][2] = x.z; v[q][3] = x.w;
+          } else {
+            v[q][0] = part[p * n + c];
+          }
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        if (p0 + q < splits) v[q] = *reinterpret_cast<const float4*>(part + (p0 + q) * n + i4);
+        if (p0 + q * SG < splits) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (p0 + q < splits) {
-          s.x += v[q].x; s.y += v[q].y; s.z += v[q].z; s.w += v[q].w;
+          for (int e = 0; e < VEC; ++e) s[e] += v[q][e];
         }
     }
-    *reinterpret_cast<float4*>(out + i4) = s;
   }
-  const long g = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (g < nb) {
-    float s = 0.f;
-    for (int p0 = 0; p0 < splits; p0 += 8) {
-      float v[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (p0 + q < splits) v[q] = dbp[static_cast<long>(p0 + q) * nb + g];
+  for (int e = 0; e < VEC; ++e) red[sg][cv * VEC + e] = s[e];
+  __syncthreads();
+  if (sg == 0 && c < n) {
+    float o[VEC];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (p0 + q < splits) s += v[q];
+    for (int e = 0; e < VEC; ++e) o[e] = red[0][cv * VEC + e];
+    for (int g = 1; g < SG; ++g)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] += red[g][cv * VEC + e];
+    if constexpr (VEC == 4) {
+      *reinterpret_cast<float4*>(out + c) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      out[c] = o[0];
     }
-    db[g] = s;
   }
+}
+
+void launch_split_sum(const float* part, long n, int splits, float* out, const float* dbp, long nb, float* db,
+                      hipStream_t st) {
+  const long b4 = (n / 4 + 15) / 16;
+  hipLaunchKernelGGL(k_split_sum<4>, dim3(static_cast<unsigned>(b4)), dim3(256), 0, st, part, n, splits, out);
+  const long b1 = (nb + 15) / 16;
+  hipLaunchKernelGGL(k_split_sum<1>, dim3(static_cast<unsigned>(b1)), dim3(256), 0, st, dbp, nb, splits, db);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -460,34 +484,40 @@ __global__ __launch_bounds__(256) void k_gemv_wgrad(const uint16_t* x, long ldx,
 
 // ---------------------------------------------------------------------------------------
 // Logistic loss on logits z [M] with labels in {0,1}: dz[m] = (sigmoid(z_m) - y_m) / M and
-// loss = (1/M) sum_m [max(z,0) - z y + log(1 + exp(-|z|))].  One workgroup; each thread
-// sums a strided subset, then a fixed-order tree in LDS (bitwise reproducible).
+// loss = (1/M) sum_m [max(z,0) - z y + log(1 + exp(-|z|))].  Workgroup w handles samples
+// [256 w, 256 w + 256): one per thread, its loss terms summed in a fixed tree into
+// partial[w] (double); one workgroup then adds the partials in order.  Bitwise reproducible.
 // ---------------------------------------------------------------------------------------
+constexpr int kBceBlock = 256;
+
 template <class T>
-__global__ __launch_bounds__(1024) void k_bce(const uint16_t* z, long ldz, const float* labels, int M,
-                                             float* loss, uint16_t* dz, long lddz) {
+__global__ __launch_bounds__(kBceBlock) void k_bce_grad(const uint16_t* z, long ldz, const float* labels, int M,
+                                                       uint16_t* dz, long lddz, double* partial) {
+  __shared__ double red[kBceBlock];
+  const int t = threadIdx.x;
+  const int m = blockIdx.x * kBceBlock + t;
+  double s = 0.0;
+  if (m < M) {
+    const float v = T::to_f(z[static_cast<long>(m) * ldz]);
+    const float y = labels[m];
+    s = static_cast<double>(fmaxf(v, 0.f) - v * y + log1pf(expf(-fabsf(v))));
+    const float p = 1.f / (1.f + expf(-v));
+    dz[static_cast<long>(m) * lddz] = T::from_f((p - y) / static_cast<float>(M));
+  }
+  red[t] = s;
+  __syncthreads();
+  for (int o = kBceBlock / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] += red[t + o];
+    __syncthreads();
+  }
+  if (t == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(1024) void k_bce_sum(const double* partial, int nparts, int M, float* loss) {
   __shared__ double red[1024];
   const int t = threadIdx.x;
   double s = 0.0;
-  const float inv = 1.0f / static_cast<float>(M);
-  // 8 samples per thread and round: their loads are issued before any of them is used
-  for (int m0 = t; m0 < M; m0 += 8 * 1024) {
-    float v[8], y[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int m = m0 + q * 1024;
-      v[q] = m < M ? T::to_f(z[static_cast<long>(m) * ldz]) : 0.f;
-      y[q] = m < M ? labels[m] : 0.f;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int m = m0 + q * 1024;
-      if (m >= M) break;
-      s += static_cast<double>(fmaxf(v[q], 0.f) - v[q] * y[q] + log1pf(expf(-fabsf(v[q]))));
-      const float p = 1.f / (1.f + expf(-v[q]));
-      dz[static_cast<long>(m) * lddz] = T::from_f((p - y[q]) * inv);
-    }
-  }
+  for (int i = t; i < nparts; i += 1024) s += partial[i];
   red[t] = s;
   __syncthreads();
   for (int o = 512; o > 0; o >>= 1) {
@@ -631,10 +661,7 @@ el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16
     float* dbp = part + static_cast<size_t>(pl.splits) * K;
     hipLaunchKernelGGL((k_gemv_wgrad<T>), dim3(pl.splits), dim3(256), 0, st, x, ldx, M, K, dz, ldz, pl.per,
                        part, dbp);
-    const long n4 = (K + 3) / 4;
-    const long nthr = std::max<long>(n4, 1);
-    hipLaunchKernelGGL(k_split_sum, dim3((nthr + 255) / 256), dim3(256), 0, st, part, static_cast<long>(K),
-                       pl.splits, dw, dbp, 1, db);
+    launch_split_sum(part, static_cast<long>(K), pl.splits, dw, dbp, 1, db, st);
     return check_launch("el_linear_bwd");
   }
   if (dx) {  // dx = dz w: with w transposed once into the workspace, both operands are
@@ -663,10 +690,7 @@ el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16
     float* dbp = part + static_cast<size_t>(pl.splits) * N * K;
     b.out = part; b.ldo = K; b.split_stride = static_cast<long>(N) * K; b.dbp = dbp;
     hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles * pl.splits), dim3(kThreads), 0, st, b);
-    const long n = static_cast<long>(N) * K;
-    const long nthr = std::max<long>((n + 3) / 4, N);
-    hipLaunchKernelGGL(k_split_sum, dim3((nthr + 255) / 256), dim3(256), 0, st, part, n, pl.splits, dw, dbp,
-                       N, db);
+    launch_split_sum(part, static_cast<long>(N) * K, pl.splits, dw, dbp, N, db, st);
   }
   return check_launch("el_linear_bwd");
 }
@@ -769,9 +793,14 @@ EL_API el_status el_relu_bwd(const void* dy, const void* y, void* dz, int32_t M,
   return check_launch(fn);
 }
 
+EL_API size_t el_bce_workspace_bytes(int32_t M) {
+  if (M < 1) return 0;
+  return static_cast<size_t>((M + kBceBlock - 1) / kBceBlock) * sizeof(double);
+}
+
 EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, int32_t M,
-                               el_dtype dtype, float* loss, void* dz, int32_t lddz,
-                               hipStream_t stream) {
+                               el_dtype dtype, float* loss, void* dz, int32_t lddz, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "el_bce_logits";
   if (dtype != EL_BF16 && dtype != EL_F16)
     return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be EL_BF16 or EL_F16");
@@ -779,12 +808,23 @@ EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, 
   if (ldz < 1 || lddz < 1) return bad(fn, "ldz and lddz must be >= 1");
   if (!z || !labels || !loss || !dz || !al(z, 2) || !al(dz, 2) || !al(labels, 4) || !al(loss, 4))
     return bad(fn, "null or misaligned pointer");
+  const size_t need = el_bce_workspace_bytes(M);
+  if (!workspace || !al(workspace, 8) || workspace_bytes < need) {
+    char buf[160];
+    std::snprintf(buf, sizeof buf, "%s: workspace of %zu bytes (8-byte aligned), %zu needed", fn, workspace_bytes, need);
+    return set_error(EL_ERR_WORKSPACE, buf);
+  }
   const uint16_t* zs = static_cast<const uint16_t*>(z);
   uint16_t* dzs = static_cast<uint16_t*>(dz);
+  double* part = static_cast<double*>(workspace);
+  const int nb = (M + kBceBlock - 1) / kBceBlock;
   if (dtype == EL_BF16)
-    hipLaunchKernelGGL((k_bce<BF16T>), dim3(1), dim3(1024), 0, stream, zs, ldz, labels, M, loss, dzs, lddz);
+    hipLaunchKernelGGL((k_bce_grad<BF16T>), dim3(nb), dim3(kBceBlock), 0, stream, zs, static_cast<long>(ldz), labels,
+                       M, dzs, static_cast<long>(lddz), part);
   else
-    hipLaunchKernelGGL((k_bce<F16T>), dim3(1), dim3(1024), 0, stream, zs, ldz, labels, M, loss, dzs, lddz);
+    hipLaunchKernelGGL((k_bce_grad<F16T>), dim3(nb), dim3(kBceBlock), 0, stream, zs, static_cast<long>(ldz), labels,
+                       M, dzs, static_cast<long>(lddz), part);
+  hipLaunchKernelGGL(k_bce_sum, dim3(1), dim3(1024), 0, stream, part, nb, M, loss);
   return check_launch(fn);
 }
 

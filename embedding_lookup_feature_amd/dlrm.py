@@ -88,8 +88,8 @@ class DLRMStep:
         self.demb = e(B, F, D)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)
         sizes = [(B, K, N) for (N, K) in self.bottom.shapes + self.top.shapes]
-        self.lin_ws = torch.empty(max(256, max(ec.linear_bwd_workspace_bytes(*s) for s in sizes)),
-                                  dtype=torch.uint8, device=device)
+        self.lin_ws = torch.empty(max(256, max(ec.linear_bwd_workspace_bytes(*s) for s in sizes),
+                                      ec.bce_workspace_bytes(B)), dtype=torch.uint8, device=device)
 
     def _g(self, i: int, n: int) -> torch.Tensor:
         return self.gbuf[i][: self.wl.batch * n].view(self.wl.batch, n)
@@ -118,7 +118,7 @@ class DLRMStep:
         `record` (a dict), a copy of every layer's dz is kept under ("top" | "bottom", i)
         for inspection."""
         keep = (lambda key, t: record.__setitem__(key, t.clone())) if record is not None else None
-        ec.bce_logits(self.h_top[-1], labels, self.loss, self.dlogit)
+        ec.bce_logits(self.h_top[-1], labels, self.loss, self.dlogit, workspace=self.lin_ws)
         # dz of each layer; the data gradient of the layer goes to the other ping-pong buffer
         dz, cur = self.dlogit, 1
         n_top = len(self.top.w)

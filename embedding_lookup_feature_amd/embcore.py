@@ -72,7 +72,9 @@ def lib() -> ctypes.CDLL:
         L.el_linear_bwd.argtypes = [vp, i32, i32, i32, vp, i32, vp, i32, vp, i32, u32, vp, vp,
                                     ctypes.c_int, vp, sz, vp]
         L.el_relu_bwd.argtypes = [vp, vp, vp, i32, i32, i32, ctypes.c_int, vp]
-        L.el_bce_logits.argtypes = [vp, i32, vp, i32, ctypes.c_int, vp, vp, i32, vp]
+        L.el_bce_workspace_bytes.argtypes = [i32]
+        L.el_bce_workspace_bytes.restype = sz
+        L.el_bce_logits.argtypes = [vp, i32, vp, i32, ctypes.c_int, vp, vp, i32, vp, sz, vp]
         L.el_sgd_dense.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, f32, vp]
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
@@ -324,16 +326,24 @@ def relu_bwd(dy: torch.Tensor, y: torch.Tensor, dz: torch.Tensor, stream=None):
     return dz
 
 
+def bce_workspace_bytes(M: int) -> int:
+    return int(lib().el_bce_workspace_bytes(M))
+
+
 def bce_logits(z: torch.Tensor, labels: torch.Tensor, loss: torch.Tensor, dz: torch.Tensor,
-               stream=None):
-    """loss[0] = batch-mean logistic loss of logits z ([M] or [M, 1] view), dz = dloss/dz."""
+               workspace: torch.Tensor = None, stream=None):
+    """loss[0] = batch-mean logistic loss of logits z ([M] or [M, 1] view), dz = dloss/dz.
+    workspace: bytes >= bce_workspace_bytes(M) (allocated here when not given)."""
     M = labels.numel()
+    if workspace is None:
+        workspace = torch.empty(max(8, bce_workspace_bytes(M)), dtype=torch.uint8, device=z.device)
     ldz = z.stride(0) if z.dim() >= 1 else 1
     lddz = dz.stride(0) if dz.dim() >= 1 else 1
     if not (z.is_cuda and dz.is_cuda):
         raise ValueError("z and dz must be device tensors")
     _check(lib().el_bce_logits(z.data_ptr(), ldz, _dev(labels, "labels"), M, _dtype(z, "z"),
-                               _dev(loss, "loss"), dz.data_ptr(), lddz, _stream(stream)))
+                               _dev(loss, "loss"), dz.data_ptr(), lddz, _dev(workspace, "workspace"),
+                               workspace.numel(), _stream(stream)))
     return loss, dz
 
 

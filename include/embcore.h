@@ -245,17 +245,23 @@ EL_API el_status el_linear_bwd(const void* x, int32_t ldx, int32_t M, int32_t K,
 EL_API el_status el_relu_bwd(const void* dy, const void* y, void* dz, int32_t M, int32_t N,
                              int32_t ld, el_dtype dtype, hipStream_t stream);
 
+/* [host, pure] Bytes of device workspace el_bce_logits needs for M samples (per-workgroup
+ * partial sums of the loss); 0 for M < 1. */
+EL_API size_t el_bce_workspace_bytes(int32_t M);
+
 /*
  * Logistic loss of one logit per sample (the model's output read as a click likelihood;
  * the page names no loss, binary cross-entropy is the plain reading), batch mean:
  *   loss[0] = (1/M) sum_m [ max(z_m, 0) - z_m y_m + log(1 + exp(-|z_m|)) ]   (fp32)
  *   dz[m]   = (sigmoid(z_m) - y_m) / M                                       (dtype)
- * z: logits at z[m * ldz]; labels: fp32 [M] in {0, 1}; dz at dz[m * lddz].  The loss is
- * summed in a fixed order (bitwise reproducible).
+ * z: logits at z[m * ldz]; labels: fp32 [M] in {0, 1}; dz at dz[m * lddz].  The loss terms
+ * are summed in double in a fixed order (per-workgroup partials in workspace, then in
+ * workgroup order): bitwise reproducible.  workspace: >= el_bce_workspace_bytes(M),
+ * 8-byte aligned.
  */
 EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, int32_t M,
                                el_dtype dtype, float* loss, void* dz, int32_t lddz,
-                               hipStream_t stream);
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Plain SGD on dense parameters kept in fp32 (--lr, same page):

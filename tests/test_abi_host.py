@@ -32,7 +32,7 @@ def test_library_loads_and_exports_every_declared_function():
                           "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
                           "el_linear_bwd_workspace_bytes", "el_linear_bwd", "el_relu_bwd",
-                          "el_bce_logits", "el_sgd_dense"}
+                          "el_bce_workspace_bytes", "el_bce_logits", "el_sgd_dense"}
     for n in names:
         assert hasattr(L, n), n
     assert ec.el_version() == 200
@@ -162,9 +162,13 @@ def test_dense_layer_calls_reject_on_the_host():
     assert L.el_relu_bwd(A, A, A, 100, 12, 16, ec.EL_BF16, None) == UNSUPPORTED
     assert L.el_relu_bwd(A, A, A + 2, 100, 16, 16, ec.EL_BF16, None) == INVALID
     assert L.el_relu_bwd(A, A, A, 0, 16, 16, ec.EL_BF16, None) == ec.EL_OK
-    assert L.el_bce_logits(A, 1, A, 0, ec.EL_BF16, A, A, 1, None) == INVALID
-    assert L.el_bce_logits(A, 1, A, 16, ec.EL_F32, A, A, 1, None) == UNSUPPORTED
-    assert L.el_bce_logits(A, 1, 0, 16, ec.EL_BF16, A, A, 1, None) == INVALID
+    assert L.el_bce_workspace_bytes(65536) == 256 * 8
+    assert L.el_bce_workspace_bytes(0) == 0
+    assert L.el_bce_logits(A, 1, A, 0, ec.EL_BF16, A, A, 1, A, 8, None) == INVALID
+    assert L.el_bce_logits(A, 1, A, 16, ec.EL_F32, A, A, 1, A, 8, None) == UNSUPPORTED
+    assert L.el_bce_logits(A, 1, 0, 16, ec.EL_BF16, A, A, 1, A, 8, None) == INVALID
+    assert L.el_bce_logits(A, 1, A, 1000, ec.EL_BF16, A, A, 1, A, 8, None) == WORKSPACE
+    assert L.el_bce_logits(A, 1, A, 1000, ec.EL_BF16, A, A, 1, 0, 64, None) == WORKSPACE
     assert L.el_sgd_dense(A, A, ec.EL_BF16, A, -1, ctypes.c_float(0.01), None) == INVALID
     assert L.el_sgd_dense(A, A, 9, A, 10, ctypes.c_float(0.01), None) == UNSUPPORTED
     assert L.el_sgd_dense(A, A, ec.EL_BF16, A, 0, ctypes.c_float(0.01), None) == ec.EL_OK
