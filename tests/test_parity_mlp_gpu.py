@@ -291,3 +291,99 @@ def test_dlrm_train_step_repeats_bitwise():
         results.append((W.clone(), step.bottom.master.clone(), step.top.master.clone(), step.loss.clone()))
     for a, b in zip(*results):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ----------------------------------------------------------------------------------------
+# the whole step at full size, in the benchmark's launch configuration
+# ----------------------------------------------------------------------------------------
+
+def _rows_sel(t, rows):
+    return to_np(t[torch.as_tensor(rows, device=t.device)])
+
+
+def test_dlrm_step_full_size_sampled():
+    """B = 65536 on the train_step tables with the page's MLP widths, one DLRMStep.train_step
+    exactly as bench.py --workload dlrm_step runs it (sort on a side stream).  Checked on
+    sampled samples (every layer's forward row and data-gradient row, each from the GPU's own
+    upstream row), on the loss and logit gradient over the whole batch, on sampled output
+    rows of every weight gradient (full-batch sums) with all of its bias gradient, and on
+    every SGD result."""
+    wl = synth.WORKLOADS["train_step"]
+    B, F, D, dt = wl.batch, wl.num_tables, wl.dim, wl.act_dtype
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    step = dlrm.DLRMStep(wl, tab, DEV)
+    dense, labels = synth.make_dense(wl, DEV), synth.make_labels(wl, DEV)
+    ws = elf.alloc_workspace(tab, bags)
+    masters = [to_np(step.bottom.master).copy(), to_np(step.top.master).copy()]
+    bot_w = [to_np(w).copy() for w in step.bottom.w]
+    top_w = [to_np(w).copy() for w in step.top.w]
+    bot_b = [to_np(b).copy() for b in step.bottom.b]
+    top_b = [to_np(b).copy() for b in step.top.b]
+    side = torch.cuda.Stream()
+
+    # the step as the benchmark runs it, with every layer's dz kept for the checks below
+    step.forward(dense, bags)
+    rec = {}
+    step.backward(dense, labels, record=rec)
+    torch.cuda.synchronize()
+    grads = [to_np(step.bottom.grad).copy(), to_np(step.top.grad).copy()]
+    step.bottom.sgd(wl.lr)
+    step.top.sgd(wl.lr)
+    torch.cuda.synchronize()
+    for got, m0, g, what in ((step.bottom.master, masters[0], grads[0], "bottom"),
+                             (step.top.master, masters[1], grads[1], "top")):
+        _close_f32(got, orc.sgd_dense(m0, g, wl.lr)[0], what + " SGD")
+    # and the same step through train_step (sort on the side stream) gives the same bits
+    W2, _ = synth.make_tables(wl, DEV)
+    step2 = dlrm.DLRMStep(wl, elf.Tables(W2, ro), DEV)
+    ws2 = elf.alloc_workspace(step2.tables, bags)
+    step2.train_step(dense, bags, labels, ws2, side=side)
+    elf.emb_grad_reduce_update(tab, bags, step.demb, wl.lr, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(step2.top.master.view(torch.int32), step.top.master.view(torch.int32))
+    assert torch.equal(step2.bottom.master.view(torch.int32), step.bottom.master.view(torch.int32))
+    assert torch.equal(W2.view(torch.int32), W.view(torch.int32))
+    del step2, W2, ws2
+
+    rows = np.unique(np.concatenate([[0, B - 1], np.random.default_rng(3).choice(B, 61, replace=False)]))
+    # forward rows, each layer from the GPU's own input rows
+    h = dense
+    for i in range(len(bot_w)):
+        ref = orc.linear_fwd(_rows_sel(h, rows), dt, bot_w[i], dt, bot_b[i], True, dt)
+        assert_close(step.h_bot[i][torch.as_tensor(rows, device=DEV)], ref, dt, f"bottom layer {i}")
+        h = step.h_bot[i]
+    h = step.inter
+    for i in range(len(top_w)):
+        ref = orc.linear_fwd(_rows_sel(h, rows), dt, top_w[i], dt, top_b[i], i < len(top_w) - 1, dt)
+        assert_close(step.h_top[i][torch.as_tensor(rows, device=DEV)], ref, dt, f"top layer {i}")
+        h = step.h_top[i]
+    # loss and logit gradient over the whole batch
+    r_loss, r_dlogit = orc.bce_logits(to_np(step.h_top[-1]), dt, to_np(labels), dt)
+    assert abs(step.loss.item() - r_loss) <= 1e-5 * abs(r_loss)
+    assert_close(rec[("top", len(top_w) - 1)].view(-1), r_dlogit, dt, "dlogit")
+    # data-gradient rows (sampled) and weight-gradient rows (sampled, full-batch sums)
+    nsel = np.array([0, 5, 77])
+    for which, ws_, bs_, acts, mlp in (("top", top_w, top_b, step.h_top, step.top),
+                                       ("bottom", bot_w, bot_b, step.h_bot, step.bottom)):
+        for i in reversed(range(len(ws_))):
+            if which == "top":
+                x = acts[i - 1] if i > 0 else step.inter
+            else:
+                x = acts[i - 1] if i > 0 else dense
+            dz = rec[(which, i)]
+            N = ws_[i].shape[0]
+            if i > 0 or which == "top":
+                r_dx, _, _ = orc.linear_bwd(_rows_sel(x, rows), dt, ws_[i], dt, _rows_sel(dz, rows), dt,
+                                            dx_dtype=dt, relu_mask=i > 0)
+                nxt = rec[(which, i - 1)] if i > 0 else step.dout
+                assert_close(nxt[torch.as_tensor(rows, device=DEV)], r_dx, dt, f"{which} dx {i}")
+            sel = nsel[nsel < N]
+            dz_sel = np.ascontiguousarray(to_np(dz)[:, sel])
+            _, r_dw, r_db = orc.linear_bwd(to_np(x), dt, np.ascontiguousarray(ws_[i][sel]), dt, dz_sel, dt)
+            _close_f32(mlp.dw[i][torch.as_tensor(sel, device=DEV)], r_dw, f"{which} dw {i} (rows {sel})")
+            _close_f32(mlp.db[i][torch.as_tensor(sel, device=DEV)], r_db, f"{which} db {i}")
+    # the bottom MLP's last ReLU, whole batch
+    assert_bits(rec[("bottom", len(bot_w) - 1)], orc.relu_bwd(to_np(step.dx0), to_np(step.h_bot[-1]), dt),
+                "bottom relu")
