@@ -30,12 +30,20 @@
 namespace el {
 namespace {
 
-constexpr int kBR = 128;          // output rows per workgroup
-constexpr int kBC = 128;          // output cols per workgroup
 constexpr int kBK = 64;           // reduction per LDS stage
 constexpr int kPitch = kBK + 8;   // LDS row pitch in elements (144 B: 16-B reads conflict-free)
-constexpr int kTile = 128 * kPitch;  // elements of one operand tile
-constexpr int kThreads = 256;
+
+// Tile shapes: WR x WC wavefronts, each owning FR x FC tiles of 32 x 32 outputs (FR along
+// output rows, FC along output columns); BR x BC outputs per workgroup.
+template <int WR_, int WC_, int FR_, int FC_>
+struct Cfg {
+  static constexpr int WR = WR_, WC = WC_, FR = FR_, FC = FC_;
+  static constexpr int BR = WR * FR * 32, BC = WC * FC * 32;
+  static constexpr int NT = WR * WC * 64;
+  static constexpr int WPS = NT == 256 ? 2 : 1;  // workgroups per CU the kernel is built for
+};
+using CfgS = Cfg<2, 2, 2, 2>;  // 128 x 128 outputs, 256 threads, two workgroups per CU
+using CfgL = Cfg<2, 4, 4, 2>;  // 256 x 256 outputs, 512 threads, wavefront 128 x 64, one per CU
 
 enum Epi { EPI_FWD = 0, EPI_DGRAD = 1, EPI_WGRAD = 2 };
 
@@ -69,18 +77,21 @@ __device__ inline u32x4 keep_if(const u32x4& v, uint32_t mask, int i) {
   return ((mask >> i) & 1u) ? v : u32x4{0, 0, 0, 0};
 }
 
-// Global -> registers for one reduction-contiguous operand tile: 128 rows x 64 reduction;
-// all 256 threads, 4 vectors each (thread t: row t/8 + 32 i, reduction 8 (t%8) .. +8).
+// Global -> registers for one reduction-contiguous operand tile of ROWS rows x 64
+// reduction; NT threads, ROWS*8/NT vectors each (thread t: row t/8 + (NT/8) i, reduction
+// 8 (t%8) .. +8).
+template <int ROWS, int NT>
 struct TileLoaderRC {
-  u32x4 v[4];
+  static constexpr int N = ROWS * 8 / NT;
+  u32x4 v[N];
   uint32_t ok = 0;  // bit i: vector i lies inside the operand
   __device__ inline void load(const uint16_t* base, long ld, int row0, int nrows, int k0, int kend,
                               int sub) {
     const int kk = k0 + (sub & 7) * 8;
     ok = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + (sub >> 3) + 32 * i;
+    for (int i = 0; i < N; ++i) {
+      const int r = row0 + (sub >> 3) + (NT / 8) * i;
       const bool in = r < nrows && kk < kend;
       v[i] = ld16(base + static_cast<long>(r) * ld + kk, base, in);
       ok |= static_cast<uint32_t>(in) << i;
@@ -88,18 +99,17 @@ struct TileLoaderRC {
   }
   __device__ inline void store(uint16_t* lds, int sub) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + 32 * i) * kPitch + (sub & 7) * 8) = keep_if(v[i], ok, i);
+    for (int i = 0; i < N; ++i)
+      *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + (NT / 8) * i) * kPitch + (sub & 7) * 8) = keep_if(v[i], ok, i);
   }
 };
 
-// One LDS stage of the product: this wavefront's 64 x 64 block accumulates the kBK-long
-// slice held in P (rows operand) and Q (cols operand); with DB, threads 0..127 also add up
-// their row of P (the bias gradient of the weight-gradient launch).
-// Both operands output-contiguous (the weight gradient, global [red][rows]): threads 0..127
-// fetch the rows operand's 128 blocks of 8 rows x 8 reductions and threads 128..255 the
-// cols operand's, through one code path (operand chosen by per-thread selects, no branch
-// between the two sets of loads); each block is transposed in registers on its way to LDS.
+// Both operands output-contiguous (the weight gradient, global [red][rows]): threads
+// 0..BR-1 fetch the rows operand's BR blocks of 8 rows x 8 reductions and threads
+// BR..BR+BC-1 the cols operand's, through one code path (operand chosen by per-thread
+// selects, no branch between the two sets of loads); each block is transposed in
+// registers on its way to LDS.
+template <int BR>
 struct PairLoaderOC {
   u32x4 v[8];
   uint32_t ok = 0;
@@ -107,12 +117,12 @@ struct PairLoaderOC {
   long ld;
   int row0, nrows, sub;
   __device__ inline PairLoaderOC(const GemmArgs& a, int tid, int prow0, int qcol0) {
-    const bool q = tid >= 128;
+    const bool q = tid >= BR;
     base = q ? a.Q : a.P;
     ld = q ? a.ldq : a.ldp;
     row0 = q ? qcol0 : prow0;
     nrows = q ? a.C : a.R;
-    sub = tid & 127;
+    sub = q ? tid - BR : tid;
   }
   __device__ inline void load(int k0, int kend) {
     const int kb = sub & 7, rb = sub >> 3;
@@ -145,23 +155,27 @@ struct PairLoaderOC {
   }
 };
 
-template <class T, bool DB>
+// One LDS stage of the product: this wavefront's (FR*32) x (FC*32) block accumulates the
+// kBK-long slice held in P (rows operand) and Q (cols operand); with DB, threads 0..BR-1
+// also add up their row of P (the bias gradient of the weight-gradient launch).
+template <class T, class C, bool DB>
 __device__ __forceinline__ void gemm_stage(const uint16_t* P, const uint16_t* Q, int wr, int wc, int half,
-                                           int l32, f32x16 (&acc)[2][2], bool do_db, int tid, float& dbsum) {
+                                           int l32, f32x16 (&acc)[C::FC][C::FR], bool do_db, int tid,
+                                           float& dbsum) {
 #pragma unroll
   for (int ks = 0; ks < kBK / 16; ++ks) {
     const int ko = ks * 16 + half * 8;
-    u32x4 qa[2], pb[2];
+    u32x4 qa[C::FC], pb[C::FR];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      qa[i] = *reinterpret_cast<const u32x4*>(Q + (wc * 64 + i * 32 + l32) * kPitch + ko);
+    for (int i = 0; i < C::FC; ++i)
+      qa[i] = *reinterpret_cast<const u32x4*>(Q + (wc * C::FC * 32 + i * 32 + l32) * kPitch + ko);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      pb[j] = *reinterpret_cast<const u32x4*>(P + (wr * 64 + j * 32 + l32) * kPitch + ko);
+    for (int j = 0; j < C::FR; ++j)
+      pb[j] = *reinterpret_cast<const u32x4*>(P + (wr * C::FR * 32 + j * 32 + l32) * kPitch + ko);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::FC; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32<T>(qa[i], pb[j], acc[i][j]);
+      for (int j = 0; j < C::FR; ++j) acc[i][j] = mfma32<T>(qa[i], pb[j], acc[i][j]);
   }
   if (DB && do_db) {
     const uint16_t* row = P + tid * kPitch;
@@ -175,10 +189,10 @@ __device__ __forceinline__ void gemm_stage(const uint16_t* P, const uint16_t* Q,
   }
 }
 
-template <class T, bool P_RC, bool Q_RC, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sP[2][kTile];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kTile];
+template <class T, class C, bool P_RC, bool Q_RC, int EPI>
+__global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2][C::BR * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][C::BC * kPitch];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // One flat grid of tiles x splits, in split-major logical order, handed to the XCDs in
@@ -190,77 +204,103 @@ __global__ __launch_bounds__(kThreads, 2) void k_gemm(GemmArgs a) {
   const int split = lid / a.tiles;
   const int bid = lid - split * a.tiles;
   const int tr = bid / a.tiles_c, tc = bid - tr * a.tiles_c;
-  const int row0 = tr * kBR, col0 = tc * kBC;
+  const int row0 = tr * C::BR, col0 = tc * C::BC;
   const int kbeg = split * a.red_per_split;
   const int kend = min(a.red, kbeg + a.red_per_split);
   const int nk = (kend - kbeg + kBK - 1) / kBK;
 
-  const int wr = wave >> 1, wc = wave & 1;  // 64 x 64 output block of this wavefront
+  const int wr = wave / C::WC, wc = wave % C::WC;  // this wavefront's block of the tile
   const int half = lane >> 5, l32 = lane & 31;
-  f32x16 acc[2][2];
+  f32x16 acc[C::FC][C::FR];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::FC; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < C::FR; ++j) acc[i][j] = f32x16{};
 
   // bias gradient (weight-gradient launch): the first column tile sums its rows operand
-  const bool do_db = (EPI == EPI_WGRAD) && tc == 0 && tid < 128;
+  const bool do_db = (EPI == EPI_WGRAD) && tc == 0 && tid < C::BR;
   float dbsum = 0.f;
 
-  // One register set: stage kt+1's loads are issued before stage kt is multiplied out of
-  // LDS and written to the other LDS buffer after it; several workgroups per CU hide the
-  // rest of the load latency.  Loads past the last stage re-read it (never written), so
-  // every stage issues the same unconditional loads.
+  // Two register sets, stage t's tile in set t % 2, and two LDS buffers.  Stage kt writes
+  // tile kt+1 (its loads issued two stages earlier) into the LDS buffer stage kt-1 has
+  // finished with, issues the loads of tile kt+3 into the set just written out, then
+  // multiplies tile kt: every load has two stages of products to arrive.  The stage count is
+  // rounded up to even; stages past the reduction load zeros (masked, from the operand's
+  // base), so the loop body has no branch and the compiler waits for exactly the older set.
+  // Scheduling fences keep each stage's LDS writes after the previous barrier and its loads
+  // ahead of its products, so no wait for a newer set is pulled into a stage.
+  const int nk2 = (nk + 1) & ~1;
+  auto k_at = [&](int t) { return kbeg + t * kBK; };
   if constexpr (P_RC && Q_RC) {
-    TileLoaderRC lp, lq;
-    lp.load(a.P, a.ldp, row0, a.R, kbeg, kend, tid);
-    lq.load(a.Q, a.ldq, col0, a.C, kbeg, kend, tid);
-    lp.store(sP[0], tid);
-    lq.store(sQ[0], tid);
+    TileLoaderRC<C::BR, C::NT> pA, pB;
+    TileLoaderRC<C::BC, C::NT> qA, qB;
+    pA.load(a.P, a.ldp, row0, a.R, k_at(0), kend, tid);
+    qA.load(a.Q, a.ldq, col0, a.C, k_at(0), kend, tid);
+    pB.load(a.P, a.ldp, row0, a.R, k_at(1), kend, tid);
+    qB.load(a.Q, a.ldq, col0, a.C, k_at(1), kend, tid);
+    pA.store(sP[0], tid);
+    qA.store(sQ[0], tid);
+    pA.load(a.P, a.ldp, row0, a.R, k_at(2), kend, tid);
+    qA.load(a.Q, a.ldq, col0, a.C, k_at(2), kend, tid);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const int k1 = kbeg + min(kt + 1, nk - 1) * kBK;
-      lp.load(a.P, a.ldp, row0, a.R, k1, kend, tid);
-      lq.load(a.Q, a.ldq, col0, a.C, k1, kend, tid);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of this stage's products
-      gemm_stage<T, false>(sP[cur], sQ[cur], wr, wc, half, l32, acc, false, tid, dbsum);
-      if (kt + 1 < nk) {
-        lp.store(sP[cur ^ 1], tid);
-        lq.store(sQ[cur ^ 1], tid);
-      }
+    for (int kt = 0; kt < nk2; kt += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      pB.store(sP[1], tid);
+      qB.store(sQ[1], tid);
+      pB.load(a.P, a.ldp, row0, a.R, k_at(kt + 3), kend, tid);
+      qB.load(a.Q, a.ldq, col0, a.C, k_at(kt + 3), kend, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_stage<T, C, false>(sP[0], sQ[0], wr, wc, half, l32, acc, false, tid, dbsum);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      pA.store(sP[0], tid);
+      qA.store(sQ[0], tid);
+      pA.load(a.P, a.ldp, row0, a.R, k_at(kt + 4), kend, tid);
+      qA.load(a.Q, a.ldq, col0, a.C, k_at(kt + 4), kend, tid);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_stage<T, C, false>(sP[1], sQ[1], wr, wc, half, l32, acc, false, tid, dbsum);
       __syncthreads();
     }
   } else {
     static_assert(!P_RC && !Q_RC, "mixed operand layouts are not instantiated");
-    PairLoaderOC l(a, tid, row0, col0);
-    uint16_t* dst[2] = {tid >= 128 ? sQ[0] : sP[0], tid >= 128 ? sQ[1] : sP[1]};
-    l.load(kbeg, kend);
-    l.store(dst[0]);
+    static_assert(C::BR + C::BC == C::NT, "one 8 x 8 block per thread");
+    PairLoaderOC<C::BR> lA(a, tid, row0, col0), lB(a, tid, row0, col0);
+    uint16_t* dst0 = tid >= C::BR ? sQ[0] : sP[0];
+    uint16_t* dst1 = tid >= C::BR ? sQ[1] : sP[1];
+    lA.load(k_at(0), kend);
+    lB.load(k_at(1), kend);
+    lA.store(dst0);
+    lA.load(k_at(2), kend);
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const int k1 = kbeg + min(kt + 1, nk - 1) * kBK;
-      l.load(k1, kend);
-      gemm_stage<T, EPI == EPI_WGRAD>(sP[cur], sQ[cur], wr, wc, half, l32, acc, do_db, tid, dbsum);
-      if (kt + 1 < nk) l.store(dst[cur ^ 1]);
+    for (int kt = 0; kt < nk2; kt += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      lB.store(dst1);
+      lB.load(k_at(kt + 3), kend);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_stage<T, C, EPI == EPI_WGRAD>(sP[0], sQ[0], wr, wc, half, l32, acc, do_db, tid, dbsum);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      lA.store(dst0);
+      lA.load(k_at(kt + 4), kend);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_stage<T, C, EPI == EPI_WGRAD>(sP[1], sQ[1], wr, wc, half, l32, acc, do_db, tid, dbsum);
       __syncthreads();
     }
   }
 
   if (EPI == EPI_WGRAD && do_db && row0 + tid < a.R) a.dbp[static_cast<long>(split) * a.R + row0 + tid] = dbsum;
 
-  // Epilogue: register rr of acc[i][j] is output column col0 + wc*64 + i*32 + 8(rr/4) +
-  // 4 half + rr%4 of output row row0 + wr*64 + j*32 + l32.
+  // Epilogue: register rr of acc[i][j] is output column col0 + wc*FC*32 + i*32 + 8(rr/4) +
+  // 4 half + rr%4 of output row row0 + wr*FR*32 + j*32 + l32.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = row0 + wr * 64 + j * 32 + l32;
+  for (int j = 0; j < C::FR; ++j) {
+    const int r = row0 + wr * C::FR * 32 + j * 32 + l32;
     if (r >= a.R) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < C::FC; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int c = col0 + wc * 64 + i * 32 + g * 8 + half * 4;
+        const int c = col0 + wc * C::FC * 32 + i * 32 + g * 8 + half * 4;
         if (c >= a.C) continue;
         float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
         if constexpr (EPI == EPI_WGRAD) {
@@ -580,14 +620,30 @@ el_status bad(const char* fn, const std::string& what) {
 bool al(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 struct WgradPlan {
+  bool large = false;   // 256 x 256 output tiles (else 128 x 128)
   int splits = 1;
   int per = 0;        // reduction rows per split
   size_t wt_bytes = 0;  // transposed weights for the data gradient (256-byte multiple)
   size_t bytes = 0;     // total
 };
 
+// The 256 x 256 tile halves the operand bytes each output needs from L2 and LDS, but one
+// workgroup fills a CU: it is taken only when its tiles still cover the chip twice.
+bool use_large(long rows, long cols) {
+  const long tiles = ((rows + CfgL::BR - 1) / CfgL::BR) * ((cols + CfgL::BC - 1) / CfgL::BC);
+  return tiles >= 512;
+}
+
+template <class C>
+void fill_tiles(GemmArgs& a) {
+  a.tiles_c = (a.C + C::BC - 1) / C::BC;
+  a.tiles = ((a.R + C::BR - 1) / C::BR) * a.tiles_c;
+}
+
 // Splits of the weight-gradient reduction over the batch: enough workgroups to cover the
 // chip about twice (output tiles x splits >= 512), each split at least 4 LDS stages long.
+// Large tiles once the output holds at least 8 of them (one workgroup per CU, so more
+// splits; with fewer tiles the split partials outweigh what the larger tile saves).
 WgradPlan plan_wgrad(int M, int K, int N) {
   WgradPlan p;
   if (M <= 0) return p;
@@ -598,7 +654,9 @@ WgradPlan plan_wgrad(int M, int K, int N) {
     p.bytes = static_cast<size_t>(p.splits) * (K + 1) * sizeof(float);
     return p;
   }
-  const int tiles = ((N + kBR - 1) / kBR) * ((K + kBC - 1) / kBC);
+  p.large = static_cast<long>((N + CfgL::BR - 1) / CfgL::BR) * ((K + CfgL::BC - 1) / CfgL::BC) >= 8;
+  const int br = p.large ? CfgL::BR : CfgS::BR, bc = p.large ? CfgL::BC : CfgS::BC;
+  const int tiles = ((N + br - 1) / br) * ((K + bc - 1) / bc);
   int s = std::max(1, (512 + tiles - 1) / tiles);
   const int max_s = std::max(1, M / (4 * kBK));
   s = std::min(std::min(s, max_s), 256);
@@ -610,6 +668,20 @@ WgradPlan plan_wgrad(int M, int K, int N) {
   p.bytes = p.wt_bytes +
             (p.splits > 1 ? static_cast<size_t>(p.splits) * (static_cast<size_t>(N) * K + N) * sizeof(float) : 0);
   return p;
+}
+
+// One product, launched with the tile configuration C over tiles x splits workgroups.
+template <class T, class C, bool RC, int EPI>
+void launch_gemm(GemmArgs a, int splits, hipStream_t st) {
+  fill_tiles<C>(a);
+  hipLaunchKernelGGL((k_gemm<T, C, RC, RC, EPI>), dim3(a.tiles * splits), dim3(C::NT), 0, st, a);
+}
+template <class T, bool RC, int EPI>
+void launch_gemm_auto(const GemmArgs& a, int splits, bool large, hipStream_t st) {
+  if (large)
+    launch_gemm<T, CfgL, RC, EPI>(a, splits, st);
+  else
+    launch_gemm<T, CfgS, RC, EPI>(a, splits, st);
 }
 
 template <class T>
@@ -633,10 +705,8 @@ el_status run_linear_fwd(const uint16_t* x, long ldx, int M, int K, const uint16
   GemmArgs a{};
   a.P = x; a.ldp = ldx; a.Q = w; a.ldq = K;
   a.R = M; a.C = N; a.red = K; a.red_per_split = (K + kBK - 1) / kBK * kBK;
-  a.tiles_c = (N + kBC - 1) / kBC;
-  a.tiles = ((M + kBR - 1) / kBR) * a.tiles_c;
   a.out = y; a.ldo = ldy; a.bias = bias; a.relu = relu;
-  hipLaunchKernelGGL((k_gemm<T, true, true, EPI_FWD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
+  launch_gemm_auto<T, true, EPI_FWD>(a, 1, use_large(M, N), st);
   return check_launch("el_linear_fwd");
 }
 
@@ -672,24 +742,20 @@ el_status run_linear_bwd(const uint16_t* x, long ldx, int M, int K, const uint16
     GemmArgs a{};
     a.P = dz; a.ldp = ldz; a.Q = wt; a.ldq = N;
     a.R = M; a.C = K; a.red = N; a.red_per_split = (N + kBK - 1) / kBK * kBK;
-    a.tiles_c = (K + kBC - 1) / kBC;
-    a.tiles = ((M + kBR - 1) / kBR) * a.tiles_c;
     a.out = dx; a.ldo = lddx; a.relu = mask; a.mask = x; a.ldm = ldx;
-    hipLaunchKernelGGL((k_gemm<T, true, true, EPI_DGRAD>), dim3(a.tiles, 1), dim3(kThreads), 0, st, a);
+    launch_gemm_auto<T, true, EPI_DGRAD>(a, 1, use_large(M, K), st);
   }
   GemmArgs b{};
   b.P = dz; b.ldp = ldz; b.Q = x; b.ldq = ldx;
   b.R = N; b.C = K; b.red = M; b.red_per_split = pl.per;
-  b.tiles_c = (K + kBC - 1) / kBC;
-  b.tiles = ((N + kBR - 1) / kBR) * b.tiles_c;
   if (pl.splits == 1) {
     b.out = dw; b.ldo = K; b.split_stride = 0; b.dbp = db;
-    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles, 1), dim3(kThreads), 0, st, b);
+    launch_gemm_auto<T, false, EPI_WGRAD>(b, 1, pl.large, st);
   } else {
     float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.wt_bytes);
     float* dbp = part + static_cast<size_t>(pl.splits) * N * K;
     b.out = part; b.ldo = K; b.split_stride = static_cast<long>(N) * K; b.dbp = dbp;
-    hipLaunchKernelGGL((k_gemm<T, false, false, EPI_WGRAD>), dim3(b.tiles * pl.splits), dim3(kThreads), 0, st, b);
+    launch_gemm_auto<T, false, EPI_WGRAD>(b, pl.splits, pl.large, st);
     launch_split_sum(part, static_cast<long>(N) * K, pl.splits, dw, dbp, N, db, st);
   }
   return check_launch("el_linear_bwd");
