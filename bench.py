@@ -1,9 +1,10 @@
 """Throughput of the embedding-bag + dot-interaction training step on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input already resident in HBM:
-  emb_dot_fwd (the gather + the interaction forward) -> dot_interact_bwd ->
-  emb_grad_apply, with emb_grad_prepare (the sort of the lookups, which needs only the
-  indices) on a side stream from the end of the forward, overlapping the backward
+  emb_dot_fwd (the gather + the interaction forward, pooled vectors stored) ->
+  dot_interact_bwd -> emb_grad_apply, with emb_grad_prepare (the sort of the lookups, which
+  needs only the indices) on a side stream from the end of the forward, overlapping the
+  backward
 on the train_step workload (B = 65536, 26 fp32 tables x 100,000 x 128, bf16 activations,
 Zipf(1.05) hotness-1 indices, SGD lr 0.01).  Eight distinct index batches rotate across
 steps so that no step replays the previous one's rows from cache.
@@ -40,7 +41,15 @@ KERNEL_SOURCES = {
                       "embedding_lookup_feature_amd/csrc/emb_dot_fwd.hip"],
 }
 KERNEL_OF_CALL = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
-                  "dot_interact_bwd": "k_dot_bwd_mfma", "emb_dot_fwd": "k_emb_dot_fwd"}
+                  "dot_interact_bwd": "k_dot_bwd_mfma", "emb_dot_fwd": "k_emb_dot_fwd",
+                  "emb_dot_bwd": "k_dot_bwd_mfma"}
+
+
+def fused_bwd_ok(wl):
+    """The shapes emb_dot_bwd's fused kernel covers (include/embcore.h)."""
+    V, D = wl.num_tables + 1, wl.dim
+    return (wl.act_dtype in ("bf16", "f16") and D % 16 == 0 and D >= 32 and V <= 32
+            and (V + 31) // 32 * 16 * (D // 8) <= 256 and wl.out_stride % 8 == 0)
 
 
 def metric_name(wl):
@@ -48,9 +57,12 @@ def metric_name(wl):
     return f"samples/s {what} (emb-bag + dot interaction) at batch {wl.batch}; achieved HBM GB/s"
 
 
-def algorithmic_bytes(wl, nnz):
+def algorithmic_bytes(wl, nnz, store_emb=None):
     """Bytes each call must move at minimum (every lookup's row counted; caches may serve
-    part of them), per launch."""
+    part of them), per launch.  store_emb: the training forward stores the pooled vectors
+    (default: whenever the workload has a backward)."""
+    if store_emb is None:
+        store_emb = wl.backward
     B, F, D = wl.batch, wl.num_tables, wl.dim
     st = 4 if wl.table_dtype == "f32" else 2
     sa = 4 if wl.act_dtype == "f32" else 2
@@ -64,9 +76,12 @@ def algorithmic_bytes(wl, nnz):
         # rows + indices + offsets + x0 in, interaction rows out (+ pooled vectors out when
         # the backward needs them); the pooled vectors are not read back from HBM
         "emb_dot_fwd": nnz * D * st + 4 * nnz + 4 * (F * B + 1) + B * D * sa + B * S * sa
-                       + (B * F * D * sa if wl.backward else 0),
+                       + (B * F * D * sa if store_emb else 0),
         # dout in, x0 + emb in, dx0 + demb out
         "dot_interact_bwd": B * S * sa + 2 * B * V * D * sa,
+        # dout + x0 + rows + indices + offsets in, dx0 + demb out
+        "emb_dot_bwd": B * S * sa + B * D * sa + nnz * D * st + 4 * nnz + 4 * (F * B + 1)
+                       + B * V * D * sa,
         # keys + bag ids read once, gradients gathered once, touched rows read + written (the
         # sort's own passes are not counted)
         "emb_grad_reduce_update": None,  # filled in by the caller (needs the unique-row count)
@@ -142,6 +157,10 @@ def main():
     ap.add_argument("--overlap-sort", choices=["none", "fwd", "bwd"], default="bwd",
                     help="run the gradient sort (emb_grad_prepare) on a side stream, from the start of "
                          "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply")
+    ap.add_argument("--recompute-emb", action="store_true",
+                    help="training: do not store the pooled vectors in the forward (emb_dot_fwd "
+                         "without emb_out); rebuild them from the tables in the backward "
+                         "(emb_dot_bwd) instead of reading them back in dot_interact_bwd")
     ap.add_argument("--inference-sweep", action="store_true",
                     help="forward-only latency / throughput over batch sizes 1 .. 1,048,576 on the "
                          "large fp16 tables (emb_dot_fwd, pooled vectors not stored); one JSON line "
@@ -186,13 +205,19 @@ def main():
 
     overlap = wl.backward and args.overlap_sort != "none"
     fused_fwd = not args.separate_fwd
+    # training: store the pooled vectors and read them back (the faster order here), or
+    # with --recompute-emb rebuild them in the backward where the fused backward covers
+    # the shape
+    recompute = wl.backward and fused_fwd and args.recompute_emb and fused_bwd_ok(wl)
+    store_emb = wl.backward and not recompute
+    bwd_name = "emb_dot_bwd" if recompute else "dot_interact_bwd"
     fwd_names = ["emb_dot_fwd"] if fused_fwd else ["emb_bag_fwd", "dot_interact_fwd"]
     if not wl.backward:
         names = fwd_names
     elif overlap:
-        names = fwd_names + ["dot_interact_bwd", "emb_grad_apply"]
+        names = fwd_names + [bwd_name, "emb_grad_apply"]
     else:
-        names = fwd_names + ["dot_interact_bwd", "emb_grad_reduce_update"]
+        names = fwd_names + [bwd_name, "emb_grad_reduce_update"]
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else None  # default priority
     applied = torch.cuda.Event()
@@ -216,8 +241,8 @@ def main():
             start_sort(bags, side_ev)
         if ev: ev[0].record()
         k = 1
-        if fused_fwd:  # forward only: the pooled vectors are not needed afterwards
-            elf.emb_dot_fwd(tab, bags, x0, out, emb if wl.backward else None)
+        if fused_fwd:  # pooled vectors stored only when the backward reads them back
+            elf.emb_dot_fwd(tab, bags, x0, out, emb if store_emb else None)
         else:
             elf.emb_bag_fwd(tab, bags, emb)
             if ev: ev[k].record()
@@ -231,7 +256,10 @@ def main():
             fwd_done.record(main_stream)
             side.wait_event(fwd_done)
             start_sort(bags, side_ev)
-        elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+        if recompute:
+            elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb)
+        else:
+            elf.dot_interact_bwd(x0, emb, G, dx0, demb)
         if ev: ev[k].record()
         k += 1
         if overlap:
@@ -284,7 +312,7 @@ def main():
     copy_gbps = None if args.no_copy_bw else copy_bandwidth(dev)
 
     nnz = batches[0][3].numel()
-    algo = algorithmic_bytes(wl, nnz)
+    algo = algorithmic_bytes(wl, nnz, store_emb)
     idx0, off0 = batches[0][3], batches[0][4]
     # unique rows touched (for the update's row read + write), from the input indices
     keys = idx0.long() + torch.repeat_interleave(ro[:-1], (off0[1:].long() - off0[:-1].long()).view(F, B).sum(1))
@@ -314,7 +342,7 @@ def main():
     # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
     # short sort / reduce kernels, each well below the interaction kernels; in training
     # emb_dot_fwd is a sequence of gather and interaction launches)
-    single = [n for n in names if n in KERNEL_OF_CALL and not (n == "emb_dot_fwd" and wl.backward)]
+    single = [n for n in names if n in KERNEL_OF_CALL and not (n == "emb_dot_fwd" and store_emb)]
     dom = max(single, key=lambda n: call_ms[n])
     kernel = KERNEL_OF_CALL[dom]
     achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
@@ -342,7 +370,8 @@ def main():
                    "tables": F, "rows_per_table": wl.rows[0] if len(set(wl.rows)) == 1 else "varied",
                    "total_rows": wl.total_rows, "dim": D,
                    "table_dtype": wl.table_dtype, "act_dtype": wl.act_dtype, "nnz": int(nnz),
-                   "unique_rows": U, "parallelism": "single-gpu"},
+                   "unique_rows": U, "parallelism": "single-gpu",
+                   "calls": " -> ".join(names) + (" (emb_grad_prepare on a side stream)" if overlap else "")},
         "hbm_gbps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "calls": calls,
         "roofline": roofline,

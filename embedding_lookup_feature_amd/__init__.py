@@ -15,6 +15,7 @@ from .embcore import (  # noqa: F401
     el_validate_bags,
     el_version,
     emb_bag_fwd,
+    emb_dot_bwd,
     emb_dot_fwd,
     emb_grad_apply,
     emb_grad_prepare,

@@ -174,6 +174,24 @@ el_status emb_dot_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
   return launch_emb_dot_fwd(*tab, *bags, flags, x0, act_dtype, emb_out, out, out_stride, stream);
 }
 
+el_status emb_dot_bwd(const el_tables* tab, const el_bags* bags, uint32_t flags, const void* x0,
+                      el_dtype act_dtype, const void* dout, int32_t out_stride, void* dx0,
+                      void* demb, el_dtype grad_dtype, hipStream_t stream) {
+  const char* fn = "emb_dot_bwd";
+  EL_TRY(check_tables(tab, fn));
+  EL_TRY(check_bags(tab, bags, fn));
+  if (flags & ~static_cast<uint32_t>(EL_FLAG_HASH_INDICES)) return bad(fn, "unknown flags");
+  const int32_t B = bags->batch;
+  EL_TRY(check_interaction(fn, B, tab->num_tables, tab->dim, out_stride, act_dtype, act_dtype, grad_dtype));
+  EL_TRY(check_dense(fn, x0, B > 0, "x0"));
+  EL_TRY(check_dense(fn, dout, B > 0, "dout"));
+  EL_TRY(check_dense(fn, dx0, B > 0, "dx0"));
+  EL_TRY(check_dense(fn, demb, B > 0, "demb"));
+  if (B == 0) return EL_OK;
+  return launch_emb_dot_bwd(*tab, *bags, flags, x0, act_dtype, dout, out_stride, dx0, demb,
+                            grad_dtype, stream);
+}
+
 size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags) {
   if (check_tables(tab, "emb_grad_workspace_bytes") != EL_OK) return 0;
   if (check_bags(tab, bags, "emb_grad_workspace_bytes") != EL_OK) return 0;

@@ -193,13 +193,32 @@ using Buf = std::integral_constant<int, N>;
 
 // An empty register use: the compiler waits here for the load that produced `v`.
 __device__ inline void settle(const u32x4& v) { asm volatile("" ::"v"(v)); }
+__device__ inline void settle_i(int v) { asm volatile("" ::"v"(v)); }
 
-template <class IT, class GT, int UPT, int GPT, int KSM, int PD>
-__global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
+// GATHER: the pooled vectors are rebuilt from the tables (TT: table type) instead of read
+// from emb, exactly as emb_bag_fwd forms them: the bag's rows summed in fp32 in CSR order
+// (starting from the first row; an empty bag is +0), one rounding to IT.  Each thread
+// resolves its own two rows through a three-stage pipeline over the grid stride: the table
+// rows of the sample 2 strides ahead, its first index 4 strides ahead, its CSR bounds 6
+// strides ahead, each stage consuming what the previous stage loaded two trips earlier (the
+// register sets alternate with the trips), so every load has two trips to arrive.  The
+// further rows of a bag longer than one are loaded where the tile is written
+// to LDS (synchronously: correct for any bag, fast for one-lookup bags).
+struct GatherSrc {
+  const void* W;            // joint table [total_rows][D] of TT
+  const int64_t* row_off;   // [F+1]
+  const int32_t* idx;       // [nnz]
+  const int32_t* off;       // [F*B+1]
+  int32_t nnz;
+  uint32_t hash;            // floor-mod the indices by the table's row count
+};
+
+template <class IT, class GT, int UPT, int GPT, int KSM, int PD, class TT, bool GATHER>
+__global__ __launch_bounds__(256, GATHER ? 2 : 1) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
                                                       const uint16_t* __restrict__ emb, int B, int F,
                                                       int D, const uint16_t* __restrict__ dout,
                                                       int out_stride, typename GT::S* __restrict__ dx0,
-                                                      typename GT::S* __restrict__ demb) {
+                                                      typename GT::S* __restrict__ demb, GatherSrc gs) {
   extern __shared__ uint4 smem[];
   char* lds = reinterpret_cast<char*>(smem);
   using GS = typename GT::S;
@@ -226,9 +245,65 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
 
   static_assert(PD == 1 || (PD == 2 && GPT > 0),
                 "several samples in flight need the gradient row in registers");
-  u32x4 t[PD][UPT][2];
+  static_assert(!GATHER || PD == 2, "the gather pipeline is built for two samples in flight");
+  using TS = typename TT::S;
+  // 16-byte vectors per 8-element row chunk: a table chunk of TT when gathering
+  constexpr int NVT = GATHER ? static_cast<int>(sizeof(TS)) / 2 : 1;
+  u32x4 t[PD][UPT][2][NVT];
   u32x4 g[PD][GPT > 0 ? GPT : 1];
-  // Loads of sample bb into register buffer BF.
+
+  // Gather state of this thread's rows (uu, m): table row base and count, and per pipeline
+  // parity: CSR bounds, first index with its bag's length, and the length of the bag whose
+  // first rows sit in register buffer `parity`.
+  constexpr int GU = GATHER ? UPT : 1;
+  uint32_t tb[GU][2] = {}, tr[GU][2] = {};
+  int bnd_s[2][GU][2] = {}, bnd_e[2][GU][2] = {}, gix[2][GU][2] = {};
+  int ibag_n[2][GU][2] = {}, bag_n[2][GU][2] = {};
+  // table of row (uu, m), or -1 for x0 / padding rows
+  auto row_table = [&](int uu, int m) {
+    int u = uu * 256 + tid;
+    u = u < units ? u : units - 1;
+    const int rp = u - (u / npairs) * npairs;
+    const int v = rp * 2 + m;
+    return v >= 1 && v < V ? v - 1 : -1;
+  };
+  const int lastb = B - 1;
+  // stage A: CSR bounds of sample j's bags (padding rows read bag 0's)
+  auto g_bounds = [&](int j, auto par) {
+    constexpr int Q = decltype(par)::value;
+    const int jc = j < lastb ? j : lastb;
+#pragma unroll
+    for (int uu = 0; uu < GU; ++uu)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int tt = row_table(uu, m);
+        const int gbag = (tt < 0 ? 0 : tt) * B + jc;
+        bnd_s[Q][uu][m] = ld_stream(gs.off + gbag);
+        bnd_e[Q][uu][m] = ld_stream(gs.off + gbag + 1);
+      }
+  };
+  // stage B: first index of the bags whose bounds are in parity Q's registers (the bag's
+  // length moves along with it)
+  auto g_first = [&](auto par) {
+    constexpr int Q = decltype(par)::value;
+#pragma unroll
+    for (int uu = 0; uu < GU; ++uu)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        int p = bnd_s[Q][uu][m];
+        ibag_n[Q][uu][m] = bnd_e[Q][uu][m] - p;
+        p = p < 0 ? 0 : (p < gs.nnz ? p : gs.nnz - 1);
+        gix[Q][uu][m] = ld_stream(gs.idx + p);
+      }
+  };
+  // joint-table row of a bag's first index (row 0 for an empty bag: read, never used)
+  auto g_row = [&](int uu, int m, int r, int n) -> uint32_t {
+    if (gs.hash) r = floor_mod(r, static_cast<int32_t>(tr[uu][m]));
+    return n > 0 ? tb[uu][m] + static_cast<uint32_t>(r) : 0u;
+  };
+
+  // Loads of sample bb into register buffer BF (GATHER: the first rows of the bags whose
+  // indices are in parity BF's registers, which are sample bb's).
   auto fetch = [&](int bb, auto bf) {
     constexpr int BF = decltype(bf)::value;
     const int64_t xb = static_cast<int64_t>(bb) * D;
@@ -242,8 +317,21 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
       for (int m = 0; m < 2; ++m) {
         const int v = rp * 2 + m;
         const int vc = v < V ? v : 0;
-        const uint16_t* src = (vc == 0 ? x0 + xb : emb + eb + static_cast<int64_t>(vc) * D) + c * 8;
-        t[BF][uu][m] = *reinterpret_cast<const u32x4*>(src);  // rows >= V are masked in put()
+        if constexpr (GATHER) {
+          // vector 0: x0's chunk for row 0 (and padding rows), else the table chunk
+          const bool trow = vc != 0;
+          bag_n[BF][uu][m] = ibag_n[BF][uu][m];
+          const uint32_t rid = g_row(uu, m, gix[BF][uu][m], bag_n[BF][uu][m]);
+          const char* tsrc = reinterpret_cast<const char*>(static_cast<const TS*>(gs.W) +
+                                                           static_cast<int64_t>(rid) * D + c * 8);
+          const char* xsrc = reinterpret_cast<const char*>(x0 + xb + c * 8);
+#pragma unroll
+          for (int q = 0; q < NVT; ++q)
+            t[BF][uu][m][q] = *reinterpret_cast<const u32x4*>(trow ? tsrc + 16 * q : xsrc);
+        } else {
+          const uint16_t* src = (vc == 0 ? x0 + xb : emb + eb + static_cast<int64_t>(vc) * D) + c * 8;
+          t[BF][uu][m][0] = *reinterpret_cast<const u32x4*>(src);  // rows >= V are masked in put()
+        }
       }
     }
     if constexpr (GPT > 0) {
@@ -259,15 +347,50 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
   auto settle_buf = [&](auto bf) {
     constexpr int BF = decltype(bf)::value;
 #pragma unroll
-    for (int uu = 0; uu < UPT; ++uu) {
-      settle(t[BF][uu][0]);
-      settle(t[BF][uu][1]);
-    }
+    for (int uu = 0; uu < UPT; ++uu)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int q = 0; q < NVT; ++q) settle(t[BF][uu][m][q]);
     if constexpr (GPT > 0) {
 #pragma unroll
       for (int gg = 0; gg < GPT; ++gg) settle(g[BF][gg]);
     }
   };
+  // GATHER: the pooled 8-element chunk of row (uu, m) as IT: the bag's first row (loaded
+  // into buffer BF by the pipeline), plus its further rows in CSR order (loaded here), in
+  // fp32 -- the association emb_bag_fwd uses; an empty bag pools to +0.
+  auto pooled = [&](int uu, int m, int c, int bb, auto bf) -> u32x4 {
+    constexpr int BF = decltype(bf)::value;
+    float acc[8];
+    const int n = bag_n[BF][uu][m];
+#pragma unroll
+    for (int q = 0; q < NVT; ++q) {
+      const u32x4 w = n > 0 ? t[BF][uu][m][q] : u32x4{0, 0, 0, 0};
+      unpack16<TT>(uint4{w[0], w[1], w[2], w[3]}, acc + q * epv<TT>());
+    }
+    if (n > 1) {
+      const int s0 = gs.off[row_table(uu, m) * B + min(bb, B - 1)];
+      for (int k = s0 + 1; k < s0 + n; ++k) {
+        const uint32_t rid = g_row(uu, m, gs.idx[k], 1);
+        const TS* src = static_cast<const TS*>(gs.W) + static_cast<int64_t>(rid) * D + c * 8;
+#pragma unroll
+        for (int q = 0; q < NVT; ++q) {
+          const uint4 w = reinterpret_cast<const uint4*>(src)[q];
+          float f[8];
+          unpack16<TT>(w, f);
+#pragma unroll
+          for (int x = 0; x < epv<TT>(); ++x) acc[q * epv<TT>() + x] += f[x];
+        }
+      }
+    }
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = static_cast<uint32_t>(IT::from_f(acc[2 * i])) | (static_cast<uint32_t>(IT::from_f(acc[2 * i + 1])) << 16);
+    return r;
+  };
+
   // Register buffer BF (sample bb) -> LDS.
   auto put = [&](int bb, auto bf) {
     constexpr int BF = decltype(bf)::value;
@@ -275,8 +398,14 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
     for (int uu = 0; uu < UPT; ++uu) {
       const int u = uu * 256 + tid;
       const int c = u / npairs, rp = u - c * npairs;
-      const u32x4 r0 = rp * 2 < V ? t[BF][uu][0] : u32x4{0, 0, 0, 0};
-      const u32x4 r1 = rp * 2 + 1 < V ? t[BF][uu][1] : u32x4{0, 0, 0, 0};
+      u32x4 r0 = rp * 2 < V ? t[BF][uu][0][0] : u32x4{0, 0, 0, 0};
+      u32x4 r1 = rp * 2 + 1 < V ? t[BF][uu][1][0] : u32x4{0, 0, 0, 0};
+      if constexpr (GATHER) {
+        if (u < units) {
+          if (rp * 2 >= 1 && rp * 2 < V) r0 = pooled(uu, 0, c, bb, bf);
+          if (rp * 2 + 1 < V) r1 = pooled(uu, 1, c, bb, bf);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // value e of both rows, row 2rp in the low half: V^T[c*8 + e][2rp .. 2rp+1]
@@ -306,7 +435,13 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
   const int NG = gridDim.x;
   auto sample = [&](int b, auto bf) {
     put(b, bf);
-    fetch(min(b + PD * NG, B - 1), bf);
+    // GATHER: every stage consumes what the same stage of the trip before last (same
+    // parity) loaded, so each load has two trips to arrive
+    fetch(min(b + PD * NG, B - 1), bf);               // rows (GATHER: stage C), sample b + 2 NG
+    if constexpr (GATHER) {
+      g_first(bf);                                    // stage B: sample b + 4 NG
+      g_bounds(b + 6 * NG, bf);                       // stage A: sample b + 6 NG
+    }
     __syncthreads();
     int cur_vt = -1;
     u32x4 Sop[KSM];  // S[v][k], k = 16 ks + 8 half + e
@@ -378,8 +513,43 @@ __global__ __launch_bounds__(256) void k_dot_bwd_mfma(const uint16_t* __restrict
   if (b >= B) return;
   // Prologue loads land before the loop (settle), so that the wait counts the compiler
   // derives for the loop are those of its steady state alone.
-  fetch(b, Buf<0>{});
-  if constexpr (PD == 2) fetch(min(b + NG, B - 1), Buf<1>{});
+  if constexpr (GATHER) {
+    // Fill the pipeline synchronously: buffers 0 and 1 with samples b and b + NG, parity 0's
+    // and 1's indices with b + 2 NG and b + 3 NG, their bounds with b + 4 NG and b + 5 NG --
+    // the state a trip of the loop leaves for the next.
+#pragma unroll
+    for (int uu = 0; uu < GU; ++uu)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int tt = row_table(uu, m);
+        const int tc = tt < 0 ? 0 : tt;
+        tb[uu][m] = static_cast<uint32_t>(gs.row_off[tc]);
+        tr[uu][m] = static_cast<uint32_t>(gs.row_off[tc + 1] - gs.row_off[tc]);
+      }
+    g_bounds(b, Buf<0>{});
+    g_first(Buf<0>{});
+    fetch(b, Buf<0>{});
+    g_bounds(b + NG, Buf<1>{});
+    g_first(Buf<1>{});
+    fetch(min(b + NG, B - 1), Buf<1>{});
+    g_bounds(b + 2 * NG, Buf<0>{});
+    g_first(Buf<0>{});
+    g_bounds(b + 3 * NG, Buf<1>{});
+    g_first(Buf<1>{});
+    g_bounds(b + 4 * NG, Buf<0>{});
+    g_bounds(b + 5 * NG, Buf<1>{});
+#pragma unroll
+    for (int uu = 0; uu < GU; ++uu)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        settle_i(bnd_s[0][uu][m]); settle_i(bnd_e[0][uu][m]);
+        settle_i(bnd_s[1][uu][m]); settle_i(bnd_e[1][uu][m]);
+        settle_i(gix[0][uu][m]); settle_i(gix[1][uu][m]);
+      }
+  } else {
+    fetch(b, Buf<0>{});
+    if constexpr (PD == 2) fetch(min(b + NG, B - 1), Buf<1>{});
+  }
   settle_buf(Buf<0>{});
   if constexpr (PD == 2) settle_buf(Buf<1>{});
   for (;;) {
@@ -551,12 +721,48 @@ el_status fwd_typed(const void* x0, const void* emb, int B, int F, int D, void* 
 template <class IT, class GT, int UPT, int GPT, int KSM, int PD>
 el_status launch_bwd_t(const void* x0, const void* emb, int B, int F, int D, const void* dout,
                        int out_stride, void* dx0, void* demb, size_t lds, hipStream_t stream) {
-  auto kern = k_dot_bwd_mfma<IT, GT, UPT, GPT, KSM, PD>;
+  auto kern = k_dot_bwd_mfma<IT, GT, UPT, GPT, KSM, PD, IT, false>;
   hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 256)),
                      dim3(256), lds, stream, static_cast<const uint16_t*>(x0),
                      static_cast<const uint16_t*>(emb), B, F, D, static_cast<const uint16_t*>(dout),
-                     out_stride, static_cast<typename GT::S*>(dx0), static_cast<typename GT::S*>(demb));
+                     out_stride, static_cast<typename GT::S*>(dx0), static_cast<typename GT::S*>(demb),
+                     GatherSrc{});
   return check_launch("dot_interact_bwd");
+}
+
+// LDS bytes of the MFMA backward: V^T [D][VP] (pitch 2 VP + 16) | gradient row | VP x D
+// output block | dV_0 in fp32 | scratch slot.
+size_t bwd_lds_bytes(int F, int D, size_t gsz) {
+  const int V = F + 1;
+  const int64_t P = static_cast<int64_t>(V) * (V - 1) / 2;
+  const int64_t gchunks = (D + P + 7) / 8;
+  const size_t VP = static_cast<size_t>((V + 31) / 32 * 32);
+  return static_cast<size_t>(D) * (VP * 2 + 16) + gchunks * 16 + VP * (D * gsz + 16) +
+         static_cast<size_t>(D) * 4 + 16;
+}
+
+template <class TT, class IT, class GT>
+el_status launch_emb_dot_bwd_t(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                               const void* x0, const void* dout, int out_stride, void* dx0,
+                               void* demb, hipStream_t stream) {
+  const int B = bags.batch, F = tab.num_tables, D = tab.dim;
+  const int V = F + 1;
+  const int64_t P = static_cast<int64_t>(V) * (V - 1) / 2;
+  const size_t lds = bwd_lds_bytes(F, D, sizeof(typename GT::S));
+  const int units = (V + 31) / 32 * 16 * (D / 8);
+  if (!(D % 16 == 0 && D >= 32 && V <= 32 && units <= 256 && (D + P + 7) / 8 <= 256 &&
+        out_stride % 8 == 0 && lds <= kMaxLds && bags.nnz > 0 && tab.total_rows > 0))
+    return set_error(EL_ERR_UNSUPPORTED,
+                     "emb_dot_bwd: the fused kernel covers 16-bit activations, D % 16 == 0, D >= 32, "
+                     "F <= 31, (F+1)/2 * D/8 <= 256, out_stride % 8 == 0 and nnz > 0");
+  auto kern = k_dot_bwd_mfma<IT, GT, 1, 1, 2, 2, TT, true>;
+  GatherSrc gs{tab.base, tab.row_offset, bags.indices, bags.offsets, static_cast<int32_t>(bags.nnz),
+               (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u};
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 256)),
+                     dim3(256), lds, stream, static_cast<const uint16_t*>(x0), nullptr, B, F, D,
+                     static_cast<const uint16_t*>(dout), out_stride,
+                     static_cast<typename GT::S*>(dx0), static_cast<typename GT::S*>(demb), gs);
+  return check_launch("emb_dot_bwd");
 }
 
 // Shape classes of the MFMA backward: K steps (vectors per sample), row pairs per thread,
@@ -589,10 +795,7 @@ el_status bwd_typed(const void* x0, const void* emb, int B, int F, int D, const 
   const int V = F + 1;
   const int64_t P = static_cast<int64_t>(V) * (V - 1) / 2;
   if constexpr (sizeof(typename IT::S) == 2 && IT::code == DT::code) {
-    const int64_t gchunks = (D + P + 7) / 8;
-    const size_t VP = static_cast<size_t>((V + 31) / 32 * 32);
-    const size_t lds = static_cast<size_t>(D) * (VP * 2 + 16) + gchunks * 16 +
-                       VP * (D * sizeof(typename GT::S) + 16) + static_cast<size_t>(D) * 4 + 16;
+    const size_t lds = bwd_lds_bytes(F, D, sizeof(typename GT::S));
     // 16-byte chunks of the gradient row must stay inside the row: stride multiple of 8
     // D = 16: the fp32 FMA kernel (one wavefront per sample) is faster than a half-empty
     // 32-row MFMA tile driven by four wavefronts
@@ -629,6 +832,25 @@ el_status launch_dot_fwd(const void* x0, const void* emb, el_dtype in_dtype, int
   return with_type(in_dtype, [&](auto it) {
     return with_type(out_dtype, [&](auto ot) {
       return fwd_typed<decltype(it), decltype(ot)>(x0, emb, B, F, D, out, out_stride, stream);
+    });
+  });
+}
+
+el_status launch_emb_dot_bwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, const void* dout, int out_stride,
+                             void* dx0, void* demb, el_dtype grad_dtype, hipStream_t stream) {
+  if (act_dtype == EL_F32)
+    return set_error(EL_ERR_UNSUPPORTED, "emb_dot_bwd: the fused kernel takes 16-bit activations");
+  return with_type(tab.dtype, [&](auto tt) {
+    return with_type(act_dtype, [&](auto it) {
+      return with_type(grad_dtype, [&](auto gt) {
+        using IT = decltype(it);
+        if constexpr (sizeof(typename IT::S) == 2)
+          return launch_emb_dot_bwd_t<decltype(tt), IT, decltype(gt)>(tab, bags, flags, x0, dout,
+                                                                      out_stride, dx0, demb, stream);
+        else
+          return EL_ERR_UNSUPPORTED;
+      });
     });
   });
 }

@@ -128,6 +128,12 @@ el_status launch_dot_bwd(const void* x0, const void* emb, el_dtype in_dtype, int
                          const void* dout, el_dtype dout_dtype, int out_stride, void* dx0,
                          void* demb, el_dtype grad_dtype, hipStream_t stream);
 
+// The interaction backward with the pooled vectors rebuilt from the tables (fused gather);
+// dout has the activation type.
+el_status launch_emb_dot_bwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, const void* dout, int out_stride,
+                             void* dx0, void* demb, el_dtype grad_dtype, hipStream_t stream);
+
 // Workspace of the gradient path; all pointers 256-byte aligned inside one allocation.
 struct GradWorkspace {
   int64_t n = 0;        // lookups

@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.emb_bag_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp]
         L.dot_interact_fwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32, vp]
         L.emb_dot_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp, vp, i32, vp]
+        L.emb_dot_bwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp, i32, vp, vp, ctypes.c_int, vp]
         L.dot_interact_bwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32,
                                        vp, vp, ctypes.c_int, vp]
         L.emb_grad_workspace_bytes.argtypes = [T, Bg]
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.el_sgd_dense.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, f32, vp]
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
-        for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
+        for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
                      "emb_grad_reduce_update", "emb_grad_prepare", "emb_grad_apply",
                      "emb_grad_sort", "el_validate_bags", "el_linear_fwd", "el_linear_bwd",
                      "el_relu_bwd", "el_bce_logits", "el_sgd_dense"):
@@ -200,6 +201,19 @@ def dot_interact_bwd(x0, emb, dout, dx0, demb, stream=None):
                                   _dev(dout, "dout"), _dtype(dout, "dout"), dout.shape[1],
                                   _dev(dx0, "dx0"), _dev(demb, "demb"), _dtype(demb, "demb"),
                                   _stream(stream)))
+    return dx0, demb
+
+
+def emb_dot_bwd(tables: Tables, bags: Bags, x0: torch.Tensor, dout: torch.Tensor,
+                dx0: torch.Tensor, demb: torch.Tensor, hash_indices=False, stream=None):
+    """emb_bag_fwd followed by dot_interact_bwd in one call (bit-identical results), the pooled
+    vectors rebuilt from the tables and never stored."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    if dout.dtype != x0.dtype:
+        raise ValueError("dout must have the activation dtype of x0")
+    _check(lib().emb_dot_bwd(ctypes.byref(tables.c), ctypes.byref(bags.c), flags, _dev(x0, "x0"),
+                             _dtype(x0, "x0"), _dev(dout, "dout"), dout.shape[1], _dev(dx0, "dx0"),
+                             _dev(demb, "demb"), _dtype(demb, "demb"), _stream(stream)))
     return dx0, demb
 
 

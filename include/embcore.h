@@ -130,6 +130,27 @@ EL_API el_status dot_interact_bwd(const void* x0, const void* emb, el_dtype in_d
                            int32_t out_stride, void* dx0, void* demb, el_dtype grad_dtype,
                            hipStream_t stream);
 
+/*
+ * The interaction backward with the pooled vectors rebuilt from the tables (same page,
+ * §Model architecture: the pooled embeddings are an input of the interaction, so its
+ * backward needs them; recomputing them from the tables replaces storing them in the
+ * forward and reading them back).  Same results, bit for bit, as
+ *   emb_bag_fwd(tab, bags, flags, emb, act_dtype);
+ *   dot_interact_bwd(x0, emb, act_dtype, B, F, D, dout, act_dtype, out_stride, dx0, demb,
+ *                    grad_dtype);
+ * with B = bags->batch, F = tab->num_tables, D = tab->dim; the pooled vectors are never
+ * stored.  The tables must not change between the forward and this call.  x0: [B][D] and
+ * dout: [B][out_stride] of act_dtype (bf16 or fp16); dx0: [B][D], demb: [B][F][D] of
+ * grad_dtype; all 16-byte aligned.  One fused kernel; it covers D % 16 == 0, D >= 32,
+ * F <= 31, (F+1)/2 * D/8 <= 256 (one row pair and column block per thread) and
+ * out_stride % 8 == 0 (other shapes, fp32 activations: EL_ERR_UNSUPPORTED, nothing
+ * enqueued).  Bags of any length are correct; one-lookup bags take the pipelined path.
+ */
+EL_API el_status emb_dot_bwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, const void* dout,
+                             int32_t out_stride, void* dx0, void* demb, el_dtype grad_dtype,
+                             hipStream_t stream);
+
 /* [host, pure] Bytes of device workspace that emb_grad_reduce_update and emb_grad_sort
  * need for these tables and bags (0 when nnz == 0).  Returns 0 for invalid arguments. */
 EL_API size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags);

@@ -27,7 +27,7 @@ def ref(x):
 def test_library_loads_and_exports_every_declared_function():
     L = ec.lib()
     names = ec.header_functions()
-    assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd",
+    assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
                           "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_prepare",
                           "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
@@ -84,6 +84,28 @@ def test_emb_dot_fwd_rejects():
     assert "emb_dot_fwd" in ec.el_last_error()
     # B == 0: valid, nothing enqueued
     assert L.emb_dot_fwd(T, ref(bags(B=0, nnz=0)), 0, A, ec.EL_BF16, None, A, 480, None) == ec.EL_OK
+
+
+def test_emb_dot_bwd_rejects():
+    L = ec.lib()
+    T, Bg = ref(tables()), ref(bags())
+    bf = ec.EL_BF16
+    assert L.emb_dot_bwd(T, Bg, 0, A, bf, A, 478, A, A, bf, None) == INVALID      # out_stride < D + P
+    assert L.emb_dot_bwd(T, Bg, 4, A, bf, A, 480, A, A, bf, None) == INVALID      # unknown flag
+    assert L.emb_dot_bwd(T, Bg, 0, 0, bf, A, 480, A, A, bf, None) == INVALID      # null x0
+    assert L.emb_dot_bwd(T, Bg, 0, A, bf, A + 8, 480, A, A, bf, None) == INVALID  # misaligned dout
+    assert L.emb_dot_bwd(T, Bg, 0, A, bf, A, 480, 0, A, bf, None) == INVALID      # null dx0
+    assert L.emb_dot_bwd(T, Bg, 0, A, bf, A, 480, A, 0, bf, None) == INVALID      # null demb
+    assert L.emb_dot_bwd(T, Bg, 0, A, bf, A, 480, A, A, 6, None) == INVALID       # unknown dtype
+    assert L.emb_dot_bwd(None, Bg, 0, A, bf, A, 480, A, A, bf, None) == INVALID
+    assert "emb_dot_bwd" in ec.el_last_error()
+    # shapes outside the fused kernel: refused on the host, nothing enqueued
+    assert L.emb_dot_bwd(ref(tables(F=40)), ref(bags(F=40)), 0, A, bf, A, 1000, A, A, bf, None) == UNSUPPORTED
+    assert L.emb_dot_bwd(ref(tables(D=16)), Bg, 0, A, bf, A, 376, A, A, bf, None) == UNSUPPORTED
+    assert L.emb_dot_bwd(T, Bg, 0, A, ec.EL_F32, A, 480, A, A, ec.EL_F32, None) == UNSUPPORTED
+    assert "emb_dot_bwd" in ec.el_last_error()
+    # B == 0: valid, nothing enqueued
+    assert L.emb_dot_bwd(T, ref(bags(B=0, nnz=0)), 0, A, bf, A, 480, A, A, bf, None) == ec.EL_OK
 
 
 def test_dot_interact_rejects():

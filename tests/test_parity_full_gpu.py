@@ -74,6 +74,18 @@ def test_train_step_full_size():
     assert_close(dx0[sel], r_dx0, "bf16", "train_step dx0")
     assert_close(demb[sel], r_demb, "bf16", "train_step demb")
 
+    # the fused forward without pooled output and the fused backward (pooled vectors rebuilt
+    # from the tables), as the benchmark's training step runs them: the same bits as above
+    out_f = torch.empty_like(out)
+    elf.emb_dot_fwd(tab, bags, x0, out_f, None)
+    dx0_f, demb_f = torch.empty_like(dx0), torch.empty_like(demb)
+    elf.emb_dot_bwd(tab, bags, x0, G, dx0_f, demb_f)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f.view(torch.int16), out.view(torch.int16)), "fused forward differs"
+    assert torch.equal(dx0_f.view(torch.int16), dx0.view(torch.int16)), "fused backward dx0 differs"
+    assert torch.equal(demb_f.view(torch.int16), demb.view(torch.int16)), "fused backward demb differs"
+    del out_f, dx0_f, demb_f
+
     # sort + segments: everything, bit for bit
     ws = elf.alloc_workspace(tab, bags)
     n = idx.numel()

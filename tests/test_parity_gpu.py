@@ -224,6 +224,76 @@ def test_dot_interact_bwd_matches_oracle(case):
     assert torch.equal(demb.view(torch.uint8), dembb.view(torch.uint8))
 
 
+FUSED_BWD_CASES = [
+    # label, rows, D, table dtype, act dtype, grad dtype, bag, index dist, hash, B
+    ("f32-bf16-26x128-zipf", (5000,) * 26, 128, "f32", "bf16", "bf16", ("one",), "zipf", False, 1000),
+    # more samples than resident workgroups: every register buffer and pipeline parity in
+    # turn, an odd number of trips, the clamped look-ahead past the last sample
+    ("f32-bf16-26x128-many-trips", (5000,) * 26, 128, "f32", "bf16", "bf16", ("one",), "zipf", False, 5001),
+    ("f32-bf16-one-sample", (5000,) * 26, 128, "f32", "bf16", "bf16", ("one",), "uniform", False, 1),
+    ("f32-bf16-f32-grad", (5000,) * 26, 128, "f32", "bf16", "f32", ("one",), "zipf", False, 700),
+    ("f16-ragged-tables", (3, 70000, 1234), 128, "f16", "f16", "f16", ("one",), "zipf", False, 1500),
+    # bags of other lengths (empty, multi-hot): pooled where the tile is written
+    ("bf16-d64-multihot-empty", (20000,) * 10, 64, "bf16", "bf16", "bf16", ("poisson", 3.0, 0, 10), "zipf", False, 300),
+    ("f32-bf16-d64-multihot", (2000,) * 12, 64, "f32", "bf16", "bf16", ("poisson", 8.0, 1, 30), "zipf", False, 2100),
+    ("f32-f16-hash", (999, 7, 5000), 32, "f32", "f16", "f16", ("one",), "uniform", True, 400),
+    ("bf16-hash-multihot", (999, 7, 5000), 64, "bf16", "bf16", "f32", ("poisson", 4.0, 0, 9), "zipf", True, 200),
+    ("bf16-32-vectors-d32", (300,) * 31, 32, "bf16", "bf16", "bf16", ("one",), "uniform", False, 999),
+    ("f16-table-bf16-act", (4000,) * 6, 128, "f16", "bf16", "bf16", ("one",), "zipf", False, 800),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_BWD_CASES, ids=[c[0] for c in FUSED_BWD_CASES])
+def test_emb_dot_bwd_matches_separate_calls_and_oracle(case):
+    label, rows, D, tdt, adt, gdt, bag, dist, hsh, B = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=adt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag, bottom_mlp=(13, 64, D))
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    x0 = synth.make_x0(wl, DEV)
+    at, gt = synth.torch_dtype(adt), synth.torch_dtype(gdt)
+    F, S = wl.num_tables, wl.out_stride
+    dout = synth.make_dout(wl, DEV).clone()
+    dout[:, wl.out_width:] = 1e3  # padding columns must be ignored
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    W_before = W.clone()
+    # the two calls
+    emb = torch.full((B, F, D), float("nan"), dtype=at, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb, hash_indices=hsh)
+    dx0_sep = torch.full((B, D), float("nan"), dtype=gt, device=DEV)
+    demb_sep = torch.full((B, F, D), float("nan"), dtype=gt, device=DEV)
+    elf.dot_interact_bwd(x0, emb, dout, dx0_sep, demb_sep)
+    # the fused call
+    dx0 = torch.full((B, D), float("nan"), dtype=gt, device=DEV)
+    demb = torch.full((B, F, D), float("nan"), dtype=gt, device=DEV)
+    elf.emb_dot_bwd(tab, bags, x0, dout, dx0, demb, hash_indices=hsh)
+    torch.cuda.synchronize()
+    assert torch.equal(dx0.view(torch.uint8), dx0_sep.view(torch.uint8)), label + ": dx0 differs from the two calls"
+    assert torch.equal(demb.view(torch.uint8), demb_sep.view(torch.uint8)), label + ": demb differs from the two calls"
+    assert torch.equal(W.view(torch.uint8), W_before.view(torch.uint8)), label + ": tables written"
+    # and the oracle, on its own pooled vectors
+    emb_ref = orc.emb_bag_fwd(to_np(W), tdt, to_np(ro), to_np(idx), to_np(off), B, D, adt, hash_indices=hsh)
+    rdx0, rdemb = orc.dot_interact_bwd(to_np(x0), emb_ref, adt, to_np(dout), adt, gdt)
+    assert_close(dx0, rdx0, gdt, label + " dx0")
+    assert_close(demb, rdemb, gdt, label + " demb")
+    # determinism
+    dx0b, dembb = torch.empty_like(dx0), torch.empty_like(demb)
+    elf.emb_dot_bwd(tab, bags, x0, dout, dx0b, dembb, hash_indices=hsh)
+    torch.cuda.synchronize()
+    assert torch.equal(dx0.view(torch.uint8), dx0b.view(torch.uint8))
+    assert torch.equal(demb.view(torch.uint8), dembb.view(torch.uint8))
+
+
+def test_emb_dot_bwd_refuses_shapes_outside_the_fused_kernel():
+    wl = base_wl(batch=16, rows=(100,) * 40, dim=32, act_dtype="bf16", bottom_mlp=(13, 64, 32))
+    W, ro, idx, off = make_problem(wl)
+    x0 = synth.make_x0(wl, DEV)
+    dout = synth.make_dout(wl, DEV)
+    dx0 = torch.zeros((16, 32), dtype=torch.bfloat16, device=DEV)
+    demb = torch.zeros((16, 40, 32), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(elf.EmbcoreError):
+        elf.emb_dot_bwd(elf.Tables(W, ro), elf.Bags(idx, off, 16), x0, dout, dx0, demb)
+
+
 SORT_CASES = [
     # label, rows, D, table dtype, grad dtype, bag, dist, hash, B
     ("hot1-zipf-26x5000", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 777),
