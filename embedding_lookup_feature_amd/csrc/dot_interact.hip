@@ -214,7 +214,7 @@ struct GatherSrc {
 };
 
 template <class IT, class GT, int UPT, int GPT, int KSM, int PD, class TT, bool GATHER>
-__global__ __launch_bounds__(256, GATHER ? 2 : 1) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
+__global__ __launch_bounds__(256, GATHER ? 2 : (UPT == 1 ? 4 : 1)) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
                                                       const uint16_t* __restrict__ emb, int B, int F,
                                                       int D, const uint16_t* __restrict__ dout,
                                                       int out_stride, typename GT::S* __restrict__ dx0,
