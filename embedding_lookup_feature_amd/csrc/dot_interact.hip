@@ -423,9 +423,21 @@ __global__ __launch_bounds__(256, GATHER ? 2 : (UPT == 1 ? 4 : 1)) void k_dot_bw
         *reinterpret_cast<u32x4*>(lds + (q < gchunks ? goff + q * 16 : trash)) = g[BF][gg];
       }
     } else {
+      // four chunks per thread in flight at once (clamped loads, masked LDS writes)
       const uint16_t* grow = dout + static_cast<int64_t>(bb) * out_stride;
-      for (int q = tid; q < gchunks; q += 256)
-        *reinterpret_cast<u32x4*>(lds + goff + q * 16) = *reinterpret_cast<const u32x4*>(grow + q * 8);
+      for (int q0 = 0; q0 < gchunks; q0 += 4 * 256) {
+        u32x4 gv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = q0 + k * 256 + tid;
+          gv[k] = *reinterpret_cast<const u32x4*>(grow + (q < gchunks ? q : gchunks - 1) * 8);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int q = q0 + k * 256 + tid;
+          *reinterpret_cast<u32x4*>(lds + (q < gchunks ? goff + q * 16 : trash)) = gv[k];
+        }
+      }
     }
   };
 
