@@ -88,6 +88,18 @@ def algorithmic_bytes(wl, nnz, store_emb=None):
     }
 
 
+def sort_start(wl, nnz):
+    """Where the sort of the lookups starts on its side stream: it needs only the indices, so
+    it may run beside the forward too, but the gather's row reuse in L2 suffers from it; it
+    starts with the step only when its passes (keys + bag ids read and written per 8-bit
+    digit) move more bytes than the interaction backward it would otherwise hide behind."""
+    sa = 4 if wl.act_dtype == "f32" else 2
+    key_bits = max(1, int(wl.total_rows - 1).bit_length())
+    sort_bytes = 16 * nnz * ((key_bits + 7) // 8)
+    bwd_bytes = wl.batch * wl.out_stride * sa + 2 * wl.batch * (wl.num_tables + 1) * wl.dim * sa
+    return "fwd" if sort_bytes > bwd_bytes else "bwd"
+
+
 def source_digest(paths):
     """sha256 over the given files (repo-relative), in order."""
     import hashlib
@@ -154,9 +166,11 @@ def main():
                     help="time emb_bag_fwd + dot_interact_fwd instead of emb_dot_fwd (which, for "
                          "forward-only workloads, does not store the pooled vectors at all, and in "
                          "training runs the two kernels on cache-sized chunks of samples)")
-    ap.add_argument("--overlap-sort", choices=["none", "fwd", "bwd"], default="bwd",
+    ap.add_argument("--overlap-sort", choices=["auto", "none", "fwd", "bwd"], default="auto",
                     help="run the gradient sort (emb_grad_prepare) on a side stream, from the start of "
-                         "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply")
+                         "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply; "
+                         "auto: from the start when the sort's passes move more bytes than the "
+                         "interaction backward, else from the end of the forward")
     ap.add_argument("--recompute-emb", action="store_true",
                     help="training: do not store the pooled vectors in the forward (emb_dot_fwd "
                          "without emb_out); rebuild them from the tables in the backward "
@@ -203,6 +217,8 @@ def main():
         ws = torch.empty(max(elf.emb_grad_workspace_bytes(tab, b[0]) for b in batches),
                          dtype=torch.uint8, device=dev)
 
+    if args.overlap_sort == "auto":
+        args.overlap_sort = sort_start(wl, batches[0][3].numel()) if wl.backward else "none"
     overlap = wl.backward and args.overlap_sort != "none"
     fused_fwd = not args.separate_fwd
     # training: store the pooled vectors and read them back (the faster order here), or
@@ -371,7 +387,9 @@ def main():
                    "total_rows": wl.total_rows, "dim": D,
                    "table_dtype": wl.table_dtype, "act_dtype": wl.act_dtype, "nnz": int(nnz),
                    "unique_rows": U, "parallelism": "single-gpu",
-                   "calls": " -> ".join(names) + (" (emb_grad_prepare on a side stream)" if overlap else "")},
+                   "calls": " -> ".join(names) + (f" (emb_grad_prepare on a side stream from the "
+                                                  f"{'start of the step' if args.overlap_sort == 'fwd' else 'end of the forward'})"
+                                                  if overlap else "")},
         "hbm_gbps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "calls": calls,
         "roofline": roofline,
