@@ -214,7 +214,7 @@ struct GatherSrc {
 };
 
 template <class IT, class GT, int UPT, int GPT, int KSM, int PD, class TT, bool GATHER>
-__global__ __launch_bounds__(256, GATHER ? 2 : (UPT == 1 ? 4 : 1)) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
+__global__ __launch_bounds__(256, GATHER ? 2 : (UPT == 1 ? 4 : (GPT == 3 ? 2 : 1))) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
                                                       const uint16_t* __restrict__ emb, int B, int F,
                                                       int D, const uint16_t* __restrict__ dout,
                                                       int out_stride, typename GT::S* __restrict__ dx0,
@@ -795,6 +795,8 @@ el_status launch_bwd_mfma(const void* x0, const void* emb, int B, int F, int D, 
     if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   } else if (V <= 128) {
+    if (units <= 512 && gchunks <= 768)
+      return launch_bwd_t<IT, GT, 2, 3, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   }
