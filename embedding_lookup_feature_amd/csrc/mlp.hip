@@ -640,8 +640,9 @@ void fill_tiles(GemmArgs& a) {
   a.tiles = ((a.R + C::BR - 1) / C::BR) * a.tiles_c;
 }
 
-// Splits of the weight-gradient reduction over the batch: enough workgroups to cover the
-// chip about twice (output tiles x splits >= 512), each split at least 4 LDS stages long.
+// Splits of the weight-gradient reduction over the batch: enough workgroups to fill every
+// CU's workgroup slots once (output tiles x splits >= 512 small or 256 large tiles), each
+// split at least 4 LDS stages long.
 // Large tiles once the output holds at least 8 of them (one workgroup per CU, so more
 // splits; with fewer tiles the split partials outweigh what the larger tile saves).
 WgradPlan plan_wgrad(int M, int K, int N) {
@@ -657,7 +658,8 @@ WgradPlan plan_wgrad(int M, int K, int N) {
   p.large = static_cast<long>((N + CfgL::BR - 1) / CfgL::BR) * ((K + CfgL::BC - 1) / CfgL::BC) >= 8;
   const int br = p.large ? CfgL::BR : CfgS::BR, bc = p.large ? CfgL::BC : CfgS::BC;
   const int tiles = ((N + br - 1) / br) * ((K + bc - 1) / bc);
-  int s = std::max(1, (512 + tiles - 1) / tiles);
+  const int target = p.large ? 256 : 512;  // workgroups: two per CU (small tiles), one (large)
+  int s = std::max(1, (target + tiles - 1) / tiles);
   const int max_s = std::max(1, M / (4 * kBK));
   s = std::min(std::min(s, max_s), 256);
   int per = (M + s - 1) / s;
