@@ -40,9 +40,24 @@ KERNEL_SOURCES = {
                       "embedding_lookup_feature_amd/csrc/el_mfma.hpp",
                       "embedding_lookup_feature_amd/csrc/emb_dot_fwd.hip"],
 }
+KERNEL_SOURCES["k_dot_fwd_valu"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
+KERNEL_SOURCES["k_dot_bwd_valu"] = KERNEL_SOURCES["k_dot_bwd_mfma"]
 KERNEL_OF_CALL = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
                   "dot_interact_bwd": "k_dot_bwd_mfma", "emb_dot_fwd": "k_emb_dot_fwd",
                   "emb_dot_bwd": "k_dot_bwd_mfma"}
+
+
+def kernel_of(call, wl):
+    """The kernel a one-kernel call runs for this workload's shape: the interaction takes
+    MFMA for 16-bit activations with D % 16 == 0 (the backward also D >= 32 and 16-byte
+    gradient rows), the fp32 FMA kernels otherwise."""
+    V, D = wl.num_tables + 1, wl.dim
+    mfma = wl.act_dtype in ("bf16", "f16") and D % 16 == 0 and V <= 128
+    if call == "dot_interact_fwd" and not mfma:
+        return "k_dot_fwd_valu"
+    if call == "dot_interact_bwd" and not (mfma and D >= 32 and wl.out_stride % 8 == 0):
+        return "k_dot_bwd_valu"
+    return KERNEL_OF_CALL[call]
 
 
 def fused_bwd_ok(wl):
@@ -179,6 +194,9 @@ def main():
                     help="forward-only latency / throughput over batch sizes 1 .. 1,048,576 on the "
                          "large fp16 tables (emb_dot_fwd, pooled vectors not stored); one JSON line "
                          "per batch size instead of the step line")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of HIP graphs, one per index batch, each capturing one whole "
+                         "step (both streams); per-call times still come from eager calls")
     ap.add_argument("--no-copy-bw", action="store_true",
                     help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
     args = ap.parse_args()
@@ -236,13 +254,17 @@ def main():
         names = fwd_names + [bwd_name, "emb_grad_reduce_update"]
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else None  # default priority
-    applied = torch.cuda.Event()
     prepared = torch.cuda.Event()
     fwd_done = torch.cuda.Event()
-    applied.record(main_stream)
+    fork = torch.cuda.Event()
 
     def start_sort(bags, side_ev):
-        side.wait_event(applied)  # the workspace is free once the previous update is done
+        # the workspace is free once the previous update is done: from the start of the step,
+        # fork from the step's stream (the update ran there before); from the end of the
+        # forward, the wait for the forward already implies it
+        if args.overlap_sort == "fwd":
+            fork.record(torch.cuda.current_stream())
+            side.wait_event(fork)
         if side_ev: side_ev[0].record(side)
         elf.emb_grad_prepare(tab, bags, ws, stream=side)
         if side_ev: side_ev[1].record(side)
@@ -269,7 +291,7 @@ def main():
         if not wl.backward:
             return
         if overlap and args.overlap_sort == "bwd":
-            fwd_done.record(main_stream)
+            fwd_done.record(torch.cuda.current_stream())
             side.wait_event(fwd_done)
             start_sort(bags, side_ev)
         if recompute:
@@ -279,9 +301,8 @@ def main():
         if ev: ev[k].record()
         k += 1
         if overlap:
-            main_stream.wait_event(prepared)
+            torch.cuda.current_stream().wait_event(prepared)
             elf.emb_grad_apply(tab, bags, demb, wl.lr, ws)
-            applied.record(main_stream)
         else:
             elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
         if ev: ev[k].record()
@@ -299,6 +320,20 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    graphs = None
+    if args.graph:
+        # one graph per index batch, each one whole step; captured after the warm-up (which
+        # filled the library's host-side occupancy cache), replayed in batch order
+        graphs = []
+        for i in range(len(batches)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(len(batches)):
+            graphs[i].replay()
+        torch.cuda.synchronize()
+
     # timed region: K whole steps, no per-call events (nothing but the path in the stream)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -306,7 +341,10 @@ def main():
     if side is not None:
         side.wait_stream(main_stream)  # no side-stream work starts before t0
     for i in range(args.steps):
-        step(i)
+        if graphs:
+            graphs[i % len(graphs)].replay()
+        else:
+            step(i)
     t1.record()  # the last update waited for the last sort, so all work is before t1
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -360,7 +398,7 @@ def main():
     # emb_dot_fwd is a sequence of gather and interaction launches)
     single = [n for n in names if n in KERNEL_OF_CALL and not (n == "emb_dot_fwd" and store_emb)]
     dom = max(single, key=lambda n: call_ms[n])
-    kernel = KERNEL_OF_CALL[dom]
+    kernel = kernel_of(dom, wl)
     achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -387,6 +425,7 @@ def main():
                    "total_rows": wl.total_rows, "dim": D,
                    "table_dtype": wl.table_dtype, "act_dtype": wl.act_dtype, "nnz": int(nnz),
                    "unique_rows": U, "parallelism": "single-gpu",
+                   "launch": "HIP graph replay, one graph per step" if args.graph else "eager",
                    "calls": " -> ".join(names) + (f" (emb_grad_prepare on a side stream from the "
                                                   f"{'start of the step' if args.overlap_sort == 'fwd' else 'end of the forward'})"
                                                   if overlap else "")},

@@ -71,3 +71,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_roofline_names_the_kernel_the_shape_runs():
+    assert bench.kernel_of("dot_interact_bwd", synth.WORKLOADS["train_step"]) == "k_dot_bwd_mfma"
+    assert bench.kernel_of("dot_interact_bwd", synth.WORKLOADS["multi_hot"]) == "k_dot_bwd_mfma"
+    assert bench.kernel_of("dot_interact_bwd", synth.WORKLOADS["tiny"]) == "k_dot_bwd_valu"       # fp32
+    assert bench.kernel_of("dot_interact_bwd", synth.WORKLOADS["train_small_tables"]) == "k_dot_bwd_valu"  # D = 16
+    assert bench.kernel_of("dot_interact_fwd", synth.WORKLOADS["tiny"]) == "k_dot_fwd_valu"
+    assert bench.kernel_of("dot_interact_fwd", synth.WORKLOADS["train_small_tables"]) == "k_dot_fwd_mfma"
