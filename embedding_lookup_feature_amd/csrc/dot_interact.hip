@@ -187,6 +187,9 @@ __global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __res
 // UPT: row pairs per thread; GPT: gradient-row chunks per thread held in registers
 // (0: loaded straight into LDS when the sample starts); KSM: K steps (>= KS); PD: samples
 // in flight per workgroup (1, or 2 with GPT > 0: a third measured no faster).
+// Workgroups per CU the register budget is set for: four for one row pair per thread
+// (117 VGPRs, measured faster than three), two for the gather variant and for three
+// register-held gradient chunks (at most 256 VGPRs), otherwise what the kernel needs.
 // ---------------------------------------------------------------------------------------
 template <int N>
 using Buf = std::integral_constant<int, N>;
@@ -213,12 +216,14 @@ struct GatherSrc {
   uint32_t hash;            // floor-mod the indices by the table's row count
 };
 
+template <int UPT, int GPT, bool GATHER>
+constexpr int bwd_wg_per_cu() { return GATHER ? 2 : (UPT == 1 ? 4 : (GPT == 3 ? 2 : 1)); }
+
 template <class IT, class GT, int UPT, int GPT, int KSM, int PD, class TT, bool GATHER>
-__global__ __launch_bounds__(256, GATHER ? 2 : (UPT == 1 ? 4 : (GPT == 3 ? 2 : 1))) void k_dot_bwd_mfma(const uint16_t* __restrict__ x0,
-                                                      const uint16_t* __restrict__ emb, int B, int F,
-                                                      int D, const uint16_t* __restrict__ dout,
-                                                      int out_stride, typename GT::S* __restrict__ dx0,
-                                                      typename GT::S* __restrict__ demb, GatherSrc gs) {
+__global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_dot_bwd_mfma(
+    const uint16_t* __restrict__ x0, const uint16_t* __restrict__ emb, int B, int F, int D,
+    const uint16_t* __restrict__ dout, int out_stride, typename GT::S* __restrict__ dx0,
+    typename GT::S* __restrict__ demb, GatherSrc gs) {
   extern __shared__ uint4 smem[];
   char* lds = reinterpret_cast<char*>(smem);
   using GS = typename GT::S;
