@@ -74,7 +74,6 @@ __global__ __launch_bounds__(64) void k_emb_dot_fwd(
     uint16_t* __restrict__ out, int32_t out_stride) {
   extern __shared__ uint4 smem[];
   char* lds = reinterpret_cast<char*>(smem);
-  using S = typename TT::S;
   const int lane = threadIdx.x;
   const int V = F + 1;
   const int P = V * (V - 1) / 2;
