@@ -182,7 +182,10 @@ __global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __res
 // them into 8 two-vector words and writes those into V^T.  Compute: the 32 x 32 output
 // tiles (vector tile, dimension tile) are dealt round-robin to the 4 wavefronts.  Store:
 // all threads write the V x D block with 16-byte stores; dx0 = G[0:D) + dV_0 is formed
-// there from an fp32 copy of dV_0.  dout has the input's 16-bit type (S is then exact).
+// there from an fp32 copy of dV_0 and the G[0:D) chunk each thread read into registers
+// before the barrier that ends the compute (the gradient row's LDS bytes are rewritten by
+// the next sample's fill once a wavefront passes that barrier, so nothing reads them after
+// it).  dout has the input's 16-bit type (S is then exact).
 // LDS: V^T [D][VP] | gradient row | VP x D output block | dV_0 in fp32 | scratch slot.
 // UPT: row pairs per thread; GPT: gradient-row chunks per thread held in registers
 // (0: loaded straight into LDS when the sample starts); KSM: K steps (>= KS); PD: samples
@@ -497,6 +500,13 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
         }
       }
     }
+    // dx0's direct term G[0:D): every thread takes gradient-row chunk qd into registers
+    // before the barrier below.  After that barrier no thread reads the gradient row: a
+    // wavefront that runs ahead may already be writing the next sample's row into the same
+    // LDS bytes (put()), and the barrier is the last one it waits at before doing so.
+    const int nd = D / 8;
+    const int qd = tid < nd ? tid : nd - 1;  // threads past D/8 repeat the last chunk
+    const u32x4 gdir = *reinterpret_cast<const u32x4*>(lds + goff + qd * 16);
     __syncthreads();
     // rows 1.. -> demb[b] (contiguous), row 0 -> dx0[b] = G[0:D) + dV_0; 16-byte stores.
     // Every thread issues a fixed number of stores (threads past the end repeat the last
@@ -514,15 +524,17 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
           *reinterpret_cast<const uint4*>(lds + ooff + row * opitch + c * 16);
     }
     {
-      // Thread q takes the 8 values of gradient-row chunk q, the chunk it wrote itself in
-      // put(): the next sample's put() cannot overwrite them before they are read.
-      const int nd = D / 8;
-      const int q = tid < nd ? tid : nd - 1;
+      // dx0 chunk qd = G[0:D) chunk (registers) + dV_0 chunk (fp32 in LDS; its next writer
+      // runs only after the next sample's first barrier, which every thread reaches after
+      // this read).  Threads past D/8 store the last chunk again with the same bytes.
       float f[8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x)
-        f[x] = reinterpret_cast<const float*>(lds + r0off)[q * 8 + x] + IT::to_f(G[q * 8 + x]);
-      store_n<GT, 8>(dx0 + static_cast<int64_t>(b) * D + q * 8, f);
+      for (int x = 0; x < 8; ++x) {
+        const uint32_t w = gdir[x >> 1];
+        const uint16_t gv = static_cast<uint16_t>((x & 1) ? (w >> 16) : (w & 0xffffu));
+        f[x] = reinterpret_cast<const float*>(lds + r0off)[qd * 8 + x] + IT::to_f(gv);
+      }
+      store_n<GT, 8>(dx0 + static_cast<int64_t>(b) * D + qd * 8, f);
     }
   };
 

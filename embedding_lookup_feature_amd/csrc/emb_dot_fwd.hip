@@ -253,7 +253,9 @@ el_status launch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags
   else if (units <= 12 * 64) EL_SPL(12);
   else if (units <= 16 * 64) EL_SPL(16);
 #undef EL_SPL
-  return EL_ERR_UNSUPPORTED;
+  return set_error(EL_ERR_UNSUPPORTED,
+                   "emb_dot_fwd: without emb_out the fused kernel covers F * D / 8 <= 1024 row chunks "
+                   "and output rows of at most 4096 bytes");
 }
 
 template <class TT>
@@ -262,7 +264,7 @@ el_status launch_act(const el_tables& tab, const el_bags& bags, uint32_t flags, 
                      hipStream_t stream) {
   if (act == EL_BF16) return launch_shape<TT, BF16T>(tab, bags, flags, x0, out, out_stride, lds, stream);
   if (act == EL_F16) return launch_shape<TT, F16T>(tab, bags, flags, x0, out, out_stride, lds, stream);
-  return EL_ERR_UNSUPPORTED;
+  return set_error(EL_ERR_UNSUPPORTED, "emb_dot_fwd: without emb_out the activations must be bf16 or fp16");
 }
 
 }  // namespace
@@ -308,7 +310,7 @@ el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t
     case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
     case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
   }
-  return EL_ERR_UNSUPPORTED;
+  return set_error(EL_ERR_INVALID_ARG, "emb_dot_fwd: unknown table dtype");
 }
 
 }  // namespace el

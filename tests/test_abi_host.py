@@ -86,6 +86,27 @@ def test_emb_dot_fwd_rejects():
     assert L.emb_dot_fwd(T, ref(bags(B=0, nnz=0)), 0, A, ec.EL_BF16, None, A, 480, None) == ec.EL_OK
 
 
+def test_emb_dot_fwd_unsupported_fused_shapes_say_why():
+    """Without emb_out, shapes outside the fused kernel's classes are refused on the host with
+    their own error text (not a stale one from an earlier call)."""
+    L = ec.lib()
+    assert L.emb_bag_fwd(None, ref(bags()), 0, A, ec.EL_BF16, None) == INVALID
+    assert "emb_bag_fwd" in ec.el_last_error()
+    # 65 vectors of 16: a 2096-element bf16 output row (4192 bytes) exceeds the fused kernel's
+    # output-row classes
+    rc = L.emb_dot_fwd(ref(tables(F=64, D=16)), ref(bags(F=64)), 0, A, ec.EL_BF16, None, A, 2096, None)
+    assert rc == UNSUPPORTED
+    assert "emb_dot_fwd" in ec.el_last_error() and "4096 bytes" in ec.el_last_error()
+    # 64 tables of 256: more row chunks per sample than the fused kernel holds
+    assert L.emb_bag_fwd(None, ref(bags()), 0, A, ec.EL_BF16, None) == INVALID
+    rc = L.emb_dot_fwd(ref(tables(F=64, D=256)), ref(bags(F=64)), 0, A, ec.EL_BF16, None, A, 2336, None)
+    assert rc == UNSUPPORTED
+    assert "emb_dot_fwd" in ec.el_last_error()
+    # fp32 activations without emb_out
+    rc = L.emb_dot_fwd(ref(tables()), ref(bags()), 0, A, ec.EL_F32, None, A, 480, None)
+    assert rc == UNSUPPORTED and "emb_dot_fwd" in ec.el_last_error()
+
+
 def test_emb_dot_bwd_rejects():
     L = ec.lib()
     T, Bg = ref(tables()), ref(bags())

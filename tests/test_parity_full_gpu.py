@@ -267,3 +267,69 @@ def test_train_small_tables_full_size_chain():
     torch.cuda.synchronize()
     r_W = orc.grad_reduce_update(W0, "f32", ro_h, idx_h, off_h, B, to_np(dsyn), "bf16", wl.lr)
     assert_close(W, r_W, "f32", "train_small SGD")
+
+
+def direct_term_dout(wl, dev, batch_id=0):
+    """Upstream gradient whose pair gradients of the pairs (i, 0) are zero: S_0j = 0 for
+    every j, so dV_0 = 0 exactly and dx0 = G[0:D) + dV_0 must equal G[0:D) bit for bit (a
+    property of the backward's definition that holds at any size, checked on every sample)."""
+    G = synth.make_dout(wl, dev, batch_id).clone()
+    V, D = wl.num_tables + 1, wl.dim
+    cols = torch.tensor([D + i * (i - 1) // 2 for i in range(1, V)], device=dev)
+    G[:, cols] = 0
+    return G
+
+
+DIRECT_TERM_CASES = {
+    # the benchmark's two backward shapes (one row pair and gradient chunk per thread, two
+    # samples in flight; the gradient row held in registers over three chunks per thread)
+    "train_step": lambda: synth.WORKLOADS["train_step"],
+    "multi_hot": lambda: synth.WORKLOADS["multi_hot"],
+    # 41 vectors of 64: the gradient row staged into LDS at each sample's start
+    "41x64-staged-gradient-row": lambda: synth.WORKLOADS["train_step"].scaled(
+        name="direct41", batch=30001, rows=(1000,) * 40, dim=64, bottom_mlp=(13, 64, 64)),
+}
+
+
+@pytest.mark.parametrize("workload", list(DIRECT_TERM_CASES))
+def test_dot_bwd_direct_term_every_sample(workload):
+    """dx0's direct term at full size in the benchmark's launch configuration, every sample:
+    the gradient row of a sample must not be mixed with that of a sample processed later by
+    the same workgroup (the interaction backward refills its gradient-row buffer for the next
+    sample while slower wavefronts may still be finishing the current one).  The other
+    pair gradients stay non-zero, so the kernel does its full work; demb is checked against
+    the oracle on sampled samples."""
+    wl = DIRECT_TERM_CASES[workload]()
+    B, F, D = wl.batch, wl.num_tables, wl.dim
+    x0 = synth.make_x0(wl, DEV)
+    emb = synth.make_emb(wl, DEV)
+    G = direct_term_dout(wl, DEV)
+    dx0 = torch.full((B, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    demb = torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV)
+    for _ in range(3):  # several launches: wavefront drift differs from run to run
+        elf.dot_interact_bwd(x0, emb, G, dx0, demb)
+        torch.cuda.synchronize()
+        assert torch.equal(dx0.view(torch.int16), G[:, :D].contiguous().view(torch.int16)), \
+            f"{workload}: dx0 != G[0:D) with dV_0 = 0"
+    s = sample_ids(B, k=64)
+    sel = torch.from_numpy(s).to(DEV)
+    _, r_demb = orc.dot_interact_bwd(to_np(x0)[s], to_np(emb)[s], "bf16", to_np(G)[s], "bf16", "bf16")
+    assert_close(demb[sel], r_demb, "bf16", f"{workload} demb")
+
+
+def test_emb_dot_bwd_direct_term_every_sample():
+    """The same property through the backward that rebuilds the pooled vectors from the
+    tables (train_step shapes, full batch)."""
+    wl = synth.WORKLOADS["train_step"]
+    B, D = wl.batch, wl.dim
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    x0 = synth.make_x0(wl, DEV)
+    G = direct_term_dout(wl, DEV)
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    dx0 = torch.full((B, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    demb = torch.empty((B, wl.num_tables, D), dtype=torch.bfloat16, device=DEV)
+    for _ in range(2):
+        elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb)
+        torch.cuda.synchronize()
+        assert torch.equal(dx0.view(torch.int16), G[:, :D].contiguous().view(torch.int16))
