@@ -312,6 +312,54 @@ int oracle_dot_interact_bwd(const void* x0, const void* emb, int in_dtype, int B
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* "cat" interaction (--interaction_op cat)                                              */
+/* ------------------------------------------------------------------------------------ */
+
+/*
+ * The interaction that concatenates instead of multiplying: out[b] = [ V_0 | V_1 | ... |
+ * V_F | +0 pad ], the sample's V = F + 1 vectors (V_0 = x0[b], V_{1+t} = the pooled
+ * embedding of table t), D values each, one after another, then zeros up to out_stride
+ * >= V*D.  The bottom-MLP output the model concatenates with the interaction output is
+ * V_0 itself, so it appears once.  Each value is rounded once to out_dtype.
+ */
+int oracle_cat_interact_fwd(const void* x0, const void* emb, int in_dtype, int B, int F, int D,
+                            void* out, int out_dtype, int out_stride) {
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return OR_BAD_DTYPE;
+  int V = F + 1;
+  if (F < 1 || D < 1 || B < 0 || out_stride < (int64_t)V * D) return OR_BAD_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    size_t row = (size_t)b * out_stride;
+    for (int v = 0; v < V; ++v)
+      for (int d = 0; d < D; ++d)
+        store_elem(out, out_dtype, row + (size_t)v * D + d, vec_elem(x0, emb, in_dtype, b, F, D, v, d));
+    for (int64_t c = (int64_t)V * D; c < out_stride; ++c) store_elem(out, out_dtype, row + c, 0.0);
+  }
+  return OR_OK;
+}
+
+/*
+ * Backward of the cat interaction for an upstream gradient G = dout[b]: each output value
+ * is one element of one vector, so a vector's gradient is its own block of G:
+ * dx0[b] = G[0:D), demb[b][t] = G[D(1+t) : D(2+t)).  Padding columns are ignored.
+ */
+int oracle_cat_interact_bwd(const void* dout, int dout_dtype, int B, int F, int D, int out_stride,
+                            void* dx0, void* demb, int grad_dtype) {
+  if (!dtype_ok(dout_dtype) || !dtype_ok(grad_dtype)) return OR_BAD_DTYPE;
+  int V = F + 1;
+  if (F < 1 || D < 1 || B < 0 || out_stride < (int64_t)V * D) return OR_BAD_SHAPE;
+  for (int b = 0; b < B; ++b) {
+    size_t row = (size_t)b * out_stride;
+    for (int d = 0; d < D; ++d)
+      store_elem(dx0, grad_dtype, (size_t)b * D + d, load_elem(dout, dout_dtype, row + d));
+    for (int t = 0; t < F; ++t)
+      for (int d = 0; d < D; ++d)
+        store_elem(demb, grad_dtype, ((size_t)b * F + t) * D + d,
+                   load_elem(dout, dout_dtype, row + (size_t)(1 + t) * D + d));
+  }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Embedding-gradient sort, run-length segments, reduce + SGD row update                 */
 /* ------------------------------------------------------------------------------------ */
 
@@ -558,4 +606,4 @@ int oracle_sgd_dense(float* master, const float* grad, int64_t n, float lr, void
   return OR_OK;
 }
 
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }

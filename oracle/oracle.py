@@ -45,6 +45,8 @@ def _configure(L):
     L.oracle_emb_bag_fwd.argtypes = [vp, i32, vp, i32, i32, vp, vp, i32, i32, vp, i32]
     L.oracle_dot_interact_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, i32]
     L.oracle_dot_interact_bwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, i32, vp, vp, i32]
+    L.oracle_cat_interact_fwd.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, i32]
+    L.oracle_cat_interact_bwd.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32]
     L.oracle_grad_sort.argtypes = [vp, i32, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     L.oracle_grad_reduce_update.argtypes = [vp, i32, vp, i32, i32, vp, vp, i32, i32, vp, i32,
                                             ctypes.c_float]
@@ -57,6 +59,7 @@ def _configure(L):
     L.oracle_bce_logits.argtypes = [vp, i32, vp, i32, vp, vp, i32]
     L.oracle_sgd_dense.argtypes = [vp, vp, i64, ctypes.c_float, vp, i32]
     for name in ("oracle_emb_bag_fwd", "oracle_dot_interact_fwd", "oracle_dot_interact_bwd",
+                 "oracle_cat_interact_fwd", "oracle_cat_interact_bwd",
                  "oracle_grad_sort", "oracle_grad_reduce_update", "oracle_linear_fwd",
                  "oracle_linear_bwd", "oracle_relu_bwd", "oracle_bce_logits", "oracle_sgd_dense", "oracle_version"):
         getattr(L, name).restype = ctypes.c_int
@@ -141,6 +144,30 @@ def dot_interact_bwd(x0, emb, in_dtype, dout, dout_dtype, grad_dtype):
     _check(lib().oracle_dot_interact_bwd(_ptr(x0), _ptr(emb), _CODES[in_dtype], B, F, D,
                                          _ptr(dout), _CODES[dout_dtype], dout.shape[1],
                                          _ptr(dx0), _ptr(demb), _CODES[grad_dtype]))
+    return dx0, demb
+
+
+def cat_interact_fwd(x0, emb, in_dtype, out_dtype, out_stride):
+    """--interaction_op cat: [x0 | emb[0] | ... | emb[F-1] | zero pad] per sample; returns
+    out [B][out_stride]."""
+    x0 = _as(x0, in_dtype)
+    emb = _as(emb, in_dtype)
+    B, F, D = emb.shape
+    out = empty((B, out_stride), out_dtype)
+    _check(lib().oracle_cat_interact_fwd(_ptr(x0), _ptr(emb), _CODES[in_dtype], B, F, D,
+                                         _ptr(out), _CODES[out_dtype], out_stride))
+    return out
+
+
+def cat_interact_bwd(dout, dout_dtype, F, D, grad_dtype):
+    """Gradients of the cat interaction (each vector's block of dout); returns
+    (dx0 [B][D], demb [B][F][D]) in `grad_dtype`."""
+    dout = _as(dout, dout_dtype)
+    B, S = dout.shape
+    dx0 = empty((B, D), grad_dtype)
+    demb = empty((B, F, D), grad_dtype)
+    _check(lib().oracle_cat_interact_bwd(_ptr(dout), _CODES[dout_dtype], B, F, D, S, _ptr(dx0),
+                                         _ptr(demb), _CODES[grad_dtype]))
     return dx0, demb
 
 

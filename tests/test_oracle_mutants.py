@@ -39,6 +39,17 @@ MUTANTS = [
      "double r = floor(n) * quantum;"),
     ("subnormal quantum not clamped", "if (E < emin) E = emin;", ""),
     ("padding not zeroed", "for (int64_t c = D + P; c < out_stride; ++c) store_elem(out, out_dtype, row + c, 0.0);", ""),
+    ("cat blocks in the wrong order",
+     "store_elem(out, out_dtype, row + (size_t)v * D + d, vec_elem(x0, emb, in_dtype, b, F, D, v, d));",
+     "store_elem(out, out_dtype, row + (size_t)v * D + d, vec_elem(x0, emb, in_dtype, b, F, D, (v + 1) % V, d));"),
+    ("cat padding not zeroed",
+     "for (int64_t c = (int64_t)V * D; c < out_stride; ++c) store_elem(out, out_dtype, row + c, 0.0);", ""),
+    ("cat gradient read from the neighbouring block",
+     "load_elem(dout, dout_dtype, row + (size_t)(1 + t) * D + d));",
+     "load_elem(dout, dout_dtype, row + (size_t)t * D + d));"),
+    ("cat gradient with tables and dimensions transposed",
+     "store_elem(demb, grad_dtype, ((size_t)b * F + t) * D + d,",
+     "store_elem(demb, grad_dtype, ((size_t)b * D + d) * F + t,"),
     ("dense layer reads its weights transposed",
      "s += load_elem(x, x_dtype, (size_t)m * ldx + k) * load_elem(w, w_dtype, (size_t)n * K + k);",
      "s += load_elem(x, x_dtype, (size_t)m * ldx + k) * load_elem(w, w_dtype, ((size_t)k * N + n) % ((size_t)N * K));"),
@@ -82,6 +93,11 @@ def battery():
         pins.test_dot_fwd_pair_sum_closed_form,
         lambda: pins.test_dot_bwd_central_differences_exact_for_quadratic(3, 4),
         pins.test_dot_bwd_matches_symmetric_matrix_product_and_euler,
+        lambda: pins.test_cat_fwd_equals_numpy_stack_of_the_vectors(8, 16, 5),
+        pins.test_cat_fwd_blocks_are_the_vectors_the_dot_interaction_multiplies,
+        pins.test_cat_fwd_bf16_is_an_exact_copy_and_f32_narrowing_rounds_once,
+        pins.test_cat_bwd_central_differences_and_adjoint_identity,
+        pins.test_cat_bwd_of_the_forward_output_returns_the_inputs_and_ignores_padding,
         lambda: pins.test_grad_sort_matches_numpy_stable_argsort(True),
         pins.test_grad_sort_counting_sort_on_tiny_key_range,
         lambda: pins.test_grad_update_equals_dense_sgd(5),

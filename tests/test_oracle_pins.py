@@ -426,6 +426,105 @@ def test_dot_bwd_ignores_padding_columns():
 
 
 # ----------------------------------------------------------------------------------------
+# "cat" interaction (--interaction_op cat): the sample's vectors side by side
+# ----------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("F,D,pad", [(1, 4, 0), (8, 16, 5), (26, 128, 0), (5, 3, 1)])
+def test_cat_fwd_equals_numpy_stack_of_the_vectors(F, D, pad):
+    """numpy's stack of [x0, emb[0], ..., emb[F-1]] along a new axis, flattened per sample
+    (vector 0 = the bottom-MLP output, vector 1+t = table t), then zeros."""
+    rng = np.random.default_rng(30 + F)
+    B = 7
+    x0 = rng.normal(size=(B, D))
+    emb = rng.normal(size=(B, F, D))
+    V = F + 1
+    out = orc.cat_interact_fwd(x0, emb, "f64", "f64", V * D + pad)
+    ref = np.stack([x0] + [emb[:, t, :] for t in range(F)], axis=1).reshape(B, V * D)
+    assert np.array_equal(out[:, :V * D], ref)
+    assert np.all(out[:, V * D:] == 0) and not np.any(np.signbit(out[:, V * D:]))
+
+
+def test_cat_fwd_blocks_are_the_vectors_the_dot_interaction_multiplies():
+    """The cat output's D-wide blocks, as a [V][D] matrix R, give numpy's Gram matrix
+    R R^T whose strict lower triangle is the dot interaction's pair output (same vector
+    order), and block 0 is the dot interaction's x0 copy."""
+    rng = np.random.default_rng(31)
+    B, F, D = 5, 6, 8
+    x0 = rng.normal(size=(B, D))
+    emb = rng.normal(size=(B, F, D))
+    V = F + 1
+    cat = orc.cat_interact_fwd(x0, emb, "f64", "f64", V * D)
+    _, Z = gram_reference(x0, emb)
+    R = cat.reshape(B, V, D)
+    np.testing.assert_allclose(R @ np.transpose(R, (0, 2, 1)), Z, rtol=1e-13, atol=1e-13)
+    assert np.array_equal(R[:, 0, :], x0)
+
+
+def test_cat_fwd_bf16_is_an_exact_copy_and_f32_narrowing_rounds_once():
+    rng = np.random.default_rng(32)
+    B, F, D = 4, 3, 16
+    x0 = orc.round_from_f64(rng.normal(size=(B, D)), "bf16")
+    emb = orc.round_from_f64(rng.normal(size=(B, F, D)), "bf16")
+    out = orc.cat_interact_fwd(x0, emb, "bf16", "bf16", (F + 1) * D + 8)
+    assert np.array_equal(out[:, :D], x0)
+    assert np.array_equal(out[:, D:(F + 1) * D].reshape(B, F, D), emb)
+    assert np.all(out[:, (F + 1) * D:] == 0)
+    # fp32 in, bf16 out: each element rounded once, to the nearest bf16 (exhaustive search)
+    x32 = rng.normal(size=(B, D)).astype(np.float32)
+    e32 = rng.normal(size=(B, F, D)).astype(np.float32)
+    o16 = orc.cat_interact_fwd(x32, e32, "f32", "bf16", (F + 1) * D)
+    for x, o in zip(np.concatenate([x32, e32.reshape(B, -1)], 1).reshape(-1)[:300], o16.reshape(-1)[:300]):
+        assert int(o) == nearest_bf16_bruteforce(float(x))
+
+
+def cat_loss_numpy(x0, emb, G):
+    """sum G * [x0 | emb flattened] (numpy; linear in the inputs)."""
+    B, F, D = emb.shape
+    return float(np.sum(G[:, :D] * x0) + np.sum(G[:, D:(F + 1) * D] * emb.reshape(B, F * D)))
+
+
+def test_cat_bwd_central_differences_and_adjoint_identity():
+    """The loss sum G * out is linear in (x0, emb): central differences are exact, and the
+    backward is the adjoint of the forward, <G, cat(x0, emb)> = <dx0, x0> + <demb, emb>."""
+    rng = np.random.default_rng(33)
+    B, F, D = 3, 4, 5
+    x0 = rng.normal(size=(B, D))
+    emb = rng.normal(size=(B, F, D))
+    G = rng.normal(size=(B, (F + 1) * D + 3))
+    dx0, demb = orc.cat_interact_bwd(G, "f64", F, D, "f64")
+    h = 0.5
+    for arr, grad in ((x0, dx0), (emb, demb)):
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            old = arr[ix]
+            arr[ix] = old + h
+            lp = cat_loss_numpy(x0, emb, G)
+            arr[ix] = old - h
+            lm = cat_loss_numpy(x0, emb, G)
+            arr[ix] = old
+            assert grad[ix] == pytest.approx((lp - lm) / (2 * h), rel=1e-12, abs=1e-12)
+    out = orc.cat_interact_fwd(x0, emb, "f64", "f64", G.shape[1])
+    lhs = float(np.sum(G * out))
+    rhs = float(np.sum(dx0 * x0) + np.sum(demb * emb))
+    assert lhs == pytest.approx(rhs, rel=1e-12)
+
+
+def test_cat_bwd_of_the_forward_output_returns_the_inputs_and_ignores_padding():
+    """Special case: with G = the forward's own output the gradient blocks are the inputs
+    themselves (bit for bit); padding columns of G do not matter."""
+    rng = np.random.default_rng(34)
+    B, F, D = 6, 7, 8
+    x0 = orc.round_from_f64(rng.normal(size=(B, D)), "bf16")
+    emb = orc.round_from_f64(rng.normal(size=(B, F, D)), "bf16")
+    S = (F + 1) * D + 8
+    out = orc.cat_interact_fwd(x0, emb, "bf16", "bf16", S)
+    out[:, (F + 1) * D:] = 0x7F00  # large values in the padding
+    dx0, demb = orc.cat_interact_bwd(out, "bf16", F, D, "bf16")
+    assert np.array_equal(dx0, x0) and np.array_equal(demb, emb)
+
+
+# ----------------------------------------------------------------------------------------
 # sort, segments, reduce + SGD
 # ----------------------------------------------------------------------------------------
 
