@@ -20,6 +20,7 @@ from .embcore import (  # noqa: F401
     emb_grad_apply,
     emb_grad_prepare,
     emb_grad_reduce_update,
+    emb_grad_reduce_update_noalloc,
     emb_grad_sort,
     emb_grad_workspace_bytes,
     bce_logits,

@@ -3,6 +3,7 @@
 #include <cinttypes>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "el_internal.hpp"
@@ -77,6 +78,34 @@ el_status check_interaction(const char* fn, int32_t B, int32_t F, int32_t D, int
   const int64_t V = static_cast<int64_t>(F) + 1;
   const int64_t P = V * (V - 1) / 2;
   if (static_cast<int64_t>(out_stride) < D + P) return bad(fn, "out_stride < D + (F+1)F/2");
+  return EL_OK;
+}
+
+// Scratch of emb_grad_reduce_update_noalloc (for callers that cannot allocate): one
+// file-scope device array, of which every GPU the library runs on holds its own copy until
+// the process ends.  In host code `scratch` only names the symbol; its device address on
+// the current device comes from hipGetSymbolAddress, taken once per device and kept here.
+constexpr size_t kNoallocScratchBytes = EL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (resolved on the first call there).
+el_status noalloc_scratch(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(EL_ERR_HIP, std::string(fn) + ": no usable current device");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(EL_ERR_HIP, std::string(fn) + ": hipGetSymbolAddress(scratch): " + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return EL_OK;
 }
 
@@ -208,6 +237,31 @@ el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bags, uint
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
   EL_TRY(check_dense(fn, demb, true, "demb"));
   GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  uint32_t *keys = nullptr, *vals = nullptr;
+  EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
+  return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
+}
+
+el_status emb_grad_reduce_update_noalloc(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                                         const void* demb, el_dtype grad_dtype, float lr,
+                                         hipStream_t stream) {
+  const char* fn = "emb_grad_reduce_update_noalloc";
+  EL_TRY(check_tables(tab, fn));
+  EL_TRY(check_bags(tab, bags, fn));
+  if (flags & ~static_cast<uint32_t>(EL_FLAG_HASH_INDICES)) return bad(fn, "unknown flags");
+  EL_TRY(check_grad_input(fn, tab, grad_dtype));
+  if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
+  EL_TRY(check_dense(fn, demb, true, "demb"));
+  const size_t need = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, nullptr).bytes;
+  if (need > kNoallocScratchBytes) {
+    char buf[200];
+    std::snprintf(buf, sizeof buf, "%s: %zu bytes of scratch needed, the library's static scratch holds %zu",
+                  fn, need, kNoallocScratchBytes);
+    return set_error(EL_ERR_WORKSPACE, buf);
+  }
+  void* scratch_ptr = nullptr;
+  EL_TRY(noalloc_scratch(fn, &scratch_ptr));
+  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, scratch_ptr);
   uint32_t *keys = nullptr, *vals = nullptr;
   EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
   return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);

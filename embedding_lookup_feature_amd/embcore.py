@@ -20,6 +20,7 @@ EL_F32, EL_F16, EL_BF16 = 0, 1, 2
 EL_FLAG_HASH_INDICES = 1
 EL_ACT_NONE, EL_ACT_RELU = 0, 1
 EL_LINEAR_DX_RELU_MASK = 1
+EL_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/embcore.h
 
 _DTYPE = {torch.float32: EL_F32, torch.float16: EL_F16, torch.bfloat16: EL_BF16}
 
@@ -62,6 +63,7 @@ def lib() -> ctypes.CDLL:
         L.emb_grad_workspace_bytes.argtypes = [T, Bg]
         L.emb_grad_workspace_bytes.restype = ctypes.c_size_t
         L.emb_grad_reduce_update.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
+        L.emb_grad_reduce_update_noalloc.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp]
         L.emb_grad_prepare.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp]
         L.emb_grad_apply.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
         L.emb_grad_sort.argtypes = [T, Bg, u32, vp, ctypes.c_size_t, vp, vp, vp, vp, vp, vp]
@@ -80,7 +82,8 @@ def lib() -> ctypes.CDLL:
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
         for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
-                     "emb_grad_reduce_update", "emb_grad_prepare", "emb_grad_apply",
+                     "emb_grad_reduce_update", "emb_grad_reduce_update_noalloc",
+                     "emb_grad_prepare", "emb_grad_apply",
                      "emb_grad_sort", "el_validate_bags", "el_linear_fwd", "el_linear_bwd",
                      "el_relu_bwd", "el_bce_logits", "el_sgd_dense"):
             getattr(L, name).restype = ctypes.c_int
@@ -234,6 +237,16 @@ def emb_grad_reduce_update(tables: Tables, bags: Bags, demb: torch.Tensor, lr: f
     _check(lib().emb_grad_reduce_update(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
                                         _dev(demb, "demb"), _dtype(demb, "demb"), float(lr),
                                         _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def emb_grad_reduce_update_noalloc(tables: Tables, bags: Bags, demb: torch.Tensor, lr: float,
+                                   hash_indices=False, stream=None):
+    """emb_grad_reduce_update with the library's static per-GPU scratch as workspace (for
+    callers that cannot allocate); workspaces above EL_NOALLOC_SCRATCH_BYTES are refused."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_grad_reduce_update_noalloc(ctypes.byref(tables.c), ctypes.byref(bags.c), flags,
+                                                _dev(demb, "demb"), _dtype(demb, "demb"), float(lr),
+                                                _stream(stream)))
 
 
 def emb_grad_prepare(tables: Tables, bags: Bags, workspace: torch.Tensor, hash_indices=False,

@@ -171,6 +171,25 @@ EL_API el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bag
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * emb_grad_reduce_update for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation, bit for bit, with the workspace taken from a static scratch array that the
+ * library holds on every GPU it runs on (EL_NOALLOC_SCRATCH_BYTES per GPU, kept until the
+ * process ends) instead of a caller-provided buffer.  The caller still passes the tables,
+ * the bags and demb as for emb_grad_reduce_update.  A call whose workspace would exceed
+ * the scratch (emb_grad_workspace_bytes(tab, bags) > EL_NOALLOC_SCRATCH_BYTES) returns
+ * EL_ERR_WORKSPACE and enqueues nothing.  The call allocates nothing: no hipMalloc or
+ * hipFree, no allocating library routine.  Nothing in the scratch needs clearing: every
+ * byte a call reads it has written first.  All calls on one GPU share that GPU's scratch, so
+ * two calls that may overlap on one GPU (other streams, other threads) race; the caller
+ * orders them.
+ */
+#define EL_NOALLOC_SCRATCH_BYTES (64u << 20)
+EL_API el_status emb_grad_reduce_update_noalloc(const el_tables* tab, const el_bags* bags,
+                                                uint32_t flags, const void* demb,
+                                                el_dtype grad_dtype, float lr, hipStream_t stream);
+
+/*
  * emb_grad_reduce_update in two halves, so that the sort -- which depends only on the
  * lookups -- can run on another stream while the forward and the interaction backward
  * produce demb:

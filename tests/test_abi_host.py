@@ -28,7 +28,8 @@ def test_library_loads_and_exports_every_declared_function():
     L = ec.lib()
     names = ec.header_functions()
     assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
-                          "emb_grad_workspace_bytes", "emb_grad_reduce_update", "emb_grad_prepare",
+                          "emb_grad_workspace_bytes", "emb_grad_reduce_update",
+                          "emb_grad_reduce_update_noalloc", "emb_grad_prepare",
                           "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
                           "el_linear_bwd_workspace_bytes", "el_linear_bwd", "el_relu_bwd",
@@ -157,6 +158,23 @@ def test_grad_calls_reject_small_or_missing_workspace():
     assert L.emb_grad_sort(ref(t), ref(b), 0, A, 16, A, A, A, A, A, None) == WORKSPACE
     assert L.el_validate_bags(ref(t), ref(b), 0, 0, None) == INVALID
     assert L.el_validate_bags(ref(t), ref(b), 0, A + 4, None) == INVALID
+
+
+def test_noalloc_update_refuses_workspaces_beyond_its_scratch_on_the_host():
+    """The no-alloc update checks its arguments and the workspace it would need against the
+    static scratch before touching a GPU."""
+    L = ec.lib()
+    lr = ctypes.c_float(0.01)
+    t, b = tables(), bags()  # 26 x 65536 lookups of 128-wide rows: above the scratch
+    need = L.emb_grad_workspace_bytes(ref(t), ref(b))
+    assert need > ec.EL_NOALLOC_SCRATCH_BYTES
+    assert L.emb_grad_reduce_update_noalloc(ref(t), ref(b), 0, A, ec.EL_BF16, lr, None) == WORKSPACE
+    assert "emb_grad_reduce_update_noalloc" in ec.el_last_error() and "scratch" in ec.el_last_error()
+    assert L.emb_grad_reduce_update_noalloc(None, ref(b), 0, A, ec.EL_BF16, lr, None) == INVALID
+    assert L.emb_grad_reduce_update_noalloc(ref(t), ref(b), 2, A, ec.EL_BF16, lr, None) == INVALID
+    assert L.emb_grad_reduce_update_noalloc(ref(t), ref(b), 0, A, 7, lr, None) == INVALID
+    assert L.emb_grad_reduce_update_noalloc(ref(t), ref(b), 0, A + 8, ec.EL_BF16, lr, None) == INVALID
+    assert L.emb_grad_reduce_update_noalloc(ref(t), ref(bags(B=0, nnz=0)), 0, A, ec.EL_BF16, lr, None) == ec.EL_OK
 
 
 def test_table_row_limits():
