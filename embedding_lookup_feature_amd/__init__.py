@@ -9,12 +9,15 @@ from .embcore import (  # noqa: F401
     EmbcoreError,
     Tables,
     alloc_workspace,
+    cat_interact_bwd,
+    cat_interact_fwd,
     dot_interact_bwd,
     dot_interact_fwd,
     el_last_error,
     el_validate_bags,
     el_version,
     emb_bag_fwd,
+    emb_cat_fwd,
     emb_dot_bwd,
     emb_dot_fwd,
     emb_grad_apply,

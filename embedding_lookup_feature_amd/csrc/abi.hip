@@ -81,6 +81,18 @@ el_status check_interaction(const char* fn, int32_t B, int32_t F, int32_t D, int
   return EL_OK;
 }
 
+el_status check_cat(const char* fn, int32_t B, int32_t F, int32_t D, int32_t out_stride, el_dtype a,
+                    el_dtype b) {
+  if (B < 0) return bad(fn, "B must be >= 0");
+  if (F < 1) return bad(fn, "F must be >= 1");
+  if (D < 1) return bad(fn, "D must be >= 1");
+  if (!dtype_valid(a) || !dtype_valid(b)) return bad(fn, "unknown dtype");
+  const int64_t VD = (static_cast<int64_t>(F) + 1) * D;
+  if (VD >= (1LL << 31)) return bad(fn, "(F+1) * D must be < 2^31");
+  if (static_cast<int64_t>(out_stride) < VD) return bad(fn, "out_stride < (F+1) * D");
+  return EL_OK;
+}
+
 // Scratch of emb_grad_reduce_update_noalloc (for callers that cannot allocate): one
 // file-scope device array, of which every GPU the library runs on holds its own copy until
 // the process ends.  In host code `scratch` only names the symbol; its device address on
@@ -219,6 +231,44 @@ el_status emb_dot_bwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
   if (B == 0) return EL_OK;
   return launch_emb_dot_bwd(*tab, *bags, flags, x0, act_dtype, dout, out_stride, dx0, demb,
                             grad_dtype, stream);
+}
+
+el_status cat_interact_fwd(const void* x0, const void* emb, el_dtype in_dtype, int32_t B, int32_t F,
+                           int32_t D, void* out, el_dtype out_dtype, int32_t out_stride,
+                           hipStream_t stream) {
+  const char* fn = "cat_interact_fwd";
+  EL_TRY(check_cat(fn, B, F, D, out_stride, in_dtype, out_dtype));
+  EL_TRY(check_dense(fn, x0, B > 0, "x0"));
+  EL_TRY(check_dense(fn, emb, B > 0, "emb"));
+  EL_TRY(check_dense(fn, out, B > 0, "out"));
+  if (B == 0) return EL_OK;
+  return launch_cat_fwd(x0, emb, in_dtype, B, F, D, out, out_dtype, out_stride, stream);
+}
+
+el_status cat_interact_bwd(const void* dout, el_dtype dout_dtype, int32_t B, int32_t F, int32_t D,
+                           int32_t out_stride, void* dx0, void* demb, el_dtype grad_dtype,
+                           hipStream_t stream) {
+  const char* fn = "cat_interact_bwd";
+  EL_TRY(check_cat(fn, B, F, D, out_stride, dout_dtype, grad_dtype));
+  EL_TRY(check_dense(fn, dout, B > 0, "dout"));
+  EL_TRY(check_dense(fn, dx0, B > 0, "dx0"));
+  EL_TRY(check_dense(fn, demb, B > 0, "demb"));
+  if (B == 0) return EL_OK;
+  return launch_cat_bwd(dout, dout_dtype, B, F, D, out_stride, dx0, demb, grad_dtype, stream);
+}
+
+el_status emb_cat_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags, const void* x0,
+                      el_dtype act_dtype, void* out, int32_t out_stride, hipStream_t stream) {
+  const char* fn = "emb_cat_fwd";
+  EL_TRY(check_tables(tab, fn));
+  EL_TRY(check_bags(tab, bags, fn));
+  if (flags & ~static_cast<uint32_t>(EL_FLAG_HASH_INDICES)) return bad(fn, "unknown flags");
+  const int32_t B = bags->batch;
+  EL_TRY(check_cat(fn, B, tab->num_tables, tab->dim, out_stride, act_dtype, act_dtype));
+  EL_TRY(check_dense(fn, x0, B > 0, "x0"));
+  EL_TRY(check_dense(fn, out, B > 0, "out"));
+  if (B == 0) return EL_OK;
+  return launch_emb_cat_fwd(*tab, *bags, flags, x0, act_dtype, out, out_stride, stream);
 }
 
 size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags) {

@@ -116,10 +116,11 @@ inline bool dtype_valid(int d) { return d == EL_F32 || d == EL_F16 || d == EL_BF
 // ---------------------------------------------------------------------------------------
 // Launchers (validated arguments only).
 // ---------------------------------------------------------------------------------------
-// Samples [b0, b0 + Bc) only (Bc < 0: all B); `out` is the whole [B][F][D] array.
+// Samples [b0, b0 + Bc) only (Bc < 0: all B).  Pooled vector (b, t) goes to element
+// b * ostride + ocol + t * D of `out` (ostride < 0: the [B][F][D] array, F * D, ocol 0).
 el_status launch_emb_bag_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
                              void* out, el_dtype out_dtype, hipStream_t stream, int b0 = 0,
-                             int Bc = -1);
+                             int Bc = -1, int64_t ostride = -1, int ocol = 0);
 
 el_status launch_dot_fwd(const void* x0, const void* emb, el_dtype in_dtype, int B, int F, int D,
                          void* out, el_dtype out_dtype, int out_stride, hipStream_t stream);
@@ -189,6 +190,15 @@ int resident_grid(const void* kernel, int B, size_t lds_bytes, int block);
 el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
                              const void* x0, el_dtype act_dtype, void* emb_out, void* out,
                              int out_stride, hipStream_t stream);
+
+// The cat interaction (vectors side by side) and its fused form with the gather.
+el_status launch_cat_fwd(const void* x0, const void* emb, el_dtype in_dtype, int B, int F, int D,
+                         void* out, el_dtype out_dtype, int out_stride, hipStream_t stream);
+el_status launch_cat_bwd(const void* dout, el_dtype dout_dtype, int B, int F, int D, int out_stride,
+                         void* dx0, void* demb, el_dtype grad_dtype, hipStream_t stream);
+el_status launch_emb_cat_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, void* out, int out_stride,
+                             hipStream_t stream);
 
 el_status launch_validate(const el_tables& tab, const el_bags& bags, uint32_t flags,
                           int64_t* bad_count, hipStream_t stream);

@@ -14,7 +14,9 @@
 //   2. every group issues the first-row loads of its U bags back to back, so U row loads
 //      per lane are in flight (for hotness-1 bags this is the whole gather); later entries
 //      of multi-hot bags follow in ascending CSR order, 4 loads in flight;
-//   3. all NB pooled rows are stored at the end.
+//   3. all NB pooled rows are stored at the end, pooled vector (b, t) at element
+//      b * ostride + ocol + t * D of the output (the [B][F][D] array: ostride = F*D,
+//      ocol = 0; the cat interaction's output rows: ostride = out_stride, ocol = D).
 // A wave never waits for its own stores (on this architecture loads and stores share one
 // completion counter), and a new wave takes its slot as soon as it is done.  Sums are fp32
 // in CSR order and rounded once to the output type, so a hotness-1 gather returns the row
@@ -36,8 +38,8 @@ template <class TT, class OT, int L, int NVL>
 __global__ __launch_bounds__(256) void k_emb_bag_fwd(
     const typename TT::S* __restrict__ W, const int64_t* __restrict__ row_off,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ off, int32_t B, int32_t F,
-    int32_t D, int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int32_t nbags,
-    int32_t b0, int32_t Bc) {
+    int32_t D, int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int64_t ostride,
+    int32_t ocol, int32_t nbags, int32_t b0, int32_t Bc) {
   constexpr int E = epv<TT>();
   constexpr int NG = 64 / L;                  // bag groups per wave
   constexpr int U = bags_per_group<L, NVL>();  // bags per group
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
     const int bi = u * NG + grp;
     const int tb = __shfl(t, bi), bb = __shfl(b, bi);
     if (tb >= 0) {
-      typename OT::S* dst = out + (static_cast<int64_t>(bb) * F + tb) * D;
+      typename OT::S* dst = out + static_cast<int64_t>(bb) * ostride + ocol + static_cast<int64_t>(tb) * D;
 #pragma unroll
       for (int m = 0; m < NVL; ++m) {
         const int c = gl + m * L;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
 
 template <class TT, class OT, int L, int NVL>
 el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                   int nvec, int b0, int Bc, hipStream_t stream) {
+                   int64_t ostride, int ocol, int nvec, int b0, int Bc, hipStream_t stream) {
   constexpr int NB = (64 / L) * bags_per_group<L, NVL>();
   const int64_t nbags = static_cast<int64_t>(tab.num_tables) * Bc;
   const int64_t waves = (nbags + NB - 1) / NB;
@@ -157,33 +159,34 @@ el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, vo
                      static_cast<const typename TT::S*>(tab.base), tab.row_offset, bags.indices,
                      bags.offsets, bags.batch, tab.num_tables, tab.dim, nvec,
                      (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
-                     static_cast<typename OT::S*>(out), static_cast<int32_t>(nbags), b0, Bc);
+                     static_cast<typename OT::S*>(out), ostride, ocol, static_cast<int32_t>(nbags), b0, Bc);
   return check_launch("emb_bag_fwd");
 }
 
 template <class TT, class OT>
 el_status dispatch_shape(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                         int b0, int Bc, hipStream_t stream) {
+                         int64_t ostride, int ocol, int b0, int Bc, hipStream_t stream) {
   const int nvec = static_cast<int>(tab.dim * sizeof(typename TT::S) / 16);
-  if (nvec <= 1) return launch_t<TT, OT, 1, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 2) return launch_t<TT, OT, 2, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 4) return launch_t<TT, OT, 4, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 8) return launch_t<TT, OT, 8, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 16) return launch_t<TT, OT, 16, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 32) return launch_t<TT, OT, 32, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 64) return launch_t<TT, OT, 64, 1>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 128) return launch_t<TT, OT, 64, 2>(tab, bags, flags, out, nvec, b0, Bc, stream);
-  if (nvec <= 256) return launch_t<TT, OT, 64, 4>(tab, bags, flags, out, nvec, b0, Bc, stream);
+  if (nvec <= 1) return launch_t<TT, OT, 1, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 2) return launch_t<TT, OT, 2, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 4) return launch_t<TT, OT, 4, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 8) return launch_t<TT, OT, 8, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 16) return launch_t<TT, OT, 16, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 32) return launch_t<TT, OT, 32, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 64) return launch_t<TT, OT, 64, 1>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 128) return launch_t<TT, OT, 64, 2>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
+  if (nvec <= 256) return launch_t<TT, OT, 64, 4>(tab, bags, flags, out, ostride, ocol, nvec, b0, Bc, stream);
   return set_error(EL_ERR_UNSUPPORTED, "emb_bag_fwd: rows longer than 4096 bytes are not supported");
 }
 
 template <class TT>
 el_status dispatch_out(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                       el_dtype out_dtype, int b0, int Bc, hipStream_t stream) {
+                       el_dtype out_dtype, int64_t ostride, int ocol, int b0, int Bc,
+                       hipStream_t stream) {
   switch (out_dtype) {
-    case EL_F32: return dispatch_shape<TT, F32T>(tab, bags, flags, out, b0, Bc, stream);
-    case EL_F16: return dispatch_shape<TT, F16T>(tab, bags, flags, out, b0, Bc, stream);
-    case EL_BF16: return dispatch_shape<TT, BF16T>(tab, bags, flags, out, b0, Bc, stream);
+    case EL_F32: return dispatch_shape<TT, F32T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
+    case EL_F16: return dispatch_shape<TT, F16T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
+    case EL_BF16: return dispatch_shape<TT, BF16T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown output dtype");
 }
@@ -191,12 +194,14 @@ el_status dispatch_out(const el_tables& tab, const el_bags& bags, uint32_t flags
 }  // namespace
 
 el_status launch_emb_bag_fwd(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
-                             el_dtype out_dtype, hipStream_t stream, int b0, int Bc) {
+                             el_dtype out_dtype, hipStream_t stream, int b0, int Bc,
+                             int64_t ostride, int ocol) {
   if (Bc < 0) Bc = bags.batch;
+  if (ostride < 0) ostride = static_cast<int64_t>(tab.num_tables) * tab.dim;
   switch (tab.dtype) {
-    case EL_F32: return dispatch_out<F32T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
-    case EL_F16: return dispatch_out<F16T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
-    case EL_BF16: return dispatch_out<BF16T>(tab, bags, flags, out, out_dtype, b0, Bc, stream);
+    case EL_F32: return dispatch_out<F32T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
+    case EL_F16: return dispatch_out<F16T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
+    case EL_BF16: return dispatch_out<BF16T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown table dtype");
 }

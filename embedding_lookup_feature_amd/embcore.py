@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.emb_dot_bwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp, i32, vp, vp, ctypes.c_int, vp]
         L.dot_interact_bwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32,
                                        vp, vp, ctypes.c_int, vp]
+        L.cat_interact_fwd.argtypes = [vp, vp, ctypes.c_int, i32, i32, i32, vp, ctypes.c_int, i32, vp]
+        L.cat_interact_bwd.argtypes = [vp, ctypes.c_int, i32, i32, i32, i32, vp, vp, ctypes.c_int, vp]
+        L.emb_cat_fwd.argtypes = [T, Bg, u32, vp, ctypes.c_int, vp, i32, vp]
         L.emb_grad_workspace_bytes.argtypes = [T, Bg]
         L.emb_grad_workspace_bytes.restype = ctypes.c_size_t
         L.emb_grad_reduce_update.argtypes = [T, Bg, u32, vp, ctypes.c_int, f32, vp, ctypes.c_size_t, vp]
@@ -82,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
         for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
+                     "cat_interact_fwd", "cat_interact_bwd", "emb_cat_fwd",
                      "emb_grad_reduce_update", "emb_grad_reduce_update_noalloc",
                      "emb_grad_prepare", "emb_grad_apply",
                      "emb_grad_sort", "el_validate_bags", "el_linear_fwd", "el_linear_bwd",
@@ -228,6 +232,32 @@ def alloc_workspace(tables: Tables, bags: Bags, device=None) -> torch.Tensor:
     """A byte tensor large enough for the gradient path (torch allocations are 256-aligned)."""
     n = max(emb_grad_workspace_bytes(tables, bags), 256)
     return torch.empty(n, dtype=torch.uint8, device=device or tables.weight.device)
+
+
+def cat_interact_fwd(x0: torch.Tensor, emb: torch.Tensor, out: torch.Tensor, stream=None):
+    """--interaction_op cat: out[b] = [x0[b] | emb[b][0] | ... | emb[b][F-1] | 0 pad]."""
+    B, F, D = emb.shape
+    _check(lib().cat_interact_fwd(_dev(x0, "x0"), _dev(emb, "emb"), _dtype(emb, "emb"), B, F, D,
+                                  _dev(out, "out"), _dtype(out, "out"), out.shape[1], _stream(stream)))
+    return out
+
+
+def cat_interact_bwd(dout: torch.Tensor, dx0: torch.Tensor, demb: torch.Tensor, stream=None):
+    """Gradients of the cat interaction: dx0 = dout[:, :D], demb[:, t] = dout[:, D(1+t):D(2+t)]."""
+    B, F, D = demb.shape
+    _check(lib().cat_interact_bwd(_dev(dout, "dout"), _dtype(dout, "dout"), B, F, D, dout.shape[1],
+                                  _dev(dx0, "dx0"), _dev(demb, "demb"), _dtype(demb, "demb"),
+                                  _stream(stream)))
+
+
+def emb_cat_fwd(tables: Tables, bags: Bags, x0: torch.Tensor, out: torch.Tensor, hash_indices=False,
+                stream=None):
+    """emb_bag_fwd + cat_interact_fwd in one call: pooled vectors written straight into their
+    blocks of the output rows."""
+    flags = EL_FLAG_HASH_INDICES if hash_indices else 0
+    _check(lib().emb_cat_fwd(ctypes.byref(tables.c), ctypes.byref(bags.c), flags, _dev(x0, "x0"),
+                             _dtype(x0, "x0"), _dev(out, "out"), out.shape[1], _stream(stream)))
+    return out
 
 
 def emb_grad_reduce_update(tables: Tables, bags: Bags, demb: torch.Tensor, lr: float,

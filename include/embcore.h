@@ -151,6 +151,43 @@ EL_API el_status emb_dot_bwd(const el_tables* tab, const el_bags* bags, uint32_t
                              int32_t out_stride, void* dx0, void* demb, el_dtype grad_dtype,
                              hipStream_t stream);
 
+/*
+ * The "cat" interaction (same page, §Command-line options, --interaction_op cat): the
+ * sample's V = F+1 vectors side by side instead of their pairwise dot products,
+ *   out[b] = [ x0[b] | emb[b][0] | ... | emb[b][F-1] | +0 pad ]   (V*D values, then zeros)
+ * The bottom-MLP output the model concatenates with the interaction output is the first
+ * block itself (it appears once).  x0: [B][D], emb: [B][F][D] of in_dtype; out:
+ * [B][out_stride] of out_dtype, out_stride >= (F+1)*D; one rounding per value (equal dtypes
+ * copy bits).  All base pointers 16-byte aligned.
+ */
+EL_API el_status cat_interact_fwd(const void* x0, const void* emb, el_dtype in_dtype, int32_t B,
+                                  int32_t F, int32_t D, void* out, el_dtype out_dtype,
+                                  int32_t out_stride, hipStream_t stream);
+
+/*
+ * Backward of the cat interaction: every vector's gradient is its own block of the upstream
+ * gradient G = dout[b]:  dx0[b] = G[0:D),  demb[b][t] = G[D(1+t) : D(2+t)).  Columns
+ * [(F+1)*D, out_stride) of dout are ignored.  dout: [B][out_stride] of dout_dtype; dx0:
+ * [B][D], demb: [B][F][D] of grad_dtype; 16-byte aligned.
+ */
+EL_API el_status cat_interact_bwd(const void* dout, el_dtype dout_dtype, int32_t B, int32_t F,
+                                  int32_t D, int32_t out_stride, void* dx0, void* demb,
+                                  el_dtype grad_dtype, hipStream_t stream);
+
+/*
+ * emb_bag_fwd and cat_interact_fwd in one call: the same bits as
+ *   emb_bag_fwd(tab, bags, flags, emb, act_dtype);
+ *   cat_interact_fwd(x0, emb, act_dtype, B, F, D, out, act_dtype, out_stride);
+ * with B = bags->batch, F = tab->num_tables, D = tab->dim, but each pooled vector is written
+ * straight into its block of the output row (the pooled vectors are not stored anywhere
+ * else).  x0: [B][D], out: [B][out_stride] of act_dtype, out_stride >= (F+1)*D;
+ * D * sizeof(act_dtype) and out_stride * sizeof(act_dtype) multiples of 16 bytes (else
+ * EL_ERR_UNSUPPORTED, nothing enqueued); 16-byte aligned.
+ */
+EL_API el_status emb_cat_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
+                             const void* x0, el_dtype act_dtype, void* out, int32_t out_stride,
+                             hipStream_t stream);
+
 /* [host, pure] Bytes of device workspace that emb_grad_reduce_update and emb_grad_sort
  * need for these tables and bags (0 when nnz == 0).  Returns 0 for invalid arguments. */
 EL_API size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags);

@@ -30,6 +30,7 @@ def test_library_loads_and_exports_every_declared_function():
     assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
                           "emb_grad_workspace_bytes", "emb_grad_reduce_update",
                           "emb_grad_reduce_update_noalloc", "emb_grad_prepare",
+                          "cat_interact_fwd", "cat_interact_bwd", "emb_cat_fwd",
                           "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
                           "el_linear_bwd_workspace_bytes", "el_linear_bwd", "el_relu_bwd",
@@ -143,6 +144,32 @@ def test_dot_interact_rejects():
     assert L.dot_interact_bwd(A, A, ec.EL_BF16, 8, 26, 128, A, ec.EL_BF16, 400, A, A, ec.EL_BF16, None) == INVALID
     assert L.dot_interact_bwd(A, A, ec.EL_BF16, 8, 26, 128, A, ec.EL_BF16, 480, 0, A, ec.EL_BF16, None) == INVALID
     assert "dot_interact_bwd" in ec.el_last_error()
+
+
+def test_cat_calls_reject_on_the_host():
+    L = ec.lib()
+    bf = ec.EL_BF16
+    # out_stride below (F+1) * D
+    assert L.cat_interact_fwd(A, A, bf, 8, 26, 128, A, bf, 27 * 128 - 1, None) == INVALID
+    assert L.cat_interact_fwd(A, A, bf, 8, 0, 128, A, bf, 27 * 128, None) == INVALID
+    assert L.cat_interact_fwd(A + 2, A, bf, 8, 26, 128, A, bf, 27 * 128, None) == INVALID
+    assert L.cat_interact_fwd(A, A, 5, 8, 26, 128, A, bf, 27 * 128, None) == INVALID
+    assert L.cat_interact_fwd(A, A, bf, -1, 26, 128, A, bf, 27 * 128, None) == INVALID
+    assert "cat_interact_fwd" in ec.el_last_error()
+    assert L.cat_interact_fwd(A, A, bf, 0, 26, 128, A, bf, 27 * 128, None) == ec.EL_OK
+    assert L.cat_interact_bwd(A, bf, 8, 26, 128, 27 * 128 - 8, A, A, bf, None) == INVALID
+    assert L.cat_interact_bwd(A, bf, 8, 26, 128, 27 * 128, 0, A, bf, None) == INVALID
+    assert L.cat_interact_bwd(A, bf, 8, 26, 128, 27 * 128, A, A + 4, bf, None) == INVALID
+    assert "cat_interact_bwd" in ec.el_last_error()
+    T, Bg = ref(tables()), ref(bags())
+    assert L.emb_cat_fwd(T, Bg, 0, A, bf, A, 27 * 128 - 1, None) == INVALID
+    assert L.emb_cat_fwd(T, Bg, 2, A, bf, A, 27 * 128, None) == INVALID
+    assert L.emb_cat_fwd(T, Bg, 0, 0, bf, A, 27 * 128, None) == INVALID
+    assert L.emb_cat_fwd(None, Bg, 0, A, bf, A, 27 * 128, None) == INVALID
+    # a row stride that is not a multiple of 16 bytes: refused before anything is enqueued
+    assert L.emb_cat_fwd(T, Bg, 0, A, bf, A, 27 * 128 + 3, None) == UNSUPPORTED
+    assert "emb_cat_fwd" in ec.el_last_error()
+    assert L.emb_cat_fwd(T, ref(bags(B=0, nnz=0)), 0, A, bf, A, 27 * 128, None) == ec.EL_OK
 
 
 def test_grad_calls_reject_small_or_missing_workspace():

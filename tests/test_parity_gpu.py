@@ -294,6 +294,96 @@ def test_emb_dot_bwd_refuses_shapes_outside_the_fused_kernel():
         elf.emb_dot_bwd(elf.Tables(W, ro), elf.Bags(idx, off, 16), x0, dout, dx0, demb)
 
 
+CAT_CASES = [
+    # label, F, D, in dtype, out dtype, out_stride (None = (F+1)*D padded to 16 bytes), B
+    ("bf16-27x128", 26, 128, "bf16", "bf16", None, 1000),
+    ("f32-tiny", 8, 16, "f32", "f32", None, 300),
+    ("f32-in-bf16-out", 26, 128, "f32", "bf16", None, 200),
+    ("bf16-in-f32-out", 5, 64, "bf16", "f32", None, 100),
+    ("f16-101x64", 100, 64, "f16", "f16", None, 60),
+    ("bf16-padded-stride", 3, 32, "bf16", "bf16", 4 * 32 + 24, 77),
+    ("bf16-d12-element-path", 4, 12, "bf16", "bf16", None, 50),
+    ("f32-odd-stride-element-path", 2, 8, "f32", "bf16", 3 * 8 + 3, 33),
+]
+
+
+def cat_stride(F, D, dt, stride):
+    if stride is not None:
+        return stride
+    per = 16 // (4 if dt == "f32" else 2)
+    return ((F + 1) * D + per - 1) // per * per
+
+
+@pytest.mark.parametrize("case", CAT_CASES, ids=[c[0] for c in CAT_CASES])
+def test_cat_interact_fwd_matches_oracle(case):
+    label, F, D, idt, odt, stride, B = case
+    wl, x0, emb, _ = dot_inputs(F, D, idt, B, None)
+    stride = cat_stride(F, D, odt, stride)
+    out = torch.full((B, stride), float("nan"), dtype=synth.torch_dtype(odt), device=DEV)
+    elf.cat_interact_fwd(x0, emb, out)
+    torch.cuda.synchronize()
+    ref = orc.cat_interact_fwd(to_np(x0), to_np(emb), idt, odt, stride)
+    assert_bits(out, ref, label)  # copies and single roundings: bit for bit
+
+
+@pytest.mark.parametrize("case", CAT_CASES, ids=[c[0] for c in CAT_CASES])
+def test_cat_interact_bwd_matches_oracle(case):
+    label, F, D, ddt, gdt, stride, B = case
+    wl = base_wl(batch=B, rows=(10,) * F, dim=D, act_dtype=ddt)
+    stride = cat_stride(F, D, ddt, stride)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(synth.seed_for(label, "cat-dout"))
+    dout = torch.randn((B, stride), generator=g, device=DEV).to(synth.torch_dtype(ddt))
+    dout[:, (F + 1) * D:] = 1e3  # padding columns must be ignored
+    gt = synth.torch_dtype(gdt)
+    dx0 = torch.full((B, D), float("nan"), dtype=gt, device=DEV)
+    demb = torch.full((B, F, D), float("nan"), dtype=gt, device=DEV)
+    elf.cat_interact_bwd(dout, dx0, demb)
+    torch.cuda.synchronize()
+    rdx0, rdemb = orc.cat_interact_bwd(to_np(dout), ddt, F, D, gdt)
+    assert_bits(dx0, rdx0, label + " dx0")
+    assert_bits(demb, rdemb, label + " demb")
+
+
+EMB_CAT_CASES = [
+    # label, rows, D, table dtype, act dtype, bag, index dist, hash, B, extra stride
+    ("f32-bf16-26x128-zipf", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 1000, 0),
+    ("f16-ragged-tables", (3, 70000, 1234), 128, "f16", "f16", ("one",), "zipf", False, 1500, 8),
+    ("bf16-d64-multihot", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300, 0),
+    ("f32-f32-d16-empty-bags", (500,) * 5, 16, "f32", "f32", ("poisson", 3.0, 0, 10), "uniform", False, 333, 4),
+    ("f32-f16-hash", (999, 7, 5000), 32, "f32", "f16", ("one",), "uniform", True, 400, 0),
+]
+
+
+@pytest.mark.parametrize("case", EMB_CAT_CASES, ids=[c[0] for c in EMB_CAT_CASES])
+def test_emb_cat_fwd_matches_separate_calls_and_oracle(case):
+    label, rows, D, tdt, adt, bag, dist, hsh, B, extra = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=adt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag, bottom_mlp=(13, 64, D))
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    x0 = synth.make_x0(wl, DEV)
+    at = synth.torch_dtype(adt)
+    F = wl.num_tables
+    S = cat_stride(F, D, adt, None) + extra
+    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+    emb = torch.full((B, F, D), float("nan"), dtype=at, device=DEV)
+    out_sep = torch.full((B, S), float("nan"), dtype=at, device=DEV)
+    elf.emb_bag_fwd(tab, bags, emb, hash_indices=hsh)
+    elf.cat_interact_fwd(x0, emb, out_sep)
+    out = torch.full((B, S), float("nan"), dtype=at, device=DEV)
+    elf.emb_cat_fwd(tab, bags, x0, out, hash_indices=hsh)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out_sep.view(torch.uint8)), label + ": differs from the two calls"
+    emb_ref = orc.emb_bag_fwd(to_np(W), tdt, to_np(ro), to_np(idx), to_np(off), B, D, adt, hash_indices=hsh)
+    out_ref = orc.cat_interact_fwd(to_np(x0), emb_ref, adt, adt, S)
+    if bag == ("one",):
+        assert_bits(out, out_ref, label)
+    else:
+        assert_bits(out[:, :D], out_ref[:, :D], label + " x0 block")
+        assert_close(out[:, D:(F + 1) * D], out_ref[:, D:(F + 1) * D], adt, label + " pooled blocks")
+        assert_bits(out[:, (F + 1) * D:], out_ref[:, (F + 1) * D:], label + " padding")
+
+
 SORT_CASES = [
     # label, rows, D, table dtype, grad dtype, bag, dist, hash, B
     ("hot1-zipf-26x5000", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 777),
