@@ -141,24 +141,70 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def copy_bandwidth(dev, gib=4, reps=3):
-    """Read + write GB/s of a plain device-to-device copy of `gib` GiB (the box's achievable
-    HBM bandwidth for a streaming kernel)."""
+def hbm_calibration(dev, gib=4, reps=5):
+    """GB/s that the library's HBM calibration kernels reach on this GPU: k_copy_calib over
+    `gib` GiB of traffic each (read only, write only, copy, and a 3:1 read/write mix), and
+    k_gather_calib reading distinct random rows of 128 / 256 / 512 bytes (half of a `gib` GiB
+    table) and writing them contiguously (gather_*: reads + writes + indices), writing only
+    their first half (gather_*_write_half: the mix of fp32 rows pooled into 16-bit outputs)
+    or only reading them (gather_read_*).  Each figure is the median of `reps` launches timed with
+    HIP events after one warm-up launch."""
+    import embedding_lookup_feature_amd as elf
+    from embedding_lookup_feature_amd import embcore as ec
     n = gib << 30
-    src = torch.ones(n, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    gbps = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def median_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    res = {}
+    for name, mode in (("read", ec.EL_CALIB_READ), ("write", ec.EL_CALIB_WRITE), ("copy", ec.EL_CALIB_COPY),
+                       ("read3_write1", ec.EL_CALIB_READ3_WRITE1)):
+        res[name] = round(n / (median_ms(lambda: elf.hbm_calib(mode, a, b, n)) * 1e-3) / 1e9, 1)
+    g = torch.Generator(device=dev)
+    g.manual_seed(12345)
+    for rb in (128, 256, 512):
+        rows = n // rb
+        nr = (n // 2) // rb  # distinct random rows, half the table's bytes, read once each
+        idx = torch.randperm(rows, generator=g, device=dev)[:nr].to(torch.int32)
+        ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER, a, b, 0, idx=idx, row_bytes=rb))
+        res[f"gather_{rb}B"] = round((2 * nr * rb + 4 * nr) / (ms * 1e-3) / 1e9, 1)
+        ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER_READ, a, b, 0, idx=idx, row_bytes=rb))
+        res[f"gather_read_{rb}B"] = round((nr * rb + 4 * nr) / (ms * 1e-3) / 1e9, 1)
+        if rb >= 256:  # rows pooled into outputs of half their size (fp32 rows, 16-bit outputs)
+            ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER, a, b, rb // 2, idx=idx, row_bytes=rb))
+            res[f"gather_{rb}B_write_half"] = round((nr * rb * 3 // 2 + 4 * nr) / (ms * 1e-3) / 1e9, 1)
+        del idx
+    del a, b
     torch.cuda.empty_cache()
-    return gbps
+    return res
+
+
+# The calibrated ceiling each call is compared with: the streaming mix closest to its traffic.
+# The gathers are read-mostly, and random rows of these sizes read as fast as a stream
+# (gather_read_* ~ read), so theirs is the streaming read.
+def ceiling_of(call, wl, calib):
+    if not calib:
+        return None, None
+    if call in ("emb_bag_fwd", "emb_dot_fwd", "emb_dot_bwd", "emb_cat_fwd"):
+        key = "read"
+    elif call in ("emb_grad_reduce_update", "emb_grad_apply"):
+        key = "read3_write1"
+    else:  # interaction forward / backward: read and write about equally
+        key = "copy"
+    return key, calib.get(key)
 
 
 def pct(xs, q):
@@ -197,8 +243,12 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs, one per index batch, each capturing one whole "
                          "step (both streams); per-call times still come from eager calls")
-    ap.add_argument("--no-copy-bw", action="store_true",
-                    help="skip the 4 GiB copy that measures the achievable HBM bandwidth")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the HBM calibration kernels (4 GiB each) that measure the bandwidth "
+                         "streaming kernels reach on this GPU")
+    ap.add_argument("--no-uniform-control", action="store_true",
+                    help="skip the no-reuse gather control (emb_bag_fwd on the workload's shapes "
+                         "with every table's lookups distinct rows, so that no row comes from cache)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -363,7 +413,29 @@ def main():
         call_samples["emb_grad_prepare"] = [e[0].elapsed_time(e[1]) for e in sevs]
     call_ms = {n: float(np.mean(v)) for n, v in call_samples.items()}
 
-    copy_gbps = None if args.no_copy_bw else copy_bandwidth(dev)
+    # the gather with no row reuse: emb_bag_fwd alone on the same shapes with every table's
+    # lookups distinct rows (each row read once, so its algorithmic bytes all come from HBM)
+    uniform = None
+    if not args.no_uniform_control and wl.bag == ("one",) and wl.index_dist == "zipf" \
+            and max(wl.batch, 1) <= min(wl.rows):
+        wu = wl.scaled(name=wl.name + "_distinct_control", index_dist="distinct")
+        iu, ou = synth.make_indices(wu, dev)
+        bu = elf.Bags(iu, ou, B)
+        eu = torch.empty((B, F, D), dtype=act, device=dev)
+        for _ in range(3):
+            elf.emb_bag_fwd(tab, bu, eu)
+        torch.cuda.synchronize()
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for e0, e1 in es:
+            e0.record()
+            elf.emb_bag_fwd(tab, bu, eu)
+            e1.record()
+        torch.cuda.synchronize()
+        uniform = float(np.mean([a.elapsed_time(b) for a, b in es]))
+        del iu, ou, bu, eu
+        torch.cuda.empty_cache()
+
+    calib = None if args.no_calib else hbm_calibration(dev)
 
     nnz = batches[0][3].numel()
     algo = algorithmic_bytes(wl, nnz, store_emb)
@@ -386,8 +458,10 @@ def main():
         c = {"ms": round(call_ms[n], 4), "median_ms": round(pct(v, 50), 4),
              "p10_ms": round(pct(v, 10), 4), "p90_ms": round(pct(v, 90), 4),
              "algo_bytes": int(algo[n]), "algo_gbps": round(algo[n] / (call_ms[n] * 1e-3) / 1e9, 1)}
-        if copy_gbps:
-            c["frac_of_copy"] = round(c["algo_gbps"] / copy_gbps, 4)
+        ck, cg = ceiling_of(n, wl, calib)
+        if cg:
+            c["ceiling"] = ck
+            c["frac_of_ceiling"] = round(c["algo_gbps"] / cg, 4)
         if n == "emb_grad_prepare":
             c["stream"] = "side (overlaps " + ("the forward and " if args.overlap_sort == "fwd" else "") + \
                           "the interaction backward)"
@@ -400,12 +474,29 @@ def main():
     dom = max(single, key=lambda n: call_ms[n])
     kernel = kernel_of(dom, wl)
     achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(wl.name, kernel)}
-    if copy_gbps:
-        roofline["copy_gbps"] = round(copy_gbps, 1)
-        roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
+    def roofline_of(call, kernel, ms, nbytes, note=None):
+        a = nbytes / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "kernel": kernel, "call": call, "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,
+             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(wl.name, kernel)}
+        ck, cg = ceiling_of(call, wl, calib)
+        if cg:
+            r.update({"ceiling": ck, "ceiling_gbps": cg, "frac_of_ceiling": round(a / cg, 4)})
+        if note:
+            r["note"] = note
+        return r
+
+    roofline = roofline_of(dom, kernel, call_ms[dom], algo[dom])
+    rooflines = [roofline]
+    upd = "emb_grad_apply" if "emb_grad_apply" in call_ms else (
+        "emb_grad_reduce_update" if "emb_grad_reduce_update" in call_ms else None)
+    if upd:
+        rooflines.append(roofline_of(upd, "k_seg_chunk + k_seg_fixup", call_ms[upd], algo[upd],
+                                     "the update's kernels in sequence; HIP-event time of the call"))
+    if uniform is not None:
+        gb = algorithmic_bytes(wl, nnz)["emb_bag_fwd"]
+        rooflines.append(roofline_of("emb_bag_fwd", "k_emb_bag_fwd", uniform, gb,
+                                     "control on the workload's shapes with every table's lookups distinct "
+                                     "rows (no row reuse), mean of 20 HIP-event timed calls"))
 
     result = {
         "metric": metric_name(wl),
@@ -432,7 +523,10 @@ def main():
         "hbm_gbps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "calls": calls,
         "roofline": roofline,
+        "rooflines": rooflines,
     }
+    if calib:
+        result["hbm_calibration_gbps"] = calib
     if not args.no_cpu_baseline:
         result["cpu_baseline"], omp = cpu_baseline(wl, W, ro, batches[0], args.cpu_seconds)
         if omp:
@@ -700,13 +794,17 @@ def cpu_baseline(wl, W, ro, batch, seconds):
     model, nproc = cpu_info()
     old = os.sched_getaffinity(0)
     os.sched_setaffinity(0, {min(old)})
+    reps = 3
     try:
         probe_n = 256
         dt = run(probe_n)
-        n = int(min(B, max(probe_n, probe_n * seconds / max(dt, 1e-6))))
-        dt = run(n)
+        per_sample = dt / probe_n
+        n = int(min(B, max(probe_n, (seconds / reps) / max(per_sample, 1e-9))))
+        dts = [run(n) for _ in range(reps)]
+        dt = float(np.median(dts))
     finally:
         os.sched_setaffinity(0, old)
+    full_s = dt * B / n
     # the same oracle source built with OpenMP (bags / samples over all host threads; the
     # update stays serial), on the same sample
     from oracle import build as obuild
@@ -714,18 +812,21 @@ def cpu_baseline(wl, W, ro, batch, seconds):
     if os.path.exists(obuild.LIB_OMP):
         prev = orc.use_library(obuild.LIB_OMP)
         try:
-            dt_omp = run(n)
+            dt_omp = float(np.median([run(n) for _ in range(reps)]))
         finally:
             orc.restore_library(prev)
         threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(old)
         omp = {"value": round(n / dt_omp, 1), "unit": "samples/s", "cores": threads,
                "kind": "oracle, OpenMP build (forward and interaction backward threaded)",
-               "sample": f"the same {n} samples, {dt_omp:.1f} s"}
+               "sample": f"the same {n} samples, median of {reps} repetitions of {dt_omp:.1f} s"}
     tables = "full tables" + ("; full-table SGD copy" if wl.backward else "") if full_tables \
         else "only the looked-up rows of the tables"
+    why = "" if n == B else (f"; not the full batch: one full-batch repetition would take about "
+                             f"{full_s:.0f} s single-threaded, beyond the benchmark's few-minute budget")
     res = {"value": round(n / dt, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
            "sample": f"first {n} of {B} samples of batch 0 (all {F} tables, {tables}), "
-                     f"single-threaded C oracle pinned to one core, {dt:.1f} s",
+                     f"single-threaded C oracle pinned to one core, median of {reps} repetitions "
+                     f"of {dt:.1f} s{why}",
            "host_cpu": model, "host_cpus_visible": nproc}
     return res, omp
 

@@ -16,6 +16,7 @@ from .embcore import (  # noqa: F401
     el_last_error,
     el_validate_bags,
     el_version,
+    hbm_calib,
     emb_bag_fwd,
     emb_cat_fwd,
     emb_dot_bwd,

@@ -376,6 +376,28 @@ el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t f
   return launch_validate(*tab, *bags, flags, bad_count, stream);
 }
 
+el_status el_hbm_calib(int32_t mode, const void* src, void* dst, size_t bytes, const int32_t* idx,
+                       int64_t nrows, int32_t row_bytes, hipStream_t stream) {
+  const char* fn = "el_hbm_calib";
+  if (mode < EL_CALIB_READ || mode > EL_CALIB_GATHER_READ) return bad(fn, "unknown mode");
+  EL_TRY(check_dense(fn, dst, true, "dst"));
+  if (mode == EL_CALIB_GATHER || mode == EL_CALIB_GATHER_READ) {
+    EL_TRY(check_dense(fn, src, true, "src"));
+    if (!idx || !aligned(idx, 4)) return bad(fn, "idx must be a non-null 4-byte aligned pointer");
+    if (nrows < 0) return bad(fn, "nrows must be >= 0");
+    if (row_bytes < 16 || row_bytes > 1024 || row_bytes % 16 != 0)
+      return bad(fn, "row_bytes must be a multiple of 16 in [16, 1024]");
+    if (mode == EL_CALIB_GATHER && (bytes % 16 != 0 || bytes > static_cast<size_t>(row_bytes)))
+      return bad(fn, "bytes written per gathered row must be a multiple of 16, at most row_bytes");
+    if (nrows == 0) return EL_OK;
+  } else {
+    if (mode != EL_CALIB_WRITE) EL_TRY(check_dense(fn, src, true, "src"));
+    if (bytes % 64 != 0) return bad(fn, "bytes must be a multiple of 64");
+    if (bytes == 0) return EL_OK;
+  }
+  return launch_hbm_calib(mode, src, dst, bytes, idx, nrows, row_bytes, stream);
+}
+
 const char* el_last_error(void) { return g_last_error.c_str(); }
 
 int el_version(void) { return 200; }

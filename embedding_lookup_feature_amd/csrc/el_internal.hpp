@@ -200,6 +200,9 @@ el_status launch_emb_cat_fwd(const el_tables& tab, const el_bags& bags, uint32_t
                              const void* x0, el_dtype act_dtype, void* out, int out_stride,
                              hipStream_t stream);
 
+el_status launch_hbm_calib(int mode, const void* src, void* dst, size_t bytes, const int32_t* idx,
+                           int64_t nrows, int row_bytes, hipStream_t stream);
+
 el_status launch_validate(const el_tables& tab, const el_bags& bags, uint32_t flags,
                           int64_t* bad_count, hipStream_t stream);
 

@@ -21,6 +21,7 @@ EL_FLAG_HASH_INDICES = 1
 EL_ACT_NONE, EL_ACT_RELU = 0, 1
 EL_LINEAR_DX_RELU_MASK = 1
 EL_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/embcore.h
+EL_CALIB_READ, EL_CALIB_WRITE, EL_CALIB_COPY, EL_CALIB_READ3_WRITE1, EL_CALIB_GATHER, EL_CALIB_GATHER_READ = range(6)
 
 _DTYPE = {torch.float32: EL_F32, torch.float16: EL_F16, torch.bfloat16: EL_BF16}
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.el_bce_workspace_bytes.restype = sz
         L.el_bce_logits.argtypes = [vp, i32, vp, i32, ctypes.c_int, vp, vp, i32, vp, sz, vp]
         L.el_sgd_dense.argtypes = [vp, vp, ctypes.c_int, vp, ctypes.c_int64, f32, vp]
+        L.el_hbm_calib.argtypes = [i32, vp, vp, ctypes.c_size_t, vp, ctypes.c_int64, i32, vp]
+        L.el_hbm_calib.restype = ctypes.c_int
         L.el_last_error.restype = ctypes.c_char_p
         L.el_version.restype = ctypes.c_int
         for name in ("emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
@@ -258,6 +261,16 @@ def emb_cat_fwd(tables: Tables, bags: Bags, x0: torch.Tensor, out: torch.Tensor,
     _check(lib().emb_cat_fwd(ctypes.byref(tables.c), ctypes.byref(bags.c), flags, _dev(x0, "x0"),
                              _dtype(x0, "x0"), _dev(out, "out"), out.shape[1], _stream(stream)))
     return out
+
+
+def hbm_calib(mode: int, src, dst: torch.Tensor, nbytes: int = 0, idx: torch.Tensor = None,
+              row_bytes: int = 0, stream=None):
+    """One HBM calibration kernel (EL_CALIB_*): `nbytes` of streaming traffic, or the rows
+    idx of the table `src` gathered into `dst` (row_bytes each)."""
+    sp = _dev(src, "src") if src is not None else None
+    ip = _dev(idx, "idx") if idx is not None else None
+    nrows = idx.numel() if idx is not None else 0
+    _check(lib().el_hbm_calib(mode, sp, _dev(dst, "dst"), nbytes, ip, nrows, row_bytes, _stream(stream)))
 
 
 def emb_grad_reduce_update(tables: Tables, bags: Bags, demb: torch.Tensor, lr: float,

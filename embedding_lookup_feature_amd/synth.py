@@ -14,7 +14,9 @@ Recipe (all from base seed 12345, the page's --seed default):
   * tables: N(0, 0.01) per element (sigma = 0.01), in the table dtype;
   * indices: per table, uniform over its rows, or truncated Zipf(alpha) over ranks 1..n
     (P(k) ~ k^-alpha, exact inverse CDF) mapped to rows by a seeded affine bijection
-    row = (a * (k - 1) + c) mod n with gcd(a, n) = 1, so hot rows are scattered;
+    row = (a * (k - 1) + c) mod n with gcd(a, n) = 1, so hot rows are scattered; for
+    measurement controls also "distinct": a seeded random permutation of the rows (no row
+    looked up twice while the table has at least as many rows as lookups);
   * bag lengths: 1, or Poisson(mean) clipped to [lo, hi], independently per bag;
   * dense features: exp(N(0, 1)) (log-normal), 13 per sample;
   * x0: bottom MLP with ReLU after every layer, weights and biases U(+-1/sqrt(fan_in));
@@ -57,7 +59,7 @@ class Workload:
     dim: int
     table_dtype: str
     act_dtype: str
-    index_dist: str  # "uniform" or "zipf"
+    index_dist: str  # "uniform", "zipf" or "distinct" (rows without repeats, a measurement control)
     zipf_alpha: float = 0.0
     bag: Tuple = ("one",)  # ("one",) or ("poisson", mean, lo, hi)
     bottom_mlp: Tuple[int, ...] = (13, 512, 256, 128)
@@ -120,14 +122,21 @@ WORKLOADS = {
         bottom_mlp=(13, 64, 16), backward=True,
         description="B=65536, 8 tables x 1000 x 16 fp32 (cache-resident), bf16 activations, "
                     "Zipf(1.05) hotness 1, 9 vectors -> 36 pairs -> 52 padded to 56, fwd+bwd+SGD"),
-    # controls: uniform indices (no reuse, so the gathered bytes all come from HBM)
+    # controls.  Uniform indices still repeat rows (65,536 lookups into a 100,000-row table
+    # touch ~48,000 rows), and a table processed table-major fits in the memory-side cache,
+    # so uniform lookups are partly served from cache; distinct rows are the honest test of
+    # HBM bandwidth: every row is read once, from HBM
     "fwd_core_uniform": Workload(
         "fwd_core_uniform", 65536, (100_000,) * 26, 128, "f32", "bf16", "uniform", backward=False,
-        description="fwd_core shapes with uniform indices (control: no row reuse)"),
+        description="fwd_core shapes with uniform indices (control: less row reuse)"),
+    "fwd_core_distinct": Workload(
+        "fwd_core_distinct", 65536, (100_000,) * 26, 128, "f32", "bf16", "distinct", backward=False,
+        description="fwd_core shapes, each table's lookups distinct rows (control: no row reuse)"),
     "large_table_uniform": Workload(
         "large_table_uniform", 262144, tuple(large_table_rows()), 128, "f16", "f16", "uniform",
         backward=False,
-        description="large_table shapes with uniform indices (control: no row reuse)"),
+        description="large_table shapes with uniform indices (control: row reuse only in the small "
+                    "tables)"),
 }
 
 
@@ -198,6 +207,13 @@ def make_indices(wl: Workload, device, batch_id: int = 0):
         g = _gen(device, wl.name, "indices", t, batch_id)
         if wl.index_dist == "uniform":
             parts.append(torch.randint(0, n, (m,), generator=g, device=device, dtype=torch.int64))
+            continue
+        if wl.index_dist == "distinct":
+            # a seeded random permutation of the table's rows, repeated only if the table has
+            # fewer rows than lookups: no row is read twice, so no cache can serve a lookup
+            reps = (m + n - 1) // n
+            perm = torch.cat([torch.randperm(n, generator=g, device=device) for _ in range(max(reps, 1))])
+            parts.append(perm[:m].to(torch.int64))
             continue
         u = torch.rand((m,), generator=g, device=device, dtype=torch.float64)
         rank = torch.searchsorted(_zipf_cdf(n, wl.zipf_alpha, device), u).clamp_(max=n - 1)  # rank - 1

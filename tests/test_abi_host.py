@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_function():
     assert set(names) == {"emb_bag_fwd", "dot_interact_fwd", "emb_dot_fwd", "dot_interact_bwd", "emb_dot_bwd",
                           "emb_grad_workspace_bytes", "emb_grad_reduce_update",
                           "emb_grad_reduce_update_noalloc", "emb_grad_prepare",
-                          "cat_interact_fwd", "cat_interact_bwd", "emb_cat_fwd",
+                          "cat_interact_fwd", "cat_interact_bwd", "emb_cat_fwd", "el_hbm_calib",
                           "emb_grad_apply", "emb_grad_sort",
                           "el_validate_bags", "el_last_error", "el_version", "el_linear_fwd",
                           "el_linear_bwd_workspace_bytes", "el_linear_bwd", "el_relu_bwd",
@@ -170,6 +170,19 @@ def test_cat_calls_reject_on_the_host():
     assert L.emb_cat_fwd(T, Bg, 0, A, bf, A, 27 * 128 + 3, None) == UNSUPPORTED
     assert "emb_cat_fwd" in ec.el_last_error()
     assert L.emb_cat_fwd(T, ref(bags(B=0, nnz=0)), 0, A, bf, A, 27 * 128, None) == ec.EL_OK
+
+
+def test_hbm_calib_rejects_on_the_host():
+    L = ec.lib()
+    assert L.el_hbm_calib(9, A, A, 1 << 20, None, 0, 0, None) == INVALID
+    assert L.el_hbm_calib(ec.EL_CALIB_COPY, A, A, 100, None, 0, 0, None) == INVALID      # not a multiple of 64
+    assert L.el_hbm_calib(ec.EL_CALIB_COPY, 0, A, 1 << 20, None, 0, 0, None) == INVALID  # null src
+    assert L.el_hbm_calib(ec.EL_CALIB_READ, A, A + 8, 1 << 20, None, 0, 0, None) == INVALID
+    assert L.el_hbm_calib(ec.EL_CALIB_GATHER, A, A, 0, None, 10, 256, None) == INVALID     # null idx
+    assert L.el_hbm_calib(ec.EL_CALIB_GATHER, A, A, 0, A, 10, 24, None) == INVALID         # row size
+    assert L.el_hbm_calib(ec.EL_CALIB_GATHER, A, A, 0, A, 10, 2048, None) == INVALID
+    assert "el_hbm_calib" in ec.el_last_error()
+    assert L.el_hbm_calib(ec.EL_CALIB_WRITE, None, A, 0, None, 0, 0, None) == ec.EL_OK     # nothing to move
 
 
 def test_grad_calls_reject_small_or_missing_workspace():
