@@ -141,25 +141,26 @@ struct GradWorkspace {
   int passes = 0;       // radix passes
   int rbits = 0;        // digit width of every pass
   int64_t nblocks = 0;  // radix tiles
-  int64_t nchunks = 0;  // reduce chunks
+  int64_t nranges = 0;  // reduce ranges (an upper bound: ranges of the fewest lookups)
   size_t bytes = 0;
   uint32_t *keys0 = nullptr, *vals0 = nullptr, *keys1 = nullptr, *vals1 = nullptr;
   uint32_t *hist = nullptr, *hist_scan = nullptr;  // digit-major tile counts, scanned per digit
   uint32_t* dtotal = nullptr;                       // per digit: keys with that digit
   uint32_t *flags = nullptr, *flags_scan = nullptr;
   uint32_t* scan_level[4][2] = {};  // per scan level: tile sums, scanned tile sums
-  float *head = nullptr, *tail = nullptr;
-  uint32_t *through = nullptr, *owner = nullptr;
-  int64_t nblk = 0;             // blocks of kBlockChunks chunks
-  float* bsum = nullptr;        // per block: sum of its chunks' head partials (fully "through" blocks)
-  uint32_t* bthrough = nullptr;  // per block: 1 if every chunk of the block is "through"
+  // per reduce range (the sorted lookups one workgroup reduces): fp32 partial row of the run
+  // that continues from the previous range (or of the whole range if one run covers it) and
+  // of the run that continues into the next range, and flags (bit 0: one run covers the
+  // range; bit 1: the range's last run continues into the next range)
+  float *range_head = nullptr, *range_tail = nullptr;
+  uint32_t* range_flags = nullptr;
 };
 
 constexpr int kRadixBits = 8;  // widest radix digit (wider digits measured slower)
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
-constexpr int kChunk = 16;       // lookups per reduce chunk
-constexpr int kBlockChunks = 64;  // chunks per fix-up block
+constexpr int kChunk = 16;         // lookups per lane group in the reduce
+constexpr int kMinRange = 4 * kChunk;  // fewest lookups per reduce range (four lane groups)
 
 // Lay out the workspace in `base` (nullptr: only compute the size).
 GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* base);

@@ -369,7 +369,7 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
   ws.passes = (bits + kRadixBits - 1) / kRadixBits;          // fewest passes of <= kRadixBits
   ws.rbits = ws.passes > 0 ? (bits + ws.passes - 1) / ws.passes : 0;  // equal widths
   ws.nblocks = (n + kSortTile - 1) / kSortTile;
-  ws.nchunks = (n + kChunk - 1) / kChunk;
+  ws.nranges = (n + kMinRange - 1) / kMinRange;
   const int64_t m_hist = ws.nblocks * (int64_t{1} << ws.rbits);
   const int64_t scan_len = n;
   char* p = static_cast<char*>(base);
@@ -395,13 +395,9 @@ GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* ba
     ws.scan_level[l][1] = static_cast<uint32_t*>(take(4 * len));
     if (len <= 1) break;
   }
-  ws.head = static_cast<float*>(take(sizeof(float) * ws.nchunks * D));
-  ws.tail = static_cast<float*>(take(sizeof(float) * ws.nchunks * D));
-  ws.through = static_cast<uint32_t*>(take(4 * ws.nchunks));
-  ws.owner = static_cast<uint32_t*>(take(4 * ws.nchunks));
-  ws.nblk = (ws.nchunks + kBlockChunks - 1) / kBlockChunks;
-  ws.bsum = static_cast<float*>(take(sizeof(float) * ws.nblk * D));
-  ws.bthrough = static_cast<uint32_t*>(take(4 * ws.nblk));
+  ws.range_head = static_cast<float*>(take(sizeof(float) * ws.nranges * D));
+  ws.range_tail = static_cast<float*>(take(sizeof(float) * ws.nranges * D));
+  ws.range_flags = static_cast<uint32_t*>(take(4 * ws.nranges));
   ws.bytes = off;
   return ws;
 }

@@ -3,29 +3,29 @@
 //
 // Plain SGD on the embedding rows (page "DLRM For PyTorch", §Command-line options --lr):
 // W[r] <- W[r] - lr * (sum of the gradients of all lookups of row r).  The lookups arrive
-// sorted by row (grad_sort.hip), so the contributions to one row form a run ("segment").
+// sorted by row (grad_sort.hip), so the contributions to one row form a run.
 //
-// Skewed (Zipf) indices make some runs thousands of lookups long, so the sorted array is
-// cut into fixed chunks of 16 lookups instead of one worker per run:
-//   k_seg_chunk : one lane group per chunk.  Every lane covers 4 consecutive elements of a
-//                 row.  The group (1) loads the chunk's 16 row numbers and bag ids, (2)
-//                 issues all 16 gradient-row loads and the table-row loads of every run that
-//                 starts and ends inside the chunk, then (3) sums the runs in order (fp32),
-//                 updates those rows and stores the partials of the runs crossing the chunk
-//                 edges: the run continuing from the previous chunk is the chunk's head
-//                 partial, the run continuing into the next chunk its tail partial (the
-//                 chunk "owns" it); a chunk that is one run from edge to edge is "through".
-//                 No load is issued after a store, so a group never waits for its stores
-//                 (loads and stores share one completion counter on this architecture).
-//   k_seg_blocksum : for every block of 64 chunks that one run covers entirely ("through"
-//                 chunks only), the sum of their head partials.
-//   k_seg_fixup : one wavefront per 64 chunks.  An owning chunk's run ends at the first
-//                 chunk after it that is not "through"; runs ending within a few chunks are
-//                 finished by small lane groups side by side (tail + head partials in chunk
-//                 order), longer ones by the whole wavefront, skipping whole "through"
-//                 blocks via their block sums.
-// Every sum has a fixed association, so results are bitwise reproducible; nothing uses
-// atomics and every row is written by exactly one lane group.
+// Skewed (Zipf) indices make some runs thousands of lookups long, so the work is cut by
+// sorted position, not by run:
+//   k_seg_reduce: a workgroup takes a range of G * 16 consecutive sorted lookups, each of
+//     its G lane groups (L lanes, EPL elements of a row per lane) 16 of them.  A group
+//     issues all 16 gradient-row loads, and the table-row loads of the runs that end in its
+//     16 lookups, before any store; it sums its lookups in order (fp32), one "piece" per run,
+//     and updates the rows of the runs that lie inside its 16 lookups.  A piece that
+//     continues into the next group's lookups goes to an LDS slot.  After one barrier the
+//     group where such a run ends adds the earlier groups' slots in group order, then its
+//     own piece, and updates the row.  Only runs that cross an edge of the workgroup's range
+//     leave an fp32 partial row in HBM: the run coming in from the previous range (its
+//     pieces in this range: the range's "head"; the whole range if one run covers it) and
+//     the run going out to the next range (the range's "tail").
+//   k_seg_fixup: one lane group per range whose last run continues into later ranges: the
+//     tail partial plus the head partials of the following ranges up to the one where the
+//     run ends, in range order, then the row update.
+// Every sum has a fixed association (lookups in sorted order within a piece, pieces in
+// group order within a range, partials in range order across ranges), so results are
+// bitwise reproducible; nothing uses atomics and every row is written by one lane group.
+// Loads and stores share one completion counter on this architecture, so a group issues
+// every load it needs before its first store.
 #include <type_traits>
 
 #include "el_internal.hpp"
@@ -33,448 +33,364 @@
 namespace el {
 namespace {
 
-// 4 consecutive elements of T as floats / back (8 or 16 bytes, naturally aligned).
-template <class T>
-__device__ inline void load4(const typename T::S* p, float* f) {
-  if constexpr (sizeof(typename T::S) == 4) {
-    unpack16<T>(*reinterpret_cast<const uint4*>(p), f);
-  } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    f[0] = T::to_f(static_cast<uint16_t>(v.x & 0xffffu));
-    f[1] = T::to_f(static_cast<uint16_t>(v.x >> 16));
-    f[2] = T::to_f(static_cast<uint16_t>(v.y & 0xffffu));
-    f[3] = T::to_f(static_cast<uint16_t>(v.y >> 16));
-  }
-}
+constexpr int CH = kChunk;              // lookups per lane group
+constexpr int kSub = 8;                 // of which loaded at once
+constexpr uint32_t NONE = 0xffffffffu;  // not a row: rows are < total_rows < 2^32 - 1
+constexpr uint32_t RANGE_THROUGH = 1u;  // one run covers the whole range
+constexpr uint32_t RANGE_OWNER = 2u;    // the range's last run continues into the next range
 
-// Raw 4-element load (kept as bits until used, so that issuing it never waits).
-template <class T>
-struct Raw4 {
-  using type = typename std::conditional<sizeof(typename T::S) == 4, uint4, uint2>::type;
+// N consecutive elements of T as raw 32-bit words (8, 16 or 32 bytes), loaded unconverted
+// so that issuing the load never waits.
+template <class T, int N>
+struct Raw {
+  static constexpr int NW = N * static_cast<int>(sizeof(typename T::S)) / 4;
+  uint32_t w[NW];
 };
-template <class T>
-__device__ inline typename Raw4<T>::type load4_raw(const typename T::S* p) {
-  return *reinterpret_cast<const typename Raw4<T>::type*>(p);
-}
-template <class T>
-__device__ inline void unpack4(const typename Raw4<T>::type& v, float* f) {
-  if constexpr (sizeof(typename T::S) == 4) {
-    unpack16<T>(v, f);
+
+template <class T, int N>
+__device__ inline Raw<T, N> load_raw(const typename T::S* p) {
+  Raw<T, N> r;
+  if constexpr (Raw<T, N>::NW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
   } else {
-    f[0] = T::to_f(static_cast<uint16_t>(v.x & 0xffffu));
-    f[1] = T::to_f(static_cast<uint16_t>(v.x >> 16));
-    f[2] = T::to_f(static_cast<uint16_t>(v.y & 0xffffu));
-    f[3] = T::to_f(static_cast<uint16_t>(v.y >> 16));
+#pragma unroll
+    for (int i = 0; i < Raw<T, N>::NW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  }
+  return r;
+}
+
+template <class T, int N>
+__device__ inline void raw_to_f(const Raw<T, N>& r, float* f) {
+  if constexpr (sizeof(typename T::S) == 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) f[i] = __uint_as_float(r.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      f[2 * i] = T::to_f(static_cast<uint16_t>(r.w[i] & 0xffffu));
+      f[2 * i + 1] = T::to_f(static_cast<uint16_t>(r.w[i] >> 16));
+    }
   }
 }
 
-// W[i] <- round(W[i] - lr * g[i]) for 4 elements at w, from the loaded old values (fp32 FMA,
-// one rounding).
-template <class WT>
-__device__ inline void sgd4(typename WT::S* w, const typename Raw4<WT>::type& old, const float* g,
-                            float lr) {
-  float cur[4];
-  unpack4<WT>(old, cur);
+// W[i] <- round(W[i] - lr * g[i]) for N elements at w, from the loaded old values (fp32
+// FMA, one rounding).
+template <class WT, int N>
+__device__ inline void sgd_store(typename WT::S* w, const Raw<WT, N>& old, const float* g, float lr) {
+  float cur[N];
+  raw_to_f<WT, N>(old, cur);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) cur[i] = fmaf(-lr, g[i], cur[i]);
-  store_n<WT, 4>(w, cur);
+  for (int i = 0; i < N; ++i) cur[i] = fmaf(-lr, g[i], cur[i]);
+  store_n<WT, N>(w, cur);
 }
 
-constexpr int CH = kChunk;  // lookups per chunk
-constexpr int kFixChunks = 32;  // chunks per fix-up wavefront (owners on lanes 0..31)
-
-// L lanes per row, each covering 4 elements per vector, NV vectors per lane.
-template <class GT, class WT, int L, int NV>
-__global__ __launch_bounds__(256) void k_seg_chunk(
-    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n, int64_t nchunks,
-    const typename GT::S* __restrict__ demb, int32_t B, int32_t F, int32_t D, int32_t nv4,
-    typename WT::S* __restrict__ W, float lr, float* __restrict__ head, float* __restrict__ tail,
-    uint32_t* __restrict__ through, uint32_t* __restrict__ owner) {
-  static_assert(CH <= 64, "one row number per lane and 16-lane sub-steps");
-  constexpr uint32_t NONE = 0xffffffffu;  // not a row: rows are < total_rows < 2^32
-  constexpr int KPL = CH > L ? CH / L : 1;  // row numbers per lane
-  const int lane = threadIdx.x & 63;
-  const int gl = lane % L;
-  const int gbase = lane - gl;  // first lane of the group
-  const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / L;
-  if (c >= nchunks) return;  // group-uniform
-  const int64_t s = c * CH;
-  const int cnt = static_cast<int>(n - s < CH ? n - s : CH);  // lookups in this chunk, >= 1
-
-  // (1) row numbers and bag ids of the chunk, and the neighbours across its edges
-  uint32_t kr[KPL], vr[KPL];
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int q = gl + j * L;
-    const int qc = q < cnt ? q : cnt - 1;
-    kr[j] = keys[s + qc];
-    vr[j] = vals[s + qc];
+// First local position i in [0, hi] of the range with key(i) == k (k occurs at hi).
+__device__ inline int first_of(const uint32_t* skey, uint32_t k, int hi) {
+  int lo = 0;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (skey[1 + mid] < k) lo = mid + 1; else hi = mid;
   }
-  const uint32_t prev_key = s > 0 ? keys[s - 1] : NONE;
-  const uint32_t next_key = s + cnt < n ? keys[s + cnt] : NONE;
+  return lo;
+}
 
-  auto key_at = [&](int q) { return static_cast<uint32_t>(__shfl(static_cast<int>(kr[q / L]), gbase + q % L)); };
-  auto val_at = [&](int q) { return static_cast<uint32_t>(__shfl(static_cast<int>(vr[q / L]), gbase + q % L)); };
-  const uint32_t k_first = key_at(0);
-  const uint32_t k_last = key_at(cnt - 1);  // cnt - 1 is group-uniform
-  const bool first_before = k_first == prev_key;  // the first run started in an earlier chunk
-  const bool last_after = k_last == next_key;     // the last run continues in a later chunk
+// GT: gradient type, WT: table type; L lanes per row (a power of two), EPL elements per lane,
+// SUB lookups loaded at once.
+template <class GT, class WT, int L, int EPL, int SUB>
+__global__ __launch_bounds__(256) void k_seg_reduce(
+    const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
+    const typename GT::S* __restrict__ demb, int32_t B, int32_t F, int32_t D,
+    typename WT::S* __restrict__ W, float lr, float* __restrict__ rhead,
+    float* __restrict__ rtail, uint32_t* __restrict__ rflags) {
+  constexpr int G = 256 / L;       // lane groups per workgroup
+  constexpr int RANGE = G * CH;    // sorted lookups per workgroup
+  constexpr int PITCH = L * EPL;   // floats per LDS slot (>= D)
+  __shared__ uint32_t skey[RANGE + 2];  // key before the range, the range's keys, key after
+  __shared__ uint32_t sval[RANGE];
+  __shared__ float slot[G * PITCH];     // per group: the piece that continues past its lookups
 
-  // (2) all loads: gradient rows, and the table rows of runs that lie inside the chunk
-  typename Raw4<GT>::type rows[CH][NV];
-  typename Raw4<WT>::type wold[CH][NV];
-  uint32_t kq[CH];
-#pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    kq[q] = key_at(q < cnt ? q : cnt - 1);
-    const uint32_t g = val_at(q < cnt ? q : cnt - 1);
-    const uint32_t t = g / static_cast<uint32_t>(B);
-    const uint32_t b = g - t * static_cast<uint32_t>(B);
-    const typename GT::S* row = demb + (static_cast<int64_t>(b) * F + t) * D;
-#pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      const int v = gl + m * L;
-      rows[q][m] = load4_raw<GT>(row + (v < nv4 ? v : nv4 - 1) * 4);
-    }
+  const int tid = threadIdx.x;
+  const int g = tid / L, gl = tid % L;
+  const int64_t w = blockIdx.x;
+  const int64_t p0 = w * RANGE;
+  const int nloc = static_cast<int>(n - p0 < RANGE ? n - p0 : RANGE);  // lookups of the range, >= 1
+
+  // keys and bag ids of the range, and the keys on either side of it (NONE past the ends)
+  for (int i = tid; i < RANGE; i += 256) {
+    const bool ok = i < nloc;
+    skey[1 + i] = ok ? ld_stream(keys + p0 + i) : NONE;
+    sval[i] = ok ? ld_stream(vals + p0 + i) : 0u;
   }
-#pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    const bool end = q < cnt && (q == cnt - 1 || kq[q + 1 < CH ? q + 1 : q] != kq[q]);
-    const bool inside = end && !(kq[q] == k_first && first_before) && !(kq[q] == k_last && last_after);
-    // unconditional, so the compiler can count outstanding loads exactly; positions that
-    // do not end an inside run re-read the first run's row (a cached line) and ignore it
-    const int64_t wr = inside ? kq[q] : k_first;
-#pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      const int v = gl + m * L;
-      wold[q][m] = load4_raw<WT>(W + wr * D + (v < nv4 ? v : nv4 - 1) * 4);
-    }
-  }
+  if (tid == 0) skey[0] = p0 > 0 ? keys[p0 - 1] : NONE;
+  if (tid == 1) skey[RANGE + 1] = p0 + RANGE < n ? keys[p0 + RANGE] : NONE;
+  __syncthreads();
 
-  // (3) run sums in order, row updates and edge partials
-  float acc[NV][4];
+  const int c0 = g * CH;  // first lookup of this group (local)
+  const int cnt = nloc - c0 <= 0 ? 0 : (nloc - c0 < CH ? nloc - c0 : CH);
+  const int e0 = gl * EPL < D ? gl * EPL : 0;  // this lane's first element (idle lanes: 0)
+  const bool lane_on = gl * EPL < D;
+  const uint32_t kbefore = skey[0];  // key before the range
+
+  float hacc[EPL];        // the group's head piece (a run that began in an earlier group)
+  Raw<WT, EPL> whead;     // and its table row, when the run began inside the range
+  bool has_head = false;  // group-uniform
 #pragma unroll
-  for (int m = 0; m < NV; ++m)
+  for (int x = 0; x < EPL; ++x) hacc[x] = 0.0f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) acc[m][x] = 0.0f;
+  for (int x = 0; x < Raw<WT, EPL>::NW; ++x) whead.w[x] = 0u;
+
+  if (cnt > 0) {  // group-uniform
+    const uint32_t khead = skey[1 + c0];
+    const bool head_cont = khead == skey[c0];  // the first run began before this group
+    float acc[EPL];
 #pragma unroll
-  for (int q = 0; q < CH; ++q) {
-    if (q < cnt) {
+    for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
+    // the group's lookups in halves of SUB (fewer rows held in registers at once); the
+    // running piece carries over from one half to the next
+#pragma unroll 1
+    for (int qb = 0; qb < cnt; qb += SUB) {
+      const int hc = cnt - qb < SUB ? cnt - qb : SUB;  // lookups of this half
+      uint32_t kq[SUB + 1];
 #pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        float f[4];
-        unpack4<GT>(rows[q][m], f);
+      for (int q = 0; q <= SUB; ++q) kq[q] = skey[1 + c0 + qb + (q < hc ? q : hc)];  // kq[hc..]: key after
+
+      // (1) every load of the half: its gradient rows (positions past the end re-read the
+      //     last one), and the table rows of the runs that end here and began inside the
+      //     range (a run that began before the range is finished by the fix-up)
+      Raw<GT, EPL> gr[SUB];
+      Raw<WT, EPL> wold[SUB];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) acc[m][x] += f[x];
+      for (int q = 0; q < SUB; ++q) {
+        const uint32_t v = sval[c0 + qb + (q < hc ? q : hc - 1)];
+        const uint32_t t = v / static_cast<uint32_t>(B);
+        const uint32_t b = v - t * static_cast<uint32_t>(B);
+        gr[q] = load_raw<GT, EPL>(demb + (static_cast<int64_t>(b) * F + t) * D + e0);
       }
-      const bool end = q == cnt - 1 || kq[q + 1 < CH ? q + 1 : q] != kq[q];
-      if (end) {
-        const bool before = kq[q] == k_first && first_before;
-        const bool after = kq[q] == k_last && last_after;
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-          const int v = gl + m * L;
-          if (v < nv4) {
-            if (!before && !after)
-              sgd4<WT>(W + static_cast<int64_t>(kq[q]) * D + v * 4, wold[q][m], acc[m], lr);
-            else
-              store_n<F32T, 4>((before ? head : tail) + c * D + v * 4, acc[m]);
+      for (int q = 0; q < SUB; ++q) {
+        const bool ends = q < hc && kq[q] != kq[q + 1];
+        if (ends && kq[q] != kbefore) {
+          wold[q] = load_raw<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0);
+        } else {
+#pragma unroll
+          for (int x = 0; x < Raw<WT, EPL>::NW; ++x) wold[q].w[x] = 0u;
+        }
+      }
+
+      // (2) pieces in order: a run inside the group is finished here; the head piece waits
+      //     for the barrier; the last piece, if it continues, goes to the group's slot
+#pragma unroll
+      for (int q = 0; q < SUB; ++q) {
+        if (q < hc) {
+          float f[EPL];
+          raw_to_f<GT, EPL>(gr[q], f);
+#pragma unroll
+          for (int x = 0; x < EPL; ++x) acc[x] += f[x];
+          if (kq[q] != kq[q + 1]) {  // a piece ends here
+            if (head_cont && kq[q] == khead) {
+#pragma unroll
+              for (int x = 0; x < EPL; ++x) hacc[x] = acc[x];
+              whead = wold[q];
+              has_head = true;
+            } else if (lane_on) {
+              sgd_store<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0, wold[q], acc, lr);
+            }
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
           }
         }
-#pragma unroll
-        for (int m = 0; m < NV; ++m)
-#pragma unroll
-          for (int x = 0; x < 4; ++x) acc[m][x] = 0.0f;
       }
     }
+    if (skey[c0 + cnt] == skey[1 + c0 + cnt]) {  // the last piece continues past this group
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) slot[g * PITCH + gl * EPL + x] = acc[x];
+    }
   }
-  if (gl == 0) {
-    through[c] = (k_first == k_last && first_before && last_after) ? 1u : 0u;
-    owner[c] = (last_after && !(k_last == k_first && first_before)) ? 1u : 0u;
+  __syncthreads();
+
+  // (3) runs that cross group edges: the group where such a run ends adds the slots of the
+  //     groups before it (in group order) and its own piece
+  if (has_head) {
+    const uint32_t kh = skey[1 + c0];
+    const int cf = first_of(skey, kh, c0) / CH;  // group where the run's first piece lies
+    float tot[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) tot[x] = 0.0f;
+    for (int c = cf; c < g; ++c) {
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) tot[x] += slot[c * PITCH + gl * EPL + x];
+    }
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) tot[x] += hacc[x];
+    if (lane_on) {
+      if (kh == kbefore)  // began before the range: its part in this range is the head partial
+        store_n<F32T, EPL>(rhead + w * D + e0, tot);
+      else
+        sgd_store<WT, EPL>(W + static_cast<int64_t>(kh) * D + e0, whead, tot, lr);
+    }
+  }
+  //     the run that continues past the range: its pieces here are the range's tail partial
+  //     (or, if one run covers the whole range, its head partial)
+  const int glast = (nloc - 1) / CH;
+  const uint32_t klast = skey[nloc];
+  const bool cont = klast == skey[1 + nloc];  // NONE past the end of the lookups
+  if (g == glast && cont) {
+    const int cf = first_of(skey, klast, nloc - 1) / CH;
+    float tot[EPL];
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) tot[x] = 0.0f;
+    for (int c = cf; c <= g; ++c) {
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) tot[x] += slot[c * PITCH + gl * EPL + x];
+    }
+    if (lane_on) store_n<F32T, EPL>((klast == kbefore ? rhead : rtail) + w * D + e0, tot);
+  }
+  if (tid == 0) {
+    const bool through = cont && klast == kbefore;
+    rflags[w] = (through ? RANGE_THROUGH : 0u) | (cont && !through ? RANGE_OWNER : 0u);
   }
 }
 
-// Sum of the fp32 rows first..last (inclusive) of a [rows][D] array into acc, for one
-// wavefront: NG = 64/LF lane groups take rows first+g, first+g+NG, ... with UF loads in
-// flight each, and the group sums are added in group order (returned in every group).
-// The association depends only on (first, last), so results are reproducible.
-template <int LF, int NV, int UF>
-__device__ inline void sum_rows(const float* __restrict__ base, int64_t first, int64_t last, int D,
-                                int nv4, float (&acc)[NV][4]) {
-  constexpr int NG = 64 / LF;
+// One lane group (LF lanes, NV 16-byte vectors of fp32 partials per lane) per range: if the
+// range's last run continues into later ranges, add its tail partial and the head partials
+// of the following ranges (those one run covers, then the one where it ends) in range
+// order, and update the row.  K partials in flight (the hottest rows' runs cross tens of
+// ranges, and their chains are the kernel's critical path).
+template <class WT, int LF, int NV>
+__global__ __launch_bounds__(256) void k_seg_fixup(
+    const uint32_t* __restrict__ keys, int64_t n, int64_t nranges, int32_t range, int32_t D,
+    typename WT::S* __restrict__ W, float lr, const float* __restrict__ rhead,
+    const float* __restrict__ rtail, const uint32_t* __restrict__ rflags) {
+  constexpr int K = 8;
+  constexpr int FL = 64 / LF;  // flags per lane per scan step: 64 per group
+  const int gl = threadIdx.x % LF;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * (256 / LF) + threadIdx.x / LF;
+  if (w >= nranges || !(rflags[w] & RANGE_OWNER)) return;  // group-uniform
+  const int64_t last = (w + 1) * range < n ? (w + 1) * range : n;
+  const uint32_t key = keys[last - 1];
+  // the range where the run ends: the first one after w that one run does not cover (the
+  // last range is never covered); 64 flags per step, the group's first hit by ballot
   const int lane = threadIdx.x & 63;
-  const int grp = lane / LF, gl = lane % LF;
-  float part[NV][4];
+  const int gbase = lane - gl;
+  int64_t e = w + 1;
+  for (;;) {
+    int hit = FL;
 #pragma unroll
-  for (int m = 0; m < NV; ++m)
+    for (int j = FL - 1; j >= 0; --j) {
+      const int64_t i = e + static_cast<int64_t>(gl) * FL + j;
+      if (i >= nranges || !(rflags[i] & RANGE_THROUGH)) hit = j;
+    }
+    const uint64_t m = (__ballot(hit < FL) >> gbase) & (LF == 64 ? ~0ull : ((1ull << LF) - 1ull));
+    if (m) {
+      const int first = __ffsll(static_cast<unsigned long long>(m)) - 1;  // group lane
+      e += static_cast<int64_t>(first) * FL + __shfl(hit, gbase + first);
+      break;
+    }
+    e += 64;
+  }
+  float tot[NV][4];
+  Raw<WT, 4> wold[NV];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) part[m][x] = 0.0f;
-  for (int64_t c0 = first + grp; c0 <= last; c0 += NG * UF) {
-    uint4 p[UF][NV];
+  for (int m = 0; m < NV; ++m) {
+    const int v = gl + m * LF;
+    const int vo = (v * 4 < D ? v : 0) * 4;
+    wold[m] = load_raw<WT, 4>(W + static_cast<int64_t>(key) * D + vo);
+    const uint4 t = *reinterpret_cast<const uint4*>(rtail + w * D + vo);
+    tot[m][0] = __uint_as_float(t.x); tot[m][1] = __uint_as_float(t.y);
+    tot[m][2] = __uint_as_float(t.z); tot[m][3] = __uint_as_float(t.w);
+  }
+  for (int64_t r0 = w + 1; r0 <= e; r0 += K) {
+    uint4 h[K][NV];
 #pragma unroll
-    for (int u = 0; u < UF; ++u) {
-      int64_t cc = c0 + static_cast<int64_t>(u) * NG;
-      cc = cc <= last ? cc : last;
+    for (int k = 0; k < K; ++k) {
+      const int64_t r = r0 + k <= e ? r0 + k : e;
 #pragma unroll
       for (int m = 0; m < NV; ++m) {
         const int v = gl + m * LF;
-        p[u][m] = *reinterpret_cast<const uint4*>(base + cc * D + (v < nv4 ? v : nv4 - 1) * 4);
+        h[k][m] = *reinterpret_cast<const uint4*>(rhead + r * D + (v * 4 < D ? v : 0) * 4);
       }
     }
 #pragma unroll
-    for (int u = 0; u < UF; ++u) {
-      if (c0 + static_cast<int64_t>(u) * NG <= last) {
+    for (int k = 0; k < K; ++k) {
+      if (r0 + k <= e) {
 #pragma unroll
         for (int m = 0; m < NV; ++m) {
-          float f[4];
-          unpack16<F32T>(p[u][m], f);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) part[m][x] += f[x];
+          tot[m][0] += __uint_as_float(h[k][m].x); tot[m][1] += __uint_as_float(h[k][m].y);
+          tot[m][2] += __uint_as_float(h[k][m].z); tot[m][3] += __uint_as_float(h[k][m].w);
         }
       }
     }
   }
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-#pragma unroll
-    for (int m = 0; m < NV; ++m)
-#pragma unroll
-      for (int x = 0; x < 4; ++x) acc[m][x] += __shfl(part[m][x], g * LF + gl);
-  }
-}
-
-// One wavefront per block of kBlockChunks chunks: if every chunk of the block is "through"
-// (one run covers the whole block), store the sum of their head partials.
-template <int LF, int NV>
-__global__ __launch_bounds__(256) void k_seg_blocksum(const float* __restrict__ head,
-                                                      const uint32_t* __restrict__ through,
-                                                      int64_t nchunks, int64_t nblk, int32_t D,
-                                                      int32_t nv4, float* __restrict__ bsum,
-                                                      uint32_t* __restrict__ bthrough) {
-  const int lane = threadIdx.x & 63;
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (j >= nblk) return;
-  const int64_t c0 = j * kBlockChunks;
-  const int64_t cc = c0 + lane;
-  const uint64_t m = __ballot(cc < nchunks && through[cc] != 0);
-  const bool full = m == ~0ull;
-  if (lane == 0) bthrough[j] = full ? 1u : 0u;
-  if (!full) return;
-  float acc[NV][4];
-#pragma unroll
-  for (int q = 0; q < NV; ++q)
-#pragma unroll
-    for (int x = 0; x < 4; ++x) acc[q][x] = 0.0f;
-  sum_rows<LF, NV, 16>(head, c0, c0 + kBlockChunks - 1, D, nv4, acc);
-  const int gl = lane % LF;
-  if (lane < LF) {
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      const int v = gl + q * LF;
-      if (v < nv4) store_n<F32T, 4>(bsum + j * D + v * 4, acc[q]);
-    }
-  }
-}
-
-// First index i >= from with flag[i] == 0 (flags past n count as 0); one wavefront.
-__device__ inline int64_t first_zero(const uint32_t* __restrict__ flag, int64_t from, int64_t n) {
-  const int lane = threadIdx.x & 63;
-  for (int64_t b0 = from;; b0 += 64) {
-    const int64_t i = b0 + lane;
-    const uint64_t m = __ballot(i >= n || flag[i] == 0);
-    if (m) return b0 + __ffsll(static_cast<unsigned long long>(m)) - 1;
-  }
-}
-
-// Row update of a long run owned by chunk c (whole wavefront): total = tail partial + head
-// partials of the chunks up to the one where the run ends, taking whole "through" blocks
-// from their block sums.
-template <class WT, int LF, int NV>
-__device__ inline void fix_long(int64_t c, uint32_t key, int64_t nchunks, int32_t D, int32_t nv4,
-                                typename WT::S* __restrict__ W, float lr,
-                                const float* __restrict__ head, const float* __restrict__ tail,
-                                const uint32_t* __restrict__ through, const float* __restrict__ bsum,
-                                const uint32_t* __restrict__ bthrough, int64_t nblk) {
-  const int lane = threadIdx.x & 63;
-  const int gl = lane % LF;
-  typename Raw4<WT>::type wold[NV];
 #pragma unroll
   for (int m = 0; m < NV; ++m) {
     const int v = gl + m * LF;
-    wold[m] = load4_raw<WT>(W + static_cast<int64_t>(key) * D + (v < nv4 ? v : nv4 - 1) * 4);
-  }
-  float tot[NV][4];
-#pragma unroll
-  for (int m = 0; m < NV; ++m) {
-    const int v = gl + m * LF;
-    unpack16<F32T>(*reinterpret_cast<const uint4*>(tail + c * D + (v < nv4 ? v : nv4 - 1) * 4), tot[m]);
-  }
-  // where does the run end?  first a window of 64 chunks, then whole blocks
-  const int64_t cw = first_zero(through, c + 1, c + 65 < nchunks ? c + 65 : nchunks);
-  if (cw < c + 65 && cw < nchunks && through[cw] == 0) {
-    sum_rows<LF, NV, 16>(head, c + 1, cw, D, nv4, tot);  // ends within the window
-  } else {
-    // chunks c+1 .. c+64 are all "through"; continue from the next block boundary
-    const int64_t jb = (c + 1 + kBlockChunks - 1) / kBlockChunks;  // first block starting after c
-    const int64_t cb = jb * kBlockChunks;                           // <= c + 64
-    const int64_t je = first_zero(bthrough, jb, nblk);              // first block not fully through
-    const int64_t cend = first_zero(through, je * kBlockChunks, nchunks);
-    if (cb > c + 1) sum_rows<LF, NV, 16>(head, c + 1, cb - 1, D, nv4, tot);
-    if (je > jb) sum_rows<LF, NV, 16>(bsum, jb, je - 1, D, nv4, tot);
-    sum_rows<LF, NV, 16>(head, je * kBlockChunks, cend, D, nv4, tot);
-  }
-  if (lane < LF) {
-#pragma unroll
-    for (int m = 0; m < NV; ++m) {
-      const int v = gl + m * LF;
-      if (v < nv4) sgd4<WT>(W + static_cast<int64_t>(key) * D + v * 4, wold[m], tot[m], lr);
-    }
-  }
-}
-
-// One wavefront per kFixChunks (32) consecutive chunks.  Ballots give the "owner" flags of
-// its chunks and the "through" flags of the 128 chunks from its first, so every owning chunk
-// sees at once where its run ends.  Runs ending at most S chunks after their owner ("short", the common case) are
-// finished by lane groups of LG lanes, 64/LG owners side by side: the group loads the tail
-// partial, the S head partials (clamped to the end chunk) and the table row together, adds
-// them in chunk order and updates the row.  Longer runs are then finished one after the
-// other by the whole wavefront (fix_long).
-template <class WT, int LG, int NVG, int S, int LF, int NV>
-__global__ __launch_bounds__(256) void k_seg_fixup(
-    const uint32_t* __restrict__ keys, int64_t n, int64_t nchunks, int32_t D, int32_t nv4,
-    typename WT::S* __restrict__ W, float lr, const float* __restrict__ head,
-    const float* __restrict__ tail, const uint32_t* __restrict__ through,
-    const uint32_t* __restrict__ owner, const float* __restrict__ bsum,
-    const uint32_t* __restrict__ bthrough, int64_t nblk) {
-  constexpr int NGW = 64 / LG;  // owner groups per wavefront
-  const int lane = threadIdx.x & 63;
-  const int64_t c0 = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kFixChunks;
-  if (c0 >= nchunks) return;  // wave-uniform
-  const int64_t cl = c0 + lane, ch = c0 + 64 + lane;
-  const bool own = lane < kFixChunks && cl < nchunks && owner[cl] != 0;
-  const uint64_t tm0 = __ballot(cl < nchunks && through[cl] != 0);
-  const uint64_t tm1 = __ballot(ch < nchunks && through[ch] != 0);
-  // row of this lane's chunk (the last key of the chunk: the run it owns)
-  const int64_t lastpos = (cl + 1) * CH < n ? (cl + 1) * CH : n;
-  const uint32_t keyl = cl < nchunks ? keys[lastpos - 1] : 0u;
-  // end chunk (relative to c0) of the run owned by chunk cl: first non-"through" chunk after it
-  int e = 128;
-  {
-    const uint64_t z0 = lane < 63 ? (~tm0 & (~0ull << (lane + 1))) : 0ull;
-    if (z0) e = __ffsll(static_cast<unsigned long long>(z0)) - 1;
-    else if (~tm1) e = 64 + __ffsll(static_cast<unsigned long long>(~tm1)) - 1;
-  }
-  const bool is_short = own && e - lane <= S;
-  const uint64_t ms = __ballot(is_short);
-  uint64_t ml = __ballot(own && !is_short);
-  const int ns = __popcll(ms);
-  // ranks: short owners first in chunk order, then every other lane (a permutation of lanes)
-  const uint64_t lt = (1ull << lane) - 1ull;
-  const int rank = is_short ? __popcll(ms & lt) : ns + __popcll(~ms & lt);
-  // lane r receives the lane index of the owner of rank r
-  const int who = __builtin_amdgcn_ds_permute(rank * 4, lane);
-  const int grp = lane / LG, gl = lane % LG;
-  for (int r0 = 0; r0 < ns; r0 += NGW) {  // wave-uniform trip count
-    const int R = r0 + grp;
-    const int i = __shfl(who, R < ns ? R : 0);
-    const int ei = __shfl(e, i);
-    const uint32_t key = static_cast<uint32_t>(__shfl(static_cast<int>(keyl), i));
-    if (R < ns) {  // group-uniform
-      const int64_t c = c0 + i, ce = c0 + ei;  // c < ce <= c + S
-      typename Raw4<WT>::type wold[NVG];
-      uint4 tl[NVG], hd[S][NVG];
-#pragma unroll
-      for (int m = 0; m < NVG; ++m) {
-        const int v = gl + m * LG;
-        const int vo = (v < nv4 ? v : nv4 - 1) * 4;
-        wold[m] = load4_raw<WT>(W + static_cast<int64_t>(key) * D + vo);
-        tl[m] = *reinterpret_cast<const uint4*>(tail + c * D + vo);
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-          const int64_t cc = c + 1 + j <= ce ? c + 1 + j : ce;
-          hd[j][m] = *reinterpret_cast<const uint4*>(head + cc * D + vo);
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < NVG; ++m) {
-        const int v = gl + m * LG;
-        float tot[4], f[4];
-        unpack16<F32T>(tl[m], tot);
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-          if (c + 1 + j <= ce) {
-            unpack16<F32T>(hd[j][m], f);
-#pragma unroll
-            for (int x = 0; x < 4; ++x) tot[x] += f[x];
-          }
-        }
-        if (v < nv4) sgd4<WT>(W + static_cast<int64_t>(key) * D + v * 4, wold[m], tot, lr);
-      }
-    }
-  }
-  while (ml) {  // wave-uniform
-    const int i = __ffsll(static_cast<unsigned long long>(ml)) - 1;
-    ml &= ml - 1;
-    const uint32_t key = static_cast<uint32_t>(__shfl(static_cast<int>(keyl), i));
-    fix_long<WT, LF, NV>(c0 + i, key, nchunks, D, nv4, W, lr, head, tail, through, bsum, bthrough, nblk);
+    if (v * 4 < D) sgd_store<WT, 4>(W + static_cast<int64_t>(key) * D + v * 4, wold[m], tot[m], lr);
   }
 }
 
 int blocks_for(int64_t n, int per) { return static_cast<int>((n + per - 1) / per); }
 
-template <class GT, class WT, int L, int NV>
-el_status chunk_t(const el_tables& tab, const el_bags& bags, const GradWorkspace& ws,
-                  const uint32_t* keys, const uint32_t* vals, const void* demb, float lr, int nv4,
-                  hipStream_t stream) {
-  hipLaunchKernelGGL((k_seg_chunk<GT, WT, L, NV>), dim3(blocks_for(ws.nchunks * L, 256)), dim3(256),
-                     0, stream, keys, vals, ws.n, ws.nchunks, static_cast<const typename GT::S*>(demb),
-                     bags.batch, tab.num_tables, tab.dim, nv4, static_cast<typename WT::S*>(tab.base),
-                     lr, ws.head, ws.tail, ws.through, ws.owner);
-  return check_launch("segment_reduce");
+template <class GT, class WT, int L, int EPL>
+el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspace& ws,
+                   const uint32_t* keys, const uint32_t* vals, const void* demb, float lr,
+                   hipStream_t stream) {
+  constexpr int RANGE = (256 / L) * CH;
+  static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
+  const int64_t nr = (ws.n + RANGE - 1) / RANGE;
+  hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub>), dim3(static_cast<unsigned>(nr)), dim3(256), 0, stream,
+                     keys, vals, ws.n, static_cast<const typename GT::S*>(demb), bags.batch,
+                     tab.num_tables, tab.dim, static_cast<typename WT::S*>(tab.base), lr,
+                     ws.range_head, ws.range_tail, ws.range_flags);
+  el_status st = check_launch("segment_reduce");
+  if (st != EL_OK || nr < 2) return st;
+  // fix-up: LF lanes x NV vectors of 4 fp32 per row
+  const int d4 = tab.dim / 4;
+  auto fix = [&](auto lf, auto nv) {
+    constexpr int LF = decltype(lf)::value, NV = decltype(nv)::value;
+    hipLaunchKernelGGL((k_seg_fixup<WT, LF, NV>), dim3(blocks_for(nr, 256 / LF)), dim3(256), 0, stream,
+                       keys, ws.n, nr, RANGE, tab.dim, static_cast<typename WT::S*>(tab.base), lr,
+                       static_cast<const float*>(ws.range_head), static_cast<const float*>(ws.range_tail),
+                       static_cast<const uint32_t*>(ws.range_flags));
+    return check_launch("segment_fixup");
+  };
+  using I = std::integral_constant<int, 1>;
+  if (d4 <= 1) return fix(I{}, I{});
+  if (d4 <= 2) return fix(std::integral_constant<int, 2>{}, I{});
+  if (d4 <= 4) return fix(std::integral_constant<int, 4>{}, I{});
+  if (d4 <= 8) return fix(std::integral_constant<int, 8>{}, I{});
+  if (d4 <= 16) return fix(std::integral_constant<int, 16>{}, I{});
+  if (d4 <= 32) return fix(std::integral_constant<int, 32>{}, I{});
+  if (d4 <= 64) return fix(std::integral_constant<int, 64>{}, I{});
+  return fix(std::integral_constant<int, 64>{}, std::integral_constant<int, 2>{});
 }
 
-template <class WT, int LG, int NVG, int S, int LF, int NV>
-el_status fixup_t(const el_tables& tab, const GradWorkspace& ws, const uint32_t* keys, float lr,
-                  int nv4, hipStream_t stream) {
-  hipLaunchKernelGGL((k_seg_blocksum<LF, NV>), dim3(blocks_for(ws.nblk, 4)), dim3(256), 0, stream,
-                     static_cast<const float*>(ws.head), static_cast<const uint32_t*>(ws.through),
-                     ws.nchunks, ws.nblk, tab.dim, nv4, ws.bsum, ws.bthrough);
-  el_status st = check_launch("segment_blocksum");
-  if (st != EL_OK) return st;
-  hipLaunchKernelGGL((k_seg_fixup<WT, LG, NVG, S, LF, NV>), dim3(blocks_for(ws.nchunks, 4 * kFixChunks)), dim3(256),
-                     0, stream,
-                     keys, ws.n, ws.nchunks, tab.dim, nv4, static_cast<typename WT::S*>(tab.base), lr,
-                     static_cast<const float*>(ws.head), static_cast<const float*>(ws.tail),
-                     static_cast<const uint32_t*>(ws.through), static_cast<const uint32_t*>(ws.owner),
-                     static_cast<const float*>(ws.bsum), static_cast<const uint32_t*>(ws.bthrough),
-                     ws.nblk);
-  return check_launch("segment_fixup");
-}
-
+// Elements per lane: 4 (8- or 16-byte parts of the rows: sixteen of each in flight per lane
+// keep the registers low enough for three or more wavefronts per SIMD); lanes per row: the
+// power of two that covers D.
 template <class GT, class WT>
 el_status reduce_typed(const el_tables& tab, const el_bags& bags, const GradWorkspace& ws,
                        const uint32_t* keys, const uint32_t* vals, const void* demb, float lr,
                        hipStream_t stream) {
-  // rows split into 4-element vectors; chunk groups need at least 16 lanes (one row number
-  // per lane), so narrow rows leave lanes idle
-  const int nv4 = tab.dim / 4;
-  el_status st;
-  if (nv4 <= 16) st = chunk_t<GT, WT, 16, 1>(tab, bags, ws, keys, vals, demb, lr, nv4, stream);
-  else if (nv4 <= 32) st = chunk_t<GT, WT, 32, 1>(tab, bags, ws, keys, vals, demb, lr, nv4, stream);
-  else if (nv4 <= 64) st = chunk_t<GT, WT, 64, 1>(tab, bags, ws, keys, vals, demb, lr, nv4, stream);
-  else if (nv4 <= 128) st = chunk_t<GT, WT, 64, 2>(tab, bags, ws, keys, vals, demb, lr, nv4, stream);
-  else return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim > 512 is not supported");
-  if (st != EL_OK) return st;
-  // fix-up: short runs by groups of LG lanes (NVG vectors each, S head partials in flight),
-  // long runs by the wavefront (LF lanes per row, NV vectors each)
-  if (nv4 <= 1) return fixup_t<WT, 1, 1, 8, 1, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 2) return fixup_t<WT, 2, 1, 8, 2, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 4) return fixup_t<WT, 4, 1, 8, 4, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 8) return fixup_t<WT, 8, 1, 8, 8, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 16) return fixup_t<WT, 16, 1, 8, 16, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 32) return fixup_t<WT, 16, 2, 8, 32, 1>(tab, ws, keys, lr, nv4, stream);
-  if (nv4 <= 64) return fixup_t<WT, 16, 4, 4, 64, 1>(tab, ws, keys, lr, nv4, stream);
-  return fixup_t<WT, 32, 4, 4, 64, 2>(tab, ws, keys, lr, nv4, stream);
+  constexpr int EPL = 4;
+  if (tab.dim % EPL != 0)
+    return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim must be a multiple of 16 bytes of both row types");
+  const int lanes = tab.dim / EPL;
+  if constexpr (EPL == 4) {  // rows of more than 64 vectors: 8 elements per lane
+    if (lanes > 64 && tab.dim % 8 == 0 && tab.dim <= 512)
+      return reduce_t<GT, WT, 64, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+  }
+  if (lanes <= 1) return reduce_t<GT, WT, 1, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 2) return reduce_t<GT, WT, 2, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 4) return reduce_t<GT, WT, 4, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 8) return reduce_t<GT, WT, 8, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 16) return reduce_t<GT, WT, 16, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 32) return reduce_t<GT, WT, 32, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  if (lanes <= 64) return reduce_t<GT, WT, 64, EPL>(tab, bags, ws, keys, vals, demb, lr, stream);
+  return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim > 512 is not supported");
 }
 
 template <class GT>
@@ -494,8 +410,6 @@ el_status reduce_w(const el_tables& tab, const el_bags& bags, const GradWorkspac
 el_status launch_reduce_update(const el_tables& tab, const el_bags& bags, const GradWorkspace& ws,
                                const uint32_t* sorted_keys, const uint32_t* sorted_vals,
                                const void* demb, el_dtype grad_dtype, float lr, hipStream_t stream) {
-  if (tab.dim % 4 != 0)
-    return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim must be a multiple of 4");
   switch (grad_dtype) {
     case EL_F32: return reduce_w<F32T>(tab, bags, ws, sorted_keys, sorted_vals, demb, lr, stream);
     case EL_F16: return reduce_w<F16T>(tab, bags, ws, sorted_keys, sorted_vals, demb, lr, stream);
