@@ -185,6 +185,27 @@ def test_bf16_overflow_and_f32_store():
     assert np.array_equal(orc.round_from_f64(x, "f32").view(np.uint32), x.astype(np.float32).view(np.uint32))
 
 
+def test_converters_exhaustive_over_all_fp32_patterns(tmp_path):
+    """All 2^32 binary32 patterns through the oracle's bf16 and fp16 rounding, against the
+    x86 F16C conversion (binary16) and round-to-nearest-even on the bit pattern (bfloat16);
+    the C program is tests/native/p4_converters.c (OpenMP, about 20 s on 8 cores)."""
+    import os
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    with open("/proc/cpuinfo") as f:
+        if "f16c" not in f.read():
+            pytest.skip("the host CPU has no F16C conversion instructions")
+    src = os.path.join(os.path.dirname(os.path.abspath(__file__)), "native", "p4_converters.c")
+    exe = str(tmp_path / "p4_converters")
+    subprocess.run(["gcc", "-O2", "-std=gnu11", "-fopenmp", "-mf16c", "-ffp-contract=off",
+                    "-Wno-unknown-pragmas", "-o", exe, src, "-lm"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "bf16 mismatches 0" in r.stdout and "f16 mismatches 0" in r.stdout
+
+
 def test_widening_is_exact():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     w = orc.widen(bits, "bf16")
