@@ -405,24 +405,33 @@ int el_version(void) { return 200; }
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------
-// el_validate_bags kernel: one workgroup, a deterministic tree reduction of the count.
+// el_validate_bags kernels: a grid of workgroups over the bags, each thread counting the
+// defects of its bags; workgroup subtotals are added to the count with one 64-bit integer
+// atomic each (an exact integer sum, the same for any order).  The count is cleared by a
+// one-thread kernel first (a kernel rather than a memset, so that the call can be captured
+// in a HIP graph).
 // ---------------------------------------------------------------------------------------
 namespace el {
 namespace {
 
-__global__ __launch_bounds__(1024) void k_validate(const int64_t* __restrict__ row_off,
-                                                   const int32_t* __restrict__ idx,
-                                                   const int32_t* __restrict__ off, int32_t F,
-                                                   int32_t B, int64_t nnz, uint32_t hash,
-                                                   int64_t* __restrict__ bad_count) {
-  __shared__ int64_t part[16];
+__global__ void k_validate_clear(int64_t* __restrict__ bad_count) {
+  if (threadIdx.x == 0) bad_count[0] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_validate(const int64_t* __restrict__ row_off,
+                                                  const int32_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ off, int32_t F,
+                                                  int32_t B, int64_t nnz, uint32_t hash,
+                                                  int64_t* __restrict__ bad_count) {
+  __shared__ int64_t part[4];
   const int64_t nbags = static_cast<int64_t>(F) * B;
   int64_t bad = 0;
-  if (threadIdx.x == 0) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
     if (off[0] != 0) ++bad;
     if (off[nbags] != nnz) ++bad;
   }
-  for (int64_t g = threadIdx.x; g < nbags; g += blockDim.x) {
+  for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < nbags;
+       g += static_cast<int64_t>(gridDim.x) * 256) {
     const int32_t s = off[g], e = off[g + 1];
     if (e < s) ++bad;
     if (!hash) {
@@ -436,14 +445,13 @@ __global__ __launch_bounds__(1024) void k_validate(const int64_t* __restrict__ r
       }
     }
   }
-  // wavefront sums, then the 16 wave sums in order
+  // wavefront sums, then the workgroup's four wave sums, added to the count
   for (int o = 32; o > 0; o >>= 1) bad += __shfl_down(bad, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = bad;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t tot = 0;
-    for (int w = 0; w < static_cast<int>(blockDim.x / 64); ++w) tot += part[w];
-    bad_count[0] = tot;
+    const int64_t tot = part[0] + part[1] + part[2] + part[3];
+    if (tot) atomicAdd(reinterpret_cast<unsigned long long*>(bad_count), static_cast<unsigned long long>(tot));
   }
 }
 
@@ -451,8 +459,14 @@ __global__ __launch_bounds__(1024) void k_validate(const int64_t* __restrict__ r
 
 el_status launch_validate(const el_tables& tab, const el_bags& bags, uint32_t flags,
                           int64_t* bad_count, hipStream_t stream) {
-  hipLaunchKernelGGL(k_validate, dim3(1), dim3(1024), 0, stream, tab.row_offset, bags.indices,
-                     bags.offsets, tab.num_tables, bags.batch, bags.nnz,
+  hipLaunchKernelGGL(k_validate_clear, dim3(1), dim3(64), 0, stream, bad_count);
+  el_status st = check_launch("el_validate_bags");
+  if (st != EL_OK) return st;
+  const int64_t nbags = static_cast<int64_t>(tab.num_tables) * bags.batch;
+  int64_t blocks = (nbags + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
+  hipLaunchKernelGGL(k_validate, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, tab.row_offset,
+                     bags.indices, bags.offsets, tab.num_tables, bags.batch, bags.nnz,
                      (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u, bad_count);
   return check_launch("el_validate_bags");
 }

@@ -7,16 +7,17 @@
 // other, so that the reduction needs no atomics.
 //
 // Radix sort: least significant digit first, the fewest passes of at most kRadixBits-bit
-// digits that cover the largest row number, with equal digit widths (22-bit rows: 3 x 8 bits).  One pass
-// = tile histograms -> per digit, a scan over the tiles -> stable scatter (which adds the
-// scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes, each
+// digits that cover the largest row number, with equal digit widths (22-bit rows: 3 x 8
+// bits).  One pass = tile histograms -> per digit, a scan over the tiles -> stable scatter
+// (which adds the scanned digit totals).  A tile is 4096 keys: 4 wavefronts x 16 steps x 64 lanes, each
 // wavefront owning 1024 consecutive keys.  Within a step the lanes holding the same digit
-// are found with one ballot per digit bit; the lowest of them adds the group's size to its
-// wavefront's private LDS counter, so every LDS counter has one writer per step and no
-// atomic is needed.  Ranks are taken in key order (wave, step, lane), which makes every
-// pass stable and the whole sort deterministic.  The ranked tile is staged in LDS in
-// sorted order and written out run by run, so that neighbouring threads store to
-// neighbouring addresses.
+// are found with one ballot per digit bit in the scatter; the lowest of them adds the
+// group's size to its wavefront's private LDS counter, so every counter has one writer per
+// step and the ranks need no atomic.  Ranks are taken in key order (wave, step, lane),
+// which makes every pass stable and the whole sort deterministic.  The tile histograms use
+// integer LDS atomics (exact counts whatever the order of the adds).  The ranked tile is
+// staged in LDS in sorted order and written out run by run, so that neighbouring threads
+// store to neighbouring addresses.
 #include "el_internal.hpp"
 
 namespace el {
@@ -76,9 +77,12 @@ __global__ __launch_bounds__(256) void k_build_keys(const int64_t* __restrict__ 
   }
 }
 
-// Digit counts of one tile.  LDS atomics into kSub sub-histograms (wavefront and lane group),
-// so that few lanes contend for one counter even when a tile holds many equal keys (the hot
-// rows of skewed indices); counts do not depend on the order of the adds.
+// Digit counts of one tile.  Integer LDS atomics into kSub sub-histograms (wavefront and
+// lane group), so that few lanes contend for one counter even when a tile holds many equal
+// keys (the hot rows of skewed indices); counts do not depend on the order of the adds, so
+// the histograms, and the sort, are deterministic.  (Measured and not kept: counting with
+// ballots as the scatter ranks, 1.7-2x slower; several tiles per workgroup; one add per run
+// of equal digits in neighbouring lanes.)
 template <int RB>
 __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
                                                     int shift, uint32_t* __restrict__ hist,

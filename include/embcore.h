@@ -261,7 +261,9 @@ EL_API el_status emb_grad_sort(const el_tables* tab, const el_bags* bags, uint32
 /*
  * Count defects of a CSR batch: offsets that decrease, offsets[0] != 0,
  * offsets[F*B] != nnz, and (without EL_FLAG_HASH_INDICES) indices outside their table.
- * bad_count: [1] int64 device, overwritten with the total.
+ * bad_count: [1] int64 device, overwritten with the total.  A grid of workgroups scans the
+ * bags; their subtotals are added with integer atomics (the count is exact whatever the
+ * order).  Not part of the computation: the other calls use no atomics.
  */
 EL_API el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t flags,
                            int64_t* bad_count, hipStream_t stream);
