@@ -333,3 +333,30 @@ def test_emb_dot_bwd_direct_term_every_sample():
         elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb)
         torch.cuda.synchronize()
         assert torch.equal(dx0.view(torch.int16), G[:, :D].contiguous().view(torch.int16))
+
+
+def test_validate_bags_at_full_multi_hot_size():
+    """el_validate_bags over the multi-hot batch (1.64M bags, 32.8M lookups): no defect, then
+    exactly the planted ones (indices outside their table, a decreasing offset pair)."""
+    wl = synth.WORKLOADS["multi_hot"]
+    B, F = wl.batch, wl.num_tables
+    W, ro = synth.make_tables(wl, DEV)
+    idx, off = synth.make_indices(wl, DEV)
+    tab = elf.Tables(W, ro)
+    cnt = torch.full((1,), -1, dtype=torch.int64, device=DEV)
+    elf.el_validate_bags(tab, elf.Bags(idx, off, B), cnt)
+    assert int(cnt.item()) == 0
+    bad = idx.clone()
+    n = idx.numel()
+    bad[0] = -1
+    bad[n // 2] = wl.rows[0]   # one past the end of its table
+    bad[n - 1] = 2 ** 30
+    elf.el_validate_bags(tab, elf.Bags(bad, off, B), cnt)
+    assert int(cnt.item()) == 3
+    elf.el_validate_bags(tab, elf.Bags(bad, off, B), cnt, hash_indices=True)
+    assert int(cnt.item()) == 0
+    bad_off = off.clone()
+    g = F * B // 3
+    bad_off[g] = bad_off[g + 1] + 1  # offsets g-1 -> g and g -> g+1: one pair decreases
+    elf.el_validate_bags(tab, elf.Bags(idx, bad_off, B), cnt)
+    assert int(cnt.item()) >= 1
