@@ -171,6 +171,89 @@ __global__ __launch_bounds__(64 * WPB) void k_dot_fwd_mfma(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------------------
+// Forward, MFMA path for many vectors (more than one 32-row tile per sample): the four
+// wavefronts of a workgroup share one sample's V x D tile in LDS (pitch 2D+16), and the
+// lower-triangular 32x32 tiles of Z are dealt out to them round-robin.  Each wavefront
+// writes its products straight from the MFMA accumulators to the output row: for one
+// accumulator register, lanes 0-31 hold 32 consecutive columns j of one row i and lanes
+// 32-63 those of row i+4, so a store covers two runs of consecutive pair positions
+// D + i(i-1)/2 + j.  No output row is staged in LDS, which leaves room for more resident
+// samples than the one-wavefront-per-sample kernel.  The next sample's tile is loaded into
+// registers before the current one is multiplied.
+// ---------------------------------------------------------------------------------------
+template <class IT, class OT, int NQ>
+__global__ __launch_bounds__(256) void k_dot_fwd_wide(const uint16_t* __restrict__ x0,
+                                                      const uint16_t* __restrict__ emb, int B,
+                                                      int F, int D, typename OT::S* __restrict__ out,
+                                                      int out_stride) {
+  extern __shared__ uint4 smem[];
+  char* lds = reinterpret_cast<char*>(smem);
+  using OS = typename OT::S;
+  const int V = F + 1;
+  const int P = V * (V - 1) / 2;
+  const int pitch = D * 2 + 16;
+  const int trash = V * pitch;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+  const int nv = D / 8;
+  const int tile = V * nv;  // 16-byte chunks of a sample's vectors
+  const int NT = (V + 31) / 32;
+  const int ntiles = NT * (NT + 1) / 2;
+
+  // chunk q of sample bb (q < tile: row q / nv of the V x D tile, contiguous from x0[bb]
+  // and emb[bb]); chunks past the tile re-load the last one
+  u32x4 r[NQ];
+  auto fetch = [&](int bb) {
+    const int64_t x0b = static_cast<int64_t>(bb) * D;
+    const int64_t eb = static_cast<int64_t>(bb) * F * D - D;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      int q = u * 256 + tid;
+      q = q < tile ? q : tile - 1;
+      const int row = q / nv, c = q - row * nv;
+      const uint16_t* src = row == 0 ? x0 + x0b + c * 8 : emb + eb + static_cast<int64_t>(row) * D + c * 8;
+      r[u] = *reinterpret_cast<const u32x4*>(src);
+    }
+  };
+  int b = blockIdx.x;
+  if (b >= B) return;
+  fetch(b);
+  for (; b < B; b += gridDim.x) {
+    __syncthreads();  // the previous sample's products have read the tile
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = u * 256 + tid;
+      const int row = q / nv, c = q - row * nv;
+      *reinterpret_cast<u32x4*>(lds + (q < tile ? row * pitch + c * 16 : trash)) = r[u];
+    }
+    if (b + static_cast<int>(gridDim.x) < B) fetch(b + gridDim.x);
+    __syncthreads();
+    OS* orow = out + static_cast<int64_t>(b) * out_stride;
+    // x0 copy (converted to the output type; exact when the types agree) and zero padding
+    for (int d = tid; d < D; d += 256) orow[d] = OT::from_f(IT::to_f(*reinterpret_cast<const uint16_t*>(lds + d * 2)));
+    for (int c = D + P + tid; c < out_stride; c += 256) orow[c] = OT::from_f(0.0f);
+    for (int t = wave; t < ntiles; t += 4) {  // wave-uniform
+      int I = 0, J = t;
+      while (J > I) { J -= I + 1; ++I; }
+      f32x16 acc = {};
+      const int ra = I * 32 + col, rb = J * 32 + col;
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int cb = (2 * ks + half) * 16;  // byte offset of this lane's 8 elements
+        const u32x4 a = lds16_or_zero(lds, ra * pitch + cb, ra < V);
+        const u32x4 bv = (I == J) ? a : lds16_or_zero(lds, rb * pitch + cb, rb < V);
+        acc = mfma32<IT>(a, bv, acc);
+      }
+      const int j = J * 32 + col;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int i = I * 32 + acc_row(rr, lane);
+        if (i < V && j < i) orow[D + i * (i - 1) / 2 + j] = OT::from_f(acc[rr]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Backward, MFMA path, computed transposed: dV^T = V^T S (S is symmetric), so that
 //   A = V^T  (lane: one dimension d, 8 consecutive vectors)  -> one 16-byte LDS read,
 //   B = S    (lane: one vector v, 8 consecutive vectors)     -> rebuilt from the gradient row,
@@ -709,10 +792,28 @@ el_status launch_fwd_t(const void* x0, const void* emb, int B, int F, int D, voi
 
 // Shape classes of the MFMA forward: input chunks per lane (NQ) and output-row chunks per
 // lane (SPL; 0 = a loop of run-time length).
+template <class IT, class OT, int NQ>
+el_status launch_fwd_wide_t(const void* x0, const void* emb, int B, int F, int D, void* out,
+                            int out_stride, size_t lds, hipStream_t stream) {
+  auto kern = k_dot_fwd_wide<IT, OT, NQ>;
+  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 256)), dim3(256),
+                     lds, stream, static_cast<const uint16_t*>(x0), static_cast<const uint16_t*>(emb), B, F, D,
+                     static_cast<typename OT::S*>(out), out_stride);
+  return check_launch("dot_interact_fwd");
+}
+
 template <class IT, class OT>
 el_status launch_fwd_mfma(const void* x0, const void* emb, int B, int F, int D, void* out,
                           int out_stride, size_t lds, hipStream_t stream) {
   const int chunks = (F + 1) * (D / 8);
+  if (F + 1 > 32) {  // several 32-row tiles: four wavefronts per sample, no staged output row
+    const size_t tlds = static_cast<size_t>(F + 1) * (D * 2 + 16) + 16;
+    if (tlds <= kMaxLds) {
+      if (chunks <= 2 * 256) return launch_fwd_wide_t<IT, OT, 2>(x0, emb, B, F, D, out, out_stride, tlds, stream);
+      if (chunks <= 4 * 256) return launch_fwd_wide_t<IT, OT, 4>(x0, emb, B, F, D, out, out_stride, tlds, stream);
+      if (chunks <= 8 * 256) return launch_fwd_wide_t<IT, OT, 8>(x0, emb, B, F, D, out, out_stride, tlds, stream);
+    }
+  }
   const int64_t ochunks = (static_cast<int64_t>(out_stride) * sizeof(typename OT::S) + 15) / 16;
   if (chunks <= 8 * 64) {
     if (ochunks <= 64) return launch_fwd_t<IT, OT, 8, 1>(x0, emb, B, F, D, out, out_stride, lds, stream);
