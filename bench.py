@@ -67,6 +67,12 @@ def fused_bwd_ok(wl):
             and (V + 31) // 32 * 16 * (D // 8) <= 256 and wl.out_stride % 8 == 0)
 
 
+def fused_fwd_ok(wl):
+    """The shapes emb_dot_fwd's fused kernel (no pooled-vector output) covers
+    (include/embcore.h): 16-bit activations, D % 16 == 0, at most 64 tables."""
+    return wl.act_dtype in ("bf16", "f16") and wl.dim % 16 == 0 and wl.num_tables <= 64
+
+
 def metric_name(wl):
     what = "fwd+bwd" if wl.backward else "fwd"
     return f"samples/s {what} (emb-bag + dot interaction) at batch {wl.batch}; achieved HBM GB/s"
@@ -293,7 +299,9 @@ def main():
     # with --recompute-emb rebuild them in the backward where the fused backward covers
     # the shape
     recompute = wl.backward and fused_fwd and args.recompute_emb and fused_bwd_ok(wl)
-    store_emb = wl.backward and not recompute
+    # forward-only shapes the fused kernel does not cover store the pooled vectors (chunked
+    # gather + interaction)
+    store_emb = (wl.backward and not recompute) or (fused_fwd and not fused_fwd_ok(wl))
     bwd_name = "emb_dot_bwd" if recompute else "dot_interact_bwd"
     fwd_names = ["emb_dot_fwd"] if fused_fwd else ["emb_bag_fwd", "dot_interact_fwd"]
     if not wl.backward:
@@ -471,9 +479,11 @@ def main():
     # short sort / reduce kernels, each well below the interaction kernels; in training
     # emb_dot_fwd is a sequence of gather and interaction launches)
     single = [n for n in names if n in KERNEL_OF_CALL and not (n == "emb_dot_fwd" and store_emb)]
-    dom = max(single, key=lambda n: call_ms[n])
-    kernel = kernel_of(dom, wl)
-    achieved = algo[dom] / (call_ms[dom] * 1e-3) / 1e9
+    if single:
+        dom = max(single, key=lambda n: call_ms[n])
+        kernel = kernel_of(dom, wl)
+    else:  # a forward-only line whose one call runs the gather and the interaction in chunks
+        dom, kernel = names[0], "k_emb_bag_fwd + interaction forward"
     def roofline_of(call, kernel, ms, nbytes, note=None):
         a = nbytes / (ms * 1e-3) / 1e9
         r = {"bound": "hbm", "kernel": kernel, "call": call, "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,

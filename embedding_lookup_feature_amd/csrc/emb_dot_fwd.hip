@@ -165,7 +165,7 @@ __global__ __launch_bounds__(64) void k_emb_dot_fwd(
         for (int x = 0; x < 8; ++x) f[x] = ne ? f[x] : 0.0f;
         *reinterpret_cast<u32x4*>(lds + (1 + t) * pitch + c * 16) = pack8<IT>(f);
       }
-    } else {  // multi-hot bags: the further entries one after the other (not pipelined)
+    } else {  // multi-hot bags: the further entries four at a time (all their loads in flight)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         int q = u * 64 + lane;
@@ -177,15 +177,28 @@ __global__ __launch_bounds__(64) void k_emb_dot_fwd(
         const int32_t nt = __shfl(static_cast<int>(trows), t);
         float f[8];
         unit_to_f<TT>(rows[u], f);
-        for (int k = bs + 1; k < be; ++k) {
-          int32_t r = idx[k];
-          if (hash) r = floor_mod(r, nt);
-          Unit<TT> w;
-          load_unit<TT>(w, W + static_cast<int64_t>(tb + static_cast<uint32_t>(r)) * D + c * 8);
-          float g[8];
-          unit_to_f<TT>(w, g);
+        for (int k = bs + 1; k < be; k += 4) {
+          // indices, then rows, of the next four entries (entries past the bag's end re-read
+          // its last entry and are not added); added in CSR order
+          int32_t r[4];
 #pragma unroll
-          for (int x = 0; x < 8; ++x) f[x] += g[x];
+          for (int e = 0; e < 4; ++e) {
+            r[e] = idx[k + e < be ? k + e : be - 1];
+            if (hash) r[e] = floor_mod(r[e], nt);
+          }
+          Unit<TT> w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            load_unit<TT>(w[e], W + static_cast<int64_t>(tb + static_cast<uint32_t>(r[e])) * D + c * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (k + e < be) {
+              float g[8];
+              unit_to_f<TT>(w[e], g);
+#pragma unroll
+              for (int x = 0; x < 8; ++x) f[x] += g[x];
+            }
+          }
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) f[x] = ne ? f[x] : 0.0f;

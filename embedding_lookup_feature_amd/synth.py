@@ -116,6 +116,12 @@ WORKLOADS = {
         bag=("poisson", 20.0, 1, 100), bottom_mlp=(13, 512, 256, 64), backward=True,
         description="B=16384, 100 bf16 tables x 1M x 64, bag length Poisson(20) clipped to [1,100], "
                     "Zipf(1.05), 101 vectors -> 5050 pairs, fwd+bwd+update"),
+    # the multi-hot shapes forward only (serving: the fused forward, pooled vectors kept on chip)
+    "multi_hot_infer": Workload(
+        "multi_hot_infer", 16384, (1_000_000,) * 100, 64, "bf16", "bf16", "zipf", 1.05,
+        bag=("poisson", 20.0, 1, 100), bottom_mlp=(13, 512, 256, 64), backward=False,
+        description="multi_hot shapes, forward only (fused gather + interaction, pooled vectors "
+                    "not stored)"),
     # secondary figure: the small tables at the large batch (cache-resident tables)
     "train_small_tables": Workload(
         "train_small_tables", 65536, (1000,) * 8, 16, "f32", "bf16", "zipf", 1.05,

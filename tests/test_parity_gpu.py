@@ -120,6 +120,9 @@ FUSED_CASES = [
     ("f32-bf16-26x128-no-emb", (5000,) * 26, 128, "f32", "bf16", ("one",), "zipf", False, 1000, False),
     ("f16-ragged-tables", (3, 70000, 1234), 128, "f16", "f16", ("one",), "zipf", False, 1500, True),
     ("bf16-d64-multihot", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300, True),
+    # the fused kernel's multi-hot branch (entries four at a time), bags of every length mod 4
+    ("bf16-d64-multihot-no-emb", (20000,) * 10, 64, "bf16", "bf16", ("poisson", 20.0, 1, 100), "zipf", False, 300, False),
+    ("f32-bf16-d128-multihot-hash-no-emb", (999, 7, 5000), 128, "f32", "bf16", ("poisson", 5.0, 0, 13), "uniform", True, 257, False),
     ("f32-bf16-d16-empty-bags", (500,) * 5, 16, "f32", "bf16", ("poisson", 3.0, 0, 10), "uniform", False, 333, True),
     ("f32-f16-hash", (999, 7, 5000), 32, "f32", "f16", ("one",), "uniform", True, 400, True),
     ("bf16-64-tables", (300,) * 64, 32, "bf16", "bf16", ("one",), "uniform", False, 100, True),
