@@ -41,7 +41,13 @@ KERNEL_SOURCES = {
                       "embedding_lookup_feature_amd/csrc/emb_dot_fwd.hip"],
 }
 KERNEL_SOURCES["k_dot_fwd_valu"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
+KERNEL_SOURCES["k_dot_fwd_wide"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
 KERNEL_SOURCES["k_dot_bwd_valu"] = KERNEL_SOURCES["k_dot_bwd_mfma"]
+for _k, _f in (("k_seg_reduce", "grad_update.hip"), ("k_seg_fixup", "grad_update.hip"),
+               ("k_build_keys", "grad_sort.hip"), ("k_radix_hist", "grad_sort.hip"),
+               ("k_radix_scatter", "grad_sort.hip"), ("k_digit_scan", "grad_sort.hip")):
+    KERNEL_SOURCES[_k] = ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
+                          "embedding_lookup_feature_amd/csrc/" + _f]
 KERNEL_OF_CALL = {"emb_bag_fwd": "k_emb_bag_fwd", "dot_interact_fwd": "k_dot_fwd_mfma",
                   "dot_interact_bwd": "k_dot_bwd_mfma", "emb_dot_fwd": "k_emb_dot_fwd",
                   "emb_dot_bwd": "k_dot_bwd_mfma"}
@@ -55,6 +61,8 @@ def kernel_of(call, wl):
     mfma = wl.act_dtype in ("bf16", "f16") and D % 16 == 0 and V <= 128
     if call == "dot_interact_fwd" and not mfma:
         return "k_dot_fwd_valu"
+    if call == "dot_interact_fwd" and V > 32:  # several 32-row tiles: four wavefronts per sample
+        return "k_dot_fwd_wide"
     if call == "dot_interact_bwd" and not (mfma and D >= 32 and wl.out_stride % 8 == 0):
         return "k_dot_bwd_valu"
     return KERNEL_OF_CALL[call]
@@ -109,41 +117,64 @@ def algorithmic_bytes(wl, nnz, store_emb=None):
     }
 
 
+def sort_passes(wl):
+    """Radix passes of the gradient sort: 8-bit digits over the local rows of the largest
+    table (every table's lookups are sorted in place by local row)."""
+    key_bits = max(1, int(max(wl.rows) - 1).bit_length())
+    return (key_bits + 7) // 8
+
+
 def sort_start(wl, nnz):
     """Where the sort of the lookups starts on its side stream: it needs only the indices, so
     it may run beside the forward too, but the gather's row reuse in L2 suffers from it; it
     starts with the step only when its passes (keys + bag ids read and written per 8-bit
     digit) move more bytes than the interaction backward it would otherwise hide behind."""
     sa = 4 if wl.act_dtype == "f32" else 2
-    key_bits = max(1, int(wl.total_rows - 1).bit_length())
-    sort_bytes = 16 * nnz * ((key_bits + 7) // 8)
+    sort_bytes = 16 * nnz * sort_passes(wl)
     bwd_bytes = wl.batch * wl.out_stride * sa + 2 * wl.batch * (wl.num_tables + 1) * wl.dim * sa
     return "fwd" if sort_bytes > bwd_bytes else "bwd"
 
 
 def source_digest(paths):
-    """sha256 over the given files (repo-relative), in order."""
+    """sha256 over the code of the given files (repo-relative), in order: C/C++ comments
+    removed and whitespace runs folded, so that an edit of comments alone keeps the digest."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in paths:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
-    when there is none for this workload or the kernel's sources changed since it was taken."""
+    """HBM bytes per launch of `kernel` (or the sum over the kernels of a call, joined by
+    " + ") from the committed rocprofv3 counter summary, or None when there is none for this
+    workload or a kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         entries = json.load(f)
-    for e in entries.get("kernels", []):
-        if e["workload"] == workload and e["kernel"] == kernel:
-            if source_digest(e["sources"]) != e["sources_sha256"]:
-                return None
-            return e["bytes_per_launch"]
+    total = 0
+    for k in kernel.split(" + "):
+        hit = [e for e in entries.get("kernels", []) if e["workload"] == workload and e["kernel"] == k]
+        if not hit or source_digest(hit[0]["sources"]) != hit[0]["sources_sha256"]:
+            return None
+        total += hit[0]["bytes_per_launch"]
+    return total
+
+
+def distinct_twin(wl):
+    """Name of the catalogued distinct-row workload with `wl`'s shapes and dtypes, or None."""
+    from embedding_lookup_feature_amd import synth
+    for name, w in synth.WORKLOADS.items():
+        if w.index_dist == "distinct" and (w.batch, tuple(w.rows), w.dim, w.table_dtype, w.act_dtype, w.bag) == \
+                (wl.batch, tuple(wl.rows), wl.dim, wl.table_dtype, wl.act_dtype, wl.bag):
+            return name
     return None
 
 
@@ -328,7 +359,7 @@ def main():
         if side_ev: side_ev[1].record(side)
         prepared.record(side)
 
-    def step(i, ev=None, side_ev=None):
+    def step(i, ev=None, side_ev=None, wait_ev=None):
         """One pass of the path over batch i.  With overlap, the sort of the lookups (it needs
         only the indices) runs on a side stream while the forward and the interaction
         backward run; the update waits for it."""
@@ -360,6 +391,8 @@ def main():
         k += 1
         if overlap:
             torch.cuda.current_stream().wait_event(prepared)
+            if wait_ev is not None:  # the update's own time starts once the sort is done
+                wait_ev.record()
             elf.emb_grad_apply(tab, bags, demb, wl.lr, ws)
         else:
             elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
@@ -412,13 +445,18 @@ def main():
     nev = len(names) + 1
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(i, evs[i], sevs[i] if overlap else None)
+        step(i, evs[i], sevs[i] if overlap else None, wevs[i] if overlap else None)
     torch.cuda.synchronize()
     call_samples = {n: [e[k].elapsed_time(e[k + 1]) for e in evs] for k, n in enumerate(names)}
     if overlap:  # side stream: the sort, overlapping the calls above
         call_samples["emb_grad_prepare"] = [e[0].elapsed_time(e[1]) for e in sevs]
+        if "emb_grad_apply" in names:  # from the end of the wait for the sort
+            ka = names.index("emb_grad_apply")
+            call_samples["wait_for_sort"] = [e[ka].elapsed_time(w) for e, w in zip(evs, wevs)]
+            call_samples["emb_grad_apply"] = [w.elapsed_time(e[ka + 1]) for e, w in zip(evs, wevs)]
     call_ms = {n: float(np.mean(v)) for n, v in call_samples.items()}
 
     # the gather with no row reuse: emb_bag_fwd alone on the same shapes with every table's
@@ -455,10 +493,9 @@ def main():
     sa = 4 if wl.act_dtype == "f32" else 2
     algo["emb_grad_reduce_update"] = 8 * nnz + nnz * D * sa + 2 * U * D * st
     algo["emb_grad_apply"] = algo["emb_grad_reduce_update"]
-    # the sort: keys + bag ids read and written once per 8-bit radix pass
-    key_bits = max(1, int(wl.total_rows - 1).bit_length())
-    algo["emb_grad_prepare"] = 16 * nnz * ((key_bits + 7) // 8)
-    timed = list(call_samples)
+    # the sort: keys + bag ids read and written once per 8-bit radix pass over local rows
+    algo["emb_grad_prepare"] = 16 * nnz * sort_passes(wl)
+    timed = [n for n in call_samples if n != "wait_for_sort"]
     algo = {n: algo[n] for n in timed}
     calls = {}
     for n in timed:
@@ -474,6 +511,11 @@ def main():
             c["stream"] = "side (overlaps " + ("the forward and " if args.overlap_sort == "fwd" else "") + \
                           "the interaction backward)"
         calls[n] = c
+    if "wait_for_sort" in call_samples:
+        v = call_samples["wait_for_sort"]
+        calls["wait_for_sort"] = {"ms": round(float(np.mean(v)), 4), "median_ms": round(pct(v, 50), 4),
+                                  "note": "main stream idle between the interaction backward and "
+                                          "emb_grad_apply, waiting for the side-stream sort"}
     step_bytes = sum(algo[n] for n in names)  # the sort's passes are not counted
     # dominant kernel: the longest of the one-kernel calls (the update call is a sequence of
     # short sort / reduce kernels, each well below the interaction kernels; in training
@@ -484,10 +526,11 @@ def main():
         kernel = kernel_of(dom, wl)
     else:  # a forward-only line whose one call runs the gather and the interaction in chunks
         dom, kernel = names[0], "k_emb_bag_fwd + interaction forward"
-    def roofline_of(call, kernel, ms, nbytes, note=None):
+    def roofline_of(call, kernel, ms, nbytes, note=None, traffic_workload=None):
         a = nbytes / (ms * 1e-3) / 1e9
         r = {"bound": "hbm", "kernel": kernel, "call": call, "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,
-             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(wl.name, kernel)}
+             "unit": "GB/s", "frac": round(a / HBM_PEAK_GBPS, 4),
+             "traffic": measured_traffic(traffic_workload or wl.name, kernel)}
         ck, cg = ceiling_of(call, wl, calib)
         if cg:
             r.update({"ceiling": ck, "ceiling_gbps": cg, "frac_of_ceiling": round(a / cg, 4)})
@@ -500,13 +543,15 @@ def main():
     upd = "emb_grad_apply" if "emb_grad_apply" in call_ms else (
         "emb_grad_reduce_update" if "emb_grad_reduce_update" in call_ms else None)
     if upd:
-        rooflines.append(roofline_of(upd, "k_seg_chunk + k_seg_fixup", call_ms[upd], algo[upd],
+        rooflines.append(roofline_of(upd, "k_seg_reduce + k_seg_fixup", call_ms[upd], algo[upd],
                                      "the update's kernels in sequence; HIP-event time of the call"))
     if uniform is not None:
         gb = algorithmic_bytes(wl, nnz)["emb_bag_fwd"]
         rooflines.append(roofline_of("emb_bag_fwd", "k_emb_bag_fwd", uniform, gb,
                                      "control on the workload's shapes with every table's lookups distinct "
-                                     "rows (no row reuse), mean of 20 HIP-event timed calls"))
+                                     "rows (no row reuse), mean of 20 HIP-event timed calls; traffic from the "
+                                     "counters of the distinct-row workload of the same shapes (another seed "
+                                     "of the same draw)", traffic_workload=distinct_twin(wl)))
 
     result = {
         "metric": metric_name(wl),

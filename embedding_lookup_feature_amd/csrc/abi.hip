@@ -46,6 +46,8 @@ el_status check_tables(const el_tables* tab, const char* fn) {
   if ((tab->dim * dtype_size(tab->dtype)) % 16 != 0)
     return set_error(EL_ERR_UNSUPPORTED, std::string(fn) + ": dim * sizeof(dtype) must be a multiple of 16 bytes");
   if (!aligned(tab->row_offset, 8)) return bad(fn, "row_offset must be 8-byte aligned");
+  if (tab->max_rows < 0 || tab->max_rows > tab->total_rows)
+    return bad(fn, "max_rows must be in [0, total_rows]");
   return EL_OK;
 }
 
@@ -132,7 +134,7 @@ el_status check_grad_call(const char* fn, const el_tables* tab, const el_bags* b
   EL_TRY(check_tables(tab, fn));
   EL_TRY(check_bags(tab, bags, fn));
   if (flags & ~static_cast<uint32_t>(EL_FLAG_HASH_INDICES)) return bad(fn, "unknown flags");
-  const size_t need = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, nullptr).bytes;
+  const size_t need = plan_grad_workspace(*tab, bags->nnz, nullptr).bytes;
   if (need > 0) {
     if (!workspace) return set_error(EL_ERR_WORKSPACE, std::string(fn) + ": workspace is null");
     if (!aligned(workspace, 256)) return bad(fn, "workspace must be 256-byte aligned");
@@ -274,7 +276,7 @@ el_status emb_cat_fwd(const el_tables* tab, const el_bags* bags, uint32_t flags,
 size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags) {
   if (check_tables(tab, "emb_grad_workspace_bytes") != EL_OK) return 0;
   if (check_bags(tab, bags, "emb_grad_workspace_bytes") != EL_OK) return 0;
-  return plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, nullptr).bytes;
+  return plan_grad_workspace(*tab, bags->nnz, nullptr).bytes;
 }
 
 
@@ -286,7 +288,7 @@ el_status emb_grad_reduce_update(const el_tables* tab, const el_bags* bags, uint
   EL_TRY(check_grad_input(fn, tab, grad_dtype));
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
   EL_TRY(check_dense(fn, demb, true, "demb"));
-  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  GradWorkspace ws = plan_grad_workspace(*tab, bags->nnz, workspace);
   uint32_t *keys = nullptr, *vals = nullptr;
   EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
   return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
@@ -302,7 +304,7 @@ el_status emb_grad_reduce_update_noalloc(const el_tables* tab, const el_bags* ba
   EL_TRY(check_grad_input(fn, tab, grad_dtype));
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
   EL_TRY(check_dense(fn, demb, true, "demb"));
-  const size_t need = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, nullptr).bytes;
+  const size_t need = plan_grad_workspace(*tab, bags->nnz, nullptr).bytes;
   if (need > kNoallocScratchBytes) {
     char buf[200];
     std::snprintf(buf, sizeof buf, "%s: %zu bytes of scratch needed, the library's static scratch holds %zu",
@@ -311,7 +313,7 @@ el_status emb_grad_reduce_update_noalloc(const el_tables* tab, const el_bags* ba
   }
   void* scratch_ptr = nullptr;
   EL_TRY(noalloc_scratch(fn, &scratch_ptr));
-  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, scratch_ptr);
+  GradWorkspace ws = plan_grad_workspace(*tab, bags->nnz, scratch_ptr);
   uint32_t *keys = nullptr, *vals = nullptr;
   EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
   return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
@@ -322,7 +324,7 @@ el_status emb_grad_prepare(const el_tables* tab, const el_bags* bags, uint32_t f
   const char* fn = "emb_grad_prepare";
   EL_TRY(check_grad_call(fn, tab, bags, flags, workspace, workspace_bytes));
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
-  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  GradWorkspace ws = plan_grad_workspace(*tab, bags->nnz, workspace);
   uint32_t *keys = nullptr, *vals = nullptr;
   return launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream);
 }
@@ -335,7 +337,7 @@ el_status emb_grad_apply(const el_tables* tab, const el_bags* bags, uint32_t fla
   EL_TRY(check_grad_input(fn, tab, grad_dtype));
   if (bags->batch == 0 || bags->nnz == 0) return EL_OK;
   EL_TRY(check_dense(fn, demb, true, "demb"));
-  GradWorkspace ws = plan_grad_workspace(bags->nnz, tab->dim, tab->total_rows, workspace);
+  GradWorkspace ws = plan_grad_workspace(*tab, bags->nnz, workspace);
   uint32_t *keys = nullptr, *vals = nullptr;
   sorted_buffers(ws, &keys, &vals);
   return launch_reduce_update(*tab, *bags, ws, keys, vals, demb, grad_dtype, lr, stream);
@@ -350,7 +352,7 @@ el_status emb_grad_sort(const el_tables* tab, const el_bags* bags, uint32_t flag
   if (!seg_offsets || !num_unique) return bad(fn, "seg_offsets / num_unique is null");
   const bool any = bags->batch > 0 && bags->nnz > 0;
   if (any && (!sorted_rows || !bag_ids || !unique_rows)) return bad(fn, "output array is null");
-  GradWorkspace ws = plan_grad_workspace(any ? bags->nnz : 0, tab->dim, tab->total_rows, workspace);
+  GradWorkspace ws = plan_grad_workspace(*tab, any ? bags->nnz : 0, workspace);
   if (!any) return launch_segments(ws, nullptr, unique_rows, seg_offsets, num_unique, stream);
   uint32_t *keys = nullptr, *vals = nullptr;
   EL_TRY(launch_grad_sort_core(*tab, *bags, flags, ws, &keys, &vals, stream));
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(256) void k_validate(const int64_t* __restrict__ ro
                                                   const int32_t* __restrict__ idx,
                                                   const int32_t* __restrict__ off, int32_t F,
                                                   int32_t B, int64_t nnz, uint32_t hash,
-                                                  int64_t* __restrict__ bad_count) {
+                                                  int64_t max_rows, int64_t* __restrict__ bad_count) {
   __shared__ int64_t part[4];
   const int64_t nbags = static_cast<int64_t>(F) * B;
   int64_t bad = 0;
@@ -430,6 +432,9 @@ __global__ __launch_bounds__(256) void k_validate(const int64_t* __restrict__ ro
     if (off[0] != 0) ++bad;
     if (off[nbags] != nnz) ++bad;
   }
+  if (blockIdx.x == 0 && max_rows > 0)  // tables larger than the declared largest
+    for (int t = threadIdx.x; t < F; t += 256)
+      if (row_off[t + 1] - row_off[t] > max_rows) ++bad;
   for (int64_t g = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; g < nbags;
        g += static_cast<int64_t>(gridDim.x) * 256) {
     const int32_t s = off[g], e = off[g + 1];
@@ -467,7 +472,7 @@ el_status launch_validate(const el_tables& tab, const el_bags& bags, uint32_t fl
   blocks = blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks);
   hipLaunchKernelGGL(k_validate, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, tab.row_offset,
                      bags.indices, bags.offsets, tab.num_tables, bags.batch, bags.nnz,
-                     (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u, bad_count);
+                     (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u, tab.max_rows, bad_count);
   return check_launch("el_validate_bags");
 }
 

@@ -135,15 +135,24 @@ el_status launch_emb_dot_bwd(const el_tables& tab, const el_bags& bags, uint32_t
                              const void* x0, el_dtype act_dtype, const void* dout, int out_stride,
                              void* dx0, void* demb, el_dtype grad_dtype, hipStream_t stream);
 
+// One tile of the gradient sort: `count` (<= kSortTile) lookups of table t from position
+// `start`; the table's lookups start at `seg_start` and own the tiles [first, end).  A tile
+// past the last one has count 0.
+struct SortTile {
+  int32_t t, start, count, seg_start, first, end, pad0, pad1;
+};
+
 // Workspace of the gradient path; all pointers 256-byte aligned inside one allocation.
 struct GradWorkspace {
   int64_t n = 0;        // lookups
   int passes = 0;       // radix passes
   int rbits = 0;        // digit width of every pass
-  int64_t nblocks = 0;  // radix tiles
+  int64_t nblocks = 0;  // radix tiles (an upper bound: ceil(n / tile) + tables)
   int64_t nranges = 0;  // reduce ranges (an upper bound: ranges of the fewest lookups)
   size_t bytes = 0;
   uint32_t *keys0 = nullptr, *vals0 = nullptr, *keys1 = nullptr, *vals1 = nullptr;
+  int32_t* tile_prefix = nullptr;  // [F+1] tiles of the tables before t
+  SortTile* tiles = nullptr;       // [nblocks]
   uint32_t *hist = nullptr, *hist_scan = nullptr;  // digit-major tile counts, scanned per digit
   uint32_t* dtotal = nullptr;                       // per digit: keys with that digit
   uint32_t *flags = nullptr, *flags_scan = nullptr;
@@ -157,13 +166,14 @@ struct GradWorkspace {
 };
 
 constexpr int kRadixBits = 8;  // widest radix digit (wider digits measured slower)
+static_assert(kRadixBits <= 8, "the sort's histogram and scatter kernels take digits of at most 8 bits");
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
 constexpr int kChunk = 16;         // lookups per lane group in the reduce
 constexpr int kMinRange = 4 * kChunk;  // fewest lookups per reduce range (four lane groups)
 
-// Lay out the workspace in `base` (nullptr: only compute the size).
-GradWorkspace plan_grad_workspace(int64_t n, int D, int64_t total_rows, void* base);
+// Lay out the workspace for n lookups into `tab` in `base` (nullptr: only compute the size).
+GradWorkspace plan_grad_workspace(const el_tables& tab, int64_t n, void* base);
 
 // Build keys, radix-sort them; returns the buffers holding the sorted keys / bag ids.
 el_status launch_grad_sort_core(const el_tables& tab, const el_bags& bags, uint32_t flags,

@@ -35,7 +35,7 @@ class EmbcoreError(RuntimeError):
 class ElTables(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("row_offset", ctypes.c_void_p),
                 ("total_rows", ctypes.c_int64), ("num_tables", ctypes.c_int32),
-                ("dim", ctypes.c_int32), ("dtype", ctypes.c_int)]
+                ("dim", ctypes.c_int32), ("dtype", ctypes.c_int), ("max_rows", ctypes.c_int64)]
 
 
 class ElBags(ctypes.Structure):
@@ -143,14 +143,21 @@ class Tables:
     """F embedding tables in one joint [total_rows, D] buffer; table t owns rows
     row_offset[t] .. row_offset[t+1]-1."""
 
-    def __init__(self, weight: torch.Tensor, row_offset: torch.Tensor, total_rows: int = None):
+    def __init__(self, weight: torch.Tensor, row_offset: torch.Tensor, total_rows: int = None,
+                 max_rows: int = None):
+        """max_rows: rows of the largest table; None reads it from row_offset (one copy to the
+        host, here and not per call), 0 leaves it unknown."""
         if weight.dim() != 2 or row_offset.dtype != torch.int64 or row_offset.dim() != 1:
             raise ValueError("weight must be [total_rows, D]; row_offset int64 [F+1]")
         self.weight = weight
         self.row_offset = row_offset
         self.total_rows = int(weight.shape[0] if total_rows is None else total_rows)
+        if max_rows is None:
+            ro = row_offset.cpu()
+            max_rows = int((ro[1:] - ro[:-1]).max()) if ro.numel() > 1 else 0
+        self.max_rows = int(max_rows)
         self.c = ElTables(_dev(weight, "weight"), _dev(row_offset, "row_offset"), self.total_rows,
-                          row_offset.numel() - 1, weight.shape[1], _dtype(weight, "weight"))
+                          row_offset.numel() - 1, weight.shape[1], _dtype(weight, "weight"), self.max_rows)
 
     @property
     def num_tables(self):

@@ -10,13 +10,17 @@
  *
  * Conventions shared by every call
  *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all memory; the
- *     library allocates nothing and keeps no state between calls.
+ *     library allocates nothing and keeps no state between calls, except the static
+ *     scratch array of emb_grad_reduce_update_noalloc (one per GPU, see there).
  *   - Work is enqueued on `stream` and runs asynchronously; no call synchronises.
  *   - Arguments are validated on the host before anything is enqueued.  A call that
  *     returns a status other than EL_OK has enqueued nothing, except EL_ERR_HIP, which
  *     reports a launch failure (text from el_last_error()).
  *   - Outputs must not alias inputs.  Only emb_grad_reduce_update writes to the tables.
- *   - Every call with the same inputs produces bitwise identical outputs (no atomics).
+ *   - Every call with the same inputs produces bitwise identical outputs: no call adds
+ *     floating-point values with atomics.  The integer atomics that remain (the radix
+ *     sort's LDS digit counters, el_validate_bags' defect count) give exact counts in any
+ *     order.
  *   - Float conversions round to nearest even; denormals are kept; NaN stays NaN.
  */
 #ifndef EMBCORE_H
@@ -63,6 +67,13 @@ typedef struct {
   int32_t num_tables;        /* F >= 1 */
   int32_t dim;               /* D >= 1 */
   el_dtype dtype;
+  int64_t max_rows;          /* [host] rows of the largest table (>= every
+                                row_offset[t+1] - row_offset[t], <= total_rows), or 0 if not
+                                known.  Only the embedding-gradient sort reads it: it sorts
+                                each table's lookups by their local row, on the fewest bits
+                                that hold max_rows - 1 (total_rows - 1 when 0); a value below
+                                the largest table's rows breaks that sort (el_validate_bags
+                                detects it). */
 } el_tables;
 
 /* Lookups in CSR form over F*B bags, table-major: bag (t, b) has number g = t*B + b and
@@ -199,7 +210,8 @@ EL_API size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags
  * Rows that are not looked up are not written.  The lookups are sorted by global row with
  * a stable, deterministic LSD radix sort; equal rows form segments that are reduced in
  * fixed-size chunks (fp32) with an ordered fix-up for segments spanning chunks.  No
- * atomics: the result is bitwise reproducible.
+ * floating-point atomics (the sort's digit histograms count with integer LDS atomics, exact
+ * in any order): the result is bitwise reproducible.
  * demb: [B][F][D] of grad_dtype, 16-byte aligned.  workspace: >= emb_grad_workspace_bytes,
  * 256-byte aligned, contents on entry irrelevant.
  */
@@ -260,10 +272,11 @@ EL_API el_status emb_grad_sort(const el_tables* tab, const el_bags* bags, uint32
 
 /*
  * Count defects of a CSR batch: offsets that decrease, offsets[0] != 0,
- * offsets[F*B] != nnz, and (without EL_FLAG_HASH_INDICES) indices outside their table.
+ * offsets[F*B] != nnz, (without EL_FLAG_HASH_INDICES) indices outside their table, and
+ * (when tab->max_rows > 0) tables with more than max_rows rows.
  * bad_count: [1] int64 device, overwritten with the total.  A grid of workgroups scans the
  * bags; their subtotals are added with integer atomics (the count is exact whatever the
- * order).  Not part of the computation: the other calls use no atomics.
+ * order).  Not part of the computation.
  */
 EL_API el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t flags,
                            int64_t* bad_count, hipStream_t stream);

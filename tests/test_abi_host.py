@@ -12,8 +12,8 @@ INVALID, UNSUPPORTED, WORKSPACE = ec.EL_ERR_INVALID_ARG, ec.EL_ERR_UNSUPPORTED, 
 A = 0x7F0000000000
 
 
-def tables(F=26, D=128, rows=100_000, dtype=ec.EL_F32, base=A, row_offset=A + 0x1000):
-    return ec.ElTables(base, row_offset, F * rows, F, D, dtype)
+def tables(F=26, D=128, rows=100_000, dtype=ec.EL_F32, base=A, row_offset=A + 0x1000, max_rows=0):
+    return ec.ElTables(base, row_offset, F * rows, F, D, dtype, max_rows)
 
 
 def bags(F=26, B=65536, nnz=None, indices=A + 0x2000, offsets=A + 0x3000):
@@ -50,6 +50,12 @@ def test_workspace_bytes_is_host_pure_and_scales():
     assert big >= 6 * 4 * nnz
     assert L.emb_grad_workspace_bytes(ref(tables()), ref(bags(B=0, nnz=0))) == 0
     assert L.emb_grad_workspace_bytes(None, ref(bags())) == 0
+    # a declared largest table: the sort works on fewer bits (17 instead of 22 here), so
+    # no more workspace than without it; beyond the total it is refused
+    declared = L.emb_grad_workspace_bytes(ref(tables(max_rows=100_000)), ref(bags()))
+    assert 0 < declared <= big
+    assert L.emb_grad_workspace_bytes(ref(tables(max_rows=26 * 100_000 + 1)), ref(bags())) == 0
+    assert L.emb_grad_workspace_bytes(ref(tables(max_rows=-1)), ref(bags())) == 0
 
 
 @pytest.mark.parametrize("tab,bg,flags,out,odt,status", [
@@ -221,6 +227,9 @@ def test_table_row_limits():
     L = ec.lib()
     t = ec.ElTables(A, A, 1 << 32, 1, 128, ec.EL_F32)  # 2^32 rows: keys would not fit 32 bits
     assert L.emb_bag_fwd(ref(t), ref(bags(F=1)), 0, A, ec.EL_F32, None) == INVALID
+    t = tables(max_rows=26 * 100_000 + 1)  # a table larger than all rows together
+    assert L.emb_bag_fwd(ref(t), ref(bags()), 0, A, ec.EL_F32, None) == INVALID
+    assert b"max_rows" in L.el_last_error()
 
 
 def test_dense_layer_calls_reject_on_the_host():

@@ -406,8 +406,8 @@ def grad_problem(case):
     return wl, W, ro, idx, off
 
 
-def run_sort(W, ro, idx, off, B, hsh):
-    tab, bags = elf.Tables(W, ro), elf.Bags(idx, off, B)
+def run_sort(W, ro, idx, off, B, hsh, max_rows=None):
+    tab, bags = elf.Tables(W, ro, max_rows=max_rows), elf.Bags(idx, off, B)
     ws = elf.alloc_workspace(tab, bags)
     n = idx.numel()
     outs = [torch.full((max(n, 1),), -1, dtype=torch.int32, device=DEV) for _ in range(3)]
@@ -430,6 +430,47 @@ def test_emb_grad_sort_bit_exact(case):
     assert_bits(bag_ids[:idx.numel()], ref["bag_ids"].view(np.int32), "bag_ids")
     assert_bits(uniq[:U], ref["unique_rows"].view(np.int32), "unique_rows")
     assert_bits(seg[:U + 1], ref["seg_offsets"].view(np.int32), "seg_offsets")
+
+
+@pytest.mark.parametrize("declared", ["unknown", "all-rows", "largest-plus-one"])
+def test_emb_grad_sort_with_other_declared_table_sizes(declared):
+    """The sort works on the bits of the declared largest table; an unknown size (0) or a
+    larger one than needed changes the passes, never the result."""
+    case = [c for c in SORT_CASES if c[0] == "f16-table-f32-grad"][0]
+    wl, W, ro, idx, off = grad_problem(case)
+    mr = {"unknown": 0, "all-rows": wl.total_rows, "largest-plus-one": max(wl.rows) + 1}[declared]
+    (srt, bag_ids, uniq), seg, nu = run_sort(W, ro, idx, off, wl.batch, False, max_rows=mr)
+    ref = orc.grad_sort(to_np(ro), to_np(idx), to_np(off), wl.batch, hash_indices=False)
+    U = ref["num_unique"]
+    assert int(nu.item()) == U
+    assert_bits(srt.view(torch.int32)[:idx.numel()], ref["sorted_rows"].view(np.int32), "sorted_rows")
+    assert_bits(bag_ids[:idx.numel()], ref["bag_ids"].view(np.int32), "bag_ids")
+    assert_bits(seg[:U + 1], ref["seg_offsets"].view(np.int32), "seg_offsets")
+
+
+def test_emb_grad_sort_tables_without_lookups():
+    """Tables whose bags are all empty own no sort tile; the tables around them still sort
+    in place (first, middle and last table empty in turn, long tables spanning tiles)."""
+    rows = (70_000, 30, 5000, 123_457)
+    wl = base_wl(batch=3000, rows=rows, dim=16, table_dtype="f32", act_dtype="f32",
+                 index_dist="uniform", bag=("poisson", 3.0, 0, 8))
+    W, ro, idx, off = make_problem(wl)
+    B, F = wl.batch, len(rows)
+    lens = (off[1:] - off[:-1]).view(F, B).clone()
+    for empty in (0, 2, F - 1):
+        ln = lens.clone()
+        ln[empty] = 0
+        off2 = torch.zeros(F * B + 1, dtype=torch.int32, device=DEV)
+        off2[1:] = torch.cumsum(ln.reshape(-1), 0).to(torch.int32)
+        keep = torch.repeat_interleave(torch.ones(F, dtype=torch.bool, device=DEV).index_fill(0, torch.tensor([empty], device=DEV), False),
+                                       lens.sum(dim=1))
+        idx2 = idx[keep].contiguous()
+        (srt, bag_ids, uniq), seg, nu = run_sort(W, ro, idx2, off2, B, False)
+        ref = orc.grad_sort(to_np(ro), to_np(idx2), to_np(off2), B, hash_indices=False)
+        U = ref["num_unique"]
+        assert int(nu.item()) == U, empty
+        assert_bits(srt.view(torch.int32)[:idx2.numel()], ref["sorted_rows"].view(np.int32), f"sorted_rows, table {empty} empty")
+        assert_bits(bag_ids[:idx2.numel()], ref["bag_ids"].view(np.int32), f"bag_ids, table {empty} empty")
 
 
 def test_emb_grad_sort_degenerate():
@@ -552,6 +593,11 @@ def test_validate_bags_counts_defects():
     bad_off[5] = bad_off[6] + 1  # decreasing pair
     elf.el_validate_bags(tab, elf.Bags(idx, bad_off, 100), cnt)
     assert int(cnt.item()) >= 1
+    # a declared largest table below the real one (table 1 has 20 rows)
+    elf.el_validate_bags(elf.Tables(W, ro, max_rows=15), elf.Bags(idx, off, 100), cnt)
+    assert int(cnt.item()) == 1
+    elf.el_validate_bags(elf.Tables(W, ro, max_rows=0), elf.Bags(idx, off, 100), cnt)
+    assert int(cnt.item()) == 0
 
 
 def test_tiny_training_step_chain_matches_oracle_chain():
