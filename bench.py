@@ -766,7 +766,7 @@ def dlrm_cpu_baseline(wl, W, ro, step, batch, seconds):
             "host_cpu": model, "host_cpus_visible": nproc}
 
 
-def inference_sweep(dev, workload, sizes=(1, 16, 256, 4096, 65536, 262144, 1048576), iters=100):
+def inference_sweep(dev, workload, sizes=(1, 16, 64, 256, 4096, 65536, 262144, 1048576), iters=100):
     """Forward-only serving figure: for each batch size, `iters` single calls of emb_dot_fwd
     (gather + interaction, pooled vectors kept on chip), each timed with its own HIP events;
     latency percentiles and samples/s = B / mean latency.  Two index batches alternate."""

@@ -320,11 +320,17 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
   const int VP = NT * 32;
   const int DT = (D + 31) / 32;  // D % 16 == 0; a last tile of 16 rows is half empty
   const int tpitch = VP * 2 + 16;
+  // DS (gradient row in registers, up to 128 vectors): S is built densely in LDS from the
+  // registers and only the gradient row's first D elements (dx0's direct term) are kept;
+  // otherwise the whole gradient row is staged and S is read from it element by element
+  constexpr bool DS = GPT == 3;
   const int goff = D * tpitch;
   const int gchunks = (D + P + 7) / 8;
   const uint16_t* G = reinterpret_cast<const uint16_t*>(lds + goff);
+  const int spitch = VP * 2 + 16;  // dense S row pitch (DS)
+  const int soff = goff + D * 2;   // D % 16 == 0: 16-byte aligned
   const int opitch = D * GSZ + 16;
-  const int ooff = goff + gchunks * 16;
+  const int ooff = DS ? soff + VP * spitch : goff + gchunks * 16;
   const int r0off = ooff + VP * opitch;  // dV_0, fp32
   const int trash = r0off + D * 4;
   const int KS = (V + 15) / 16;
@@ -507,7 +513,36 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
         *reinterpret_cast<uint32_t*>(lds + off) = word;
       }
     }
-    if constexpr (GPT > 0) {
+    if constexpr (DS) {
+      // chunk q holds elements 8q .. 8q+7 of the gradient row: the direct term (q < D/8,
+      // kept for dx0) or pairs p = element - D, each written to S[i][j] and S[j][i]
+      // (p = i(i-1)/2 + j, j < i); the diagonal and the padding of S stay zero
+#pragma unroll
+      for (int gg = 0; gg < GPT; ++gg) {
+        const int q = gg * 256 + tid;
+        if (q < D / 8) {
+          *reinterpret_cast<u32x4*>(lds + goff + q * 16) = g[BF][gg];
+        } else if (q < gchunks) {
+          int p = q * 8 - D;
+          int i = static_cast<int>((1.0f + sqrtf(1.0f + 8.0f * static_cast<float>(p))) * 0.5f);
+          while (i * (i - 1) / 2 > p) --i;
+          while ((i + 1) * i / 2 <= p) ++i;
+          int j = p - i * (i - 1) / 2;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (p + e < P) {
+              const uint16_t sv = static_cast<uint16_t>(g[BF][gg][e >> 1] >> ((e & 1) * 16));
+              *reinterpret_cast<uint16_t*>(lds + soff + i * spitch + j * 2) = sv;
+              *reinterpret_cast<uint16_t*>(lds + soff + j * spitch + i * 2) = sv;
+            }
+            if (++j == i) {
+              ++i;
+              j = 0;
+            }
+          }
+        }
+      }
+    } else if constexpr (GPT > 0) {
 #pragma unroll
       for (int gg = 0; gg < GPT; ++gg) {
         const int q = gg * 256 + tid;
@@ -548,10 +583,19 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
     __syncthreads();
     int cur_vt = -1;
     u32x4 Sop[KSM];  // S[v][k], k = 16 ks + 8 half + e
-    for (int tile = wave; tile < NT * DT; tile += 4) {
+    // each wavefront takes a run of consecutive tiles in row-tile-major order, so that it
+    // builds the S operand of a row tile once and reuses it across the column tiles
+    const int tpw = (NT * DT + 3) / 4;
+    const int tile_end = min((wave + 1) * tpw, NT * DT);
+    for (int tile = wave * tpw; tile < tile_end; ++tile) {
       const int vt = tile / DT, dt = tile - vt * DT;
       const int v = vt * 32 + col;
-      if (vt != cur_vt) {  // wave-uniform
+      if (vt != cur_vt && DS) {  // wave-uniform: S[v][16 ks + 8 half ..], one aligned read
+        cur_vt = vt;
+#pragma unroll
+        for (int ks = 0; ks < KSM; ++ks)
+          Sop[ks] = *reinterpret_cast<const u32x4*>(lds + soff + v * spitch + (ks * 16 + half * 8) * 2);
+      } else if (vt != cur_vt) {  // wave-uniform
         cur_vt = vt;
 #pragma unroll
         for (int ks = 0; ks < KSM; ++ks) {
@@ -623,6 +667,11 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
 
   int b = blockIdx.x;
   if (b >= B) return;
+  if constexpr (DS) {  // S's diagonal and padding are never written: zero once
+    for (int o = tid * 16; o < VP * spitch; o += 256 * 16)
+      *reinterpret_cast<u32x4*>(lds + soff + o) = u32x4{0, 0, 0, 0};
+    __syncthreads();
+  }
   // Prologue loads land before the loop (settle), so that the wait counts the compiler
   // derives for the loop are those of its steady state alone.
   if constexpr (GATHER) {
@@ -871,6 +920,16 @@ size_t bwd_lds_bytes(int F, int D, size_t gsz) {
          static_cast<size_t>(D) * 4 + 16;
 }
 
+// LDS bytes of the dense-S class (gradient row in registers): V^T | dx0's direct term (D
+// elements) | S [VP][VP] (pitch 2 VP + 16) | output block | dV_0 in fp32 | scratch slot.
+// Two workgroups per CU of up to kMaxLdsDense bytes fit the 160 KB of LDS.
+constexpr size_t kMaxLdsDense = 80 * 1024;
+size_t bwd_lds_bytes_dense(int F, int D, size_t gsz) {
+  const size_t VP = static_cast<size_t>((F + 1 + 31) / 32 * 32);
+  return static_cast<size_t>(D) * (VP * 2 + 16) + static_cast<size_t>(D) * 2 + VP * (VP * 2 + 16) +
+         VP * (D * gsz + 16) + static_cast<size_t>(D) * 4 + 16;
+}
+
 template <class TT, class IT, class GT>
 el_status launch_emb_dot_bwd_t(const el_tables& tab, const el_bags& bags, uint32_t flags,
                                const void* x0, const void* dout, int out_stride, void* dx0,
@@ -913,8 +972,11 @@ el_status launch_bwd_mfma(const void* x0, const void* emb, int B, int F, int D, 
     if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 4, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   } else if (V <= 128) {
-    if (units <= 512 && gchunks <= 768)
-      return launch_bwd_t<IT, GT, 2, 3, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
+    if (units <= 512 && gchunks <= 768) {
+      const size_t dlds = bwd_lds_bytes_dense(F, D, sizeof(typename GT::S));
+      if (dlds <= kMaxLdsDense)
+        return launch_bwd_t<IT, GT, 2, 3, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, dlds, stream);
+    }
     if (units <= 512) return launch_bwd_t<IT, GT, 2, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
     if (units <= 1024) return launch_bwd_t<IT, GT, 4, 0, 8, 1>(x0, emb, B, F, D, dout, out_stride, dx0, demb, lds, stream);
   }

@@ -169,8 +169,10 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
   constexpr int kSteps = kSortTile / 256;
   constexpr int kLaneGroups = 8;  // sub-histograms per wavefront
   constexpr int kSub = 4 * kLaneGroups;
-  __shared__ uint32_t cnt[kSub][kRadix];
-  for (int i = threadIdx.x; i < kSub * kRadix; i += 256) (&cnt[0][0])[i] = 0;
+  // one pad word per sub-histogram: a digit's counters in the different sub-histograms
+  // then fall in different LDS banks
+  __shared__ uint32_t cnt[kSub][kRadix + 1];
+  for (int i = threadIdx.x; i < kSub * (kRadix + 1); i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
   const SortTile ti = tiles[blockIdx.x];
   const int sub = (threadIdx.x >> 6) * kLaneGroups + (threadIdx.x & 63) % kLaneGroups;

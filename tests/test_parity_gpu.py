@@ -195,6 +195,10 @@ BWD_CASES = [
     ("f16-27x128", 26, 128, "f16", "f16", "f16", None, 300),
     ("bf16-101x64", 100, 64, "bf16", "bf16", "bf16", None, 60),
     ("bf16-101x64-odd-stride", 100, 64, "bf16", "bf16", "bf16", 5114 + 1, 20),
+    # the dense-S class over several samples per workgroup, and at another padded width
+    # (96 vectors) with fp32 gradients
+    ("bf16-101x64-many-trips", 100, 64, "bf16", "bf16", "bf16", None, 3001),
+    ("bf16-80x80-f32-grad", 79, 80, "bf16", "bf16", "f32", None, 700),
     ("bf16-two-vectors-d32", 1, 32, "bf16", "bf16", "f32", None, 64),
     ("bf16-33-vectors", 32, 32, "bf16", "bf16", "bf16", None, 99),
     ("bf16-128-vectors", 127, 32, "bf16", "bf16", "bf16", None, 8),
