@@ -63,6 +63,28 @@ __device__ inline Raw<T, N> load_raw(const typename T::S* p) {
   return r;
 }
 
+// The same from the table: non-temporal, since every table row the update touches is read
+// once and written once, and the cache space is better left to the gradient rows (a
+// multi-hot bag's gradient row is read once per lookup of the bag).
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T, int N>
+__device__ inline Raw<T, N> load_raw_nt(const typename T::S* p) {
+  Raw<T, N> r;
+  if constexpr (Raw<T, N>::NW == 2) {
+    const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < Raw<T, N>::NW / 4; ++i) {
+      const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p) + i);
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  }
+  return r;
+}
+
 template <class T, int N>
 __device__ inline void raw_to_f(const Raw<T, N>& r, float* f) {
   if constexpr (sizeof(typename T::S) == 4) {
@@ -85,7 +107,25 @@ __device__ inline void sgd_store(typename WT::S* w, const Raw<WT, N>& old, const
   raw_to_f<WT, N>(old, cur);
 #pragma unroll
   for (int i = 0; i < N; ++i) cur[i] = fmaf(-lr, g[i], cur[i]);
-  store_n<WT, N>(w, cur);
+  // non-temporal stores of the rounded row (see load_raw_nt)
+  constexpr int NW = Raw<WT, N>::NW;
+  uint32_t wd[NW];
+  if constexpr (sizeof(typename WT::S) == 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) wd[i] = __float_as_uint(cur[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i)
+      wd[i] = static_cast<uint32_t>(WT::from_f(cur[2 * i])) | (static_cast<uint32_t>(WT::from_f(cur[2 * i + 1])) << 16);
+  }
+  if constexpr (NW == 2) {
+    __builtin_nontemporal_store(nt_u32x2{wd[0], wd[1]}, reinterpret_cast<nt_u32x2*>(w));
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW / 4; ++i)
+      __builtin_nontemporal_store(nt_u32x4{wd[4 * i], wd[4 * i + 1], wd[4 * i + 2], wd[4 * i + 3]},
+                                  reinterpret_cast<nt_u32x4*>(w) + i);
+  }
 }
 
 // First local position i in [0, hi] of the range with key(i) == k (k occurs at hi).
@@ -174,7 +214,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
       for (int q = 0; q < SUB; ++q) {
         const bool ends = q < hc && kq[q] != kq[q + 1];
         if (ends && kq[q] != kbefore) {
-          wold[q] = load_raw<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0);
+          wold[q] = load_raw_nt<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0);
         } else {
 #pragma unroll
           for (int x = 0; x < Raw<WT, EPL>::NW; ++x) wold[q].w[x] = 0u;
@@ -298,7 +338,7 @@ __global__ __launch_bounds__(256) void k_seg_fixup(
   for (int m = 0; m < NV; ++m) {
     const int v = gl + m * LF;
     const int vo = (v * 4 < D ? v : 0) * 4;
-    wold[m] = load_raw<WT, 4>(W + static_cast<int64_t>(key) * D + vo);
+    wold[m] = load_raw_nt<WT, 4>(W + static_cast<int64_t>(key) * D + vo);
     const uint4 t = *reinterpret_cast<const uint4*>(rtail + w * D + vo);
     tot[m][0] = __uint_as_float(t.x); tot[m][1] = __uint_as_float(t.y);
     tot[m][2] = __uint_as_float(t.z); tot[m][3] = __uint_as_float(t.w);
