@@ -44,7 +44,8 @@ KERNEL_SOURCES["k_dot_fwd_valu"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
 KERNEL_SOURCES["k_dot_fwd_wide"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
 KERNEL_SOURCES["k_dot_bwd_valu"] = KERNEL_SOURCES["k_dot_bwd_mfma"]
 for _k, _f in (("k_seg_reduce", "grad_update.hip"), ("k_seg_fixup", "grad_update.hip"),
-               ("k_build_keys", "grad_sort.hip"), ("k_radix_hist", "grad_sort.hip"),
+               ("k_build_vals", "grad_sort.hip"), ("k_sort_tiles", "grad_sort.hip"),
+               ("k_tile_info", "grad_sort.hip"), ("k_radix_hist", "grad_sort.hip"),
                ("k_radix_scatter", "grad_sort.hip"), ("k_digit_scan", "grad_sort.hip")):
     KERNEL_SOURCES[_k] = ["include/embcore.h", "embedding_lookup_feature_amd/csrc/el_internal.hpp",
                           "embedding_lookup_feature_amd/csrc/" + _f]

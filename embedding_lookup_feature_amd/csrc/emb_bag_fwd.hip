@@ -18,7 +18,16 @@
 //      b * ostride + ocol + t * D of the output (the [B][F][D] array: ostride = F*D,
 //      ocol = 0; the cat interaction's output rows: ostride = out_stride, ocol = D).
 // A wave never waits for its own stores (on this architecture loads and stores share one
-// completion counter), and a new wave takes its slot as soon as it is done.  Sums are fp32
+// completion counter), and a new wave takes its slot as soon as it is done.
+//
+// Long bags (on average four lookups or more, rows of at least 128 bytes): k_emb_bag_long
+// gives each group one bag, so a wave's NG bags advance side by side instead of a group's
+// U bags one after another.  A group walks its bag in rounds of R = 8 entries: the first R
+// lanes of the group hold the round's indices (loaded one round ahead, while the rows of the
+// current round are in flight), and the group issues the round's R row loads before adding
+// any of them, in CSR order.  The sum starts from -0.0, which leaves the first row unchanged
+// bit for bit (x + (-0) = x for every x, signed zeros included), so the result is the same
+// as starting from the first row; an empty bag stores +0.  Sums are fp32
 // in CSR order and rounded once to the output type, so a hotness-1 gather returns the row
 // itself (bit-exact up to the output rounding).
 #include "el_internal.hpp"
@@ -149,10 +158,104 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
 }
 
 template <class TT, class OT, int L, int NVL>
+__global__ __launch_bounds__(256) void k_emb_bag_long(
+    const typename TT::S* __restrict__ W, const int64_t* __restrict__ row_off,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ off, int32_t B, int32_t D,
+    int32_t nvec, uint32_t hash, typename OT::S* __restrict__ out, int64_t ostride, int32_t ocol,
+    int32_t nbags, int32_t b0, int32_t Bc) {
+  constexpr int E = epv<TT>();
+  constexpr int NG = 64 / L;  // bags per wave, one per group
+  constexpr int R = 8;        // entries per round
+  static_assert(L >= R, "the round's indices sit in the group's first R lanes");
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / L;
+  const int gl = lane % L;
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gw = (static_cast<int64_t>(blk) * 4 + (threadIdx.x >> 6)) * NG;
+  if (gw >= nbags) return;  // the whole wave
+  const int64_t gc = gw + grp;
+  const bool valid = gc < nbags;  // group-uniform
+  int s = 0, e = 0, t = 0, b = 0, nt = 1;
+  int64_t base = 0;
+  if (valid) {
+    t = static_cast<int>(gc / Bc);
+    b = b0 + static_cast<int>(gc - static_cast<int64_t>(t) * Bc);
+    const int64_t g = static_cast<int64_t>(t) * B + b;
+    s = ld_stream(off + g);
+    e = ld_stream(off + g + 1);
+    base = row_off[t];
+    if (hash) nt = static_cast<int32_t>(row_off[t + 1] - base);
+  }
+  float acc[NVL][E];
+#pragma unroll
+  for (int m = 0; m < NVL; ++m)
+#pragma unroll
+    for (int x = 0; x < E; ++x) acc[m][x] = -0.0f;
+  const int src0 = grp * L;  // the group's first lane
+  int ri = s + (gl & (R - 1)) < e ? ld_stream(idx + s + (gl & (R - 1))) : 0;
+  if (hash) ri = floor_mod(ri, nt);
+  for (int k = s; k < e; k += R) {  // group-uniform trip count
+    // the next round's indices, in flight with this round's rows
+    const int kn = k + R + (gl & (R - 1));
+    int rn = kn < e ? ld_stream(idx + kn) : 0;
+    uint4 w[R][NVL];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const int rq = __shfl(ri, src0 + q);  // entries past the end read row 0, never added
+      const typename TT::S* row = W + (base + rq) * D;
+#pragma unroll
+      for (int m = 0; m < NVL; ++m) {
+        const int c = gl + m * L;
+        w[q][m] = load16<TT>(row + (c < nvec ? c : nvec - 1) * E);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      if (k + q < e) {
+#pragma unroll
+        for (int m = 0; m < NVL; ++m) {
+          float f[E];
+          unpack16<TT>(w[q][m], f);
+#pragma unroll
+          for (int x = 0; x < E; ++x) acc[m][x] += f[x];
+        }
+      }
+    }
+    if (hash) rn = floor_mod(rn, nt);
+    ri = rn;
+  }
+  if (!valid) return;
+  if (e <= s) {  // an empty bag pools to +0
+#pragma unroll
+    for (int m = 0; m < NVL; ++m)
+#pragma unroll
+      for (int x = 0; x < E; ++x) acc[m][x] = 0.0f;
+  }
+  typename OT::S* dst = out + static_cast<int64_t>(b) * ostride + ocol + static_cast<int64_t>(t) * D;
+#pragma unroll
+  for (int m = 0; m < NVL; ++m) {
+    const int c = gl + m * L;
+    if (c < nvec) store_n<OT, E>(dst + c * E, acc[m]);
+  }
+}
+
+template <class TT, class OT, int L, int NVL>
 el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, void* out,
                    int64_t ostride, int ocol, int nvec, int b0, int Bc, hipStream_t stream) {
-  constexpr int NB = (64 / L) * bags_per_group<L, NVL>();
   const int64_t nbags = static_cast<int64_t>(tab.num_tables) * Bc;
+  if constexpr (L >= 8) {
+    // long bags: one bag per group (four lookups or more per bag on average)
+    if (bags.nnz >= 4 * static_cast<int64_t>(tab.num_tables) * bags.batch) {
+      const int64_t waves = (nbags + (64 / L) - 1) / (64 / L);
+      const int blocks = round_up8((waves + 3) / 4);
+      hipLaunchKernelGGL((k_emb_bag_long<TT, OT, L, NVL>), dim3(blocks), dim3(256), 0, stream,
+                         static_cast<const typename TT::S*>(tab.base), tab.row_offset, bags.indices,
+                         bags.offsets, bags.batch, tab.dim, nvec, (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
+                         static_cast<typename OT::S*>(out), ostride, ocol, static_cast<int32_t>(nbags), b0, Bc);
+      return check_launch("emb_bag_fwd");
+    }
+  }
+  constexpr int NB = (64 / L) * bags_per_group<L, NVL>();
   const int64_t waves = (nbags + NB - 1) / NB;
   const int blocks = round_up8((waves + 3) / 4);
   hipLaunchKernelGGL((k_emb_bag_fwd<TT, OT, L, NVL>), dim3(blocks), dim3(256), 0, stream,

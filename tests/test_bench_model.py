@@ -80,3 +80,31 @@ def test_roofline_names_the_kernel_the_shape_runs():
     assert bench.kernel_of("dot_interact_bwd", synth.WORKLOADS["train_small_tables"]) == "k_dot_bwd_valu"  # D = 16
     assert bench.kernel_of("dot_interact_fwd", synth.WORKLOADS["tiny"]) == "k_dot_fwd_valu"
     assert bench.kernel_of("dot_interact_fwd", synth.WORKLOADS["train_small_tables"]) == "k_dot_fwd_mfma"
+    assert bench.kernel_of("dot_interact_fwd", synth.WORKLOADS["multi_hot"]) == "k_dot_fwd_wide"  # 101 vectors
+
+
+def test_every_path_kernel_has_its_sources_listed():
+    """The counter summary's validity check hashes each kernel's sources: every kernel of the
+    gather, interaction, sort and update files must be in that map."""
+    import re
+    csrc = os.path.join(ROOT, "embedding_lookup_feature_amd", "csrc")
+    for f in ("emb_bag_fwd.hip", "dot_interact.hip", "emb_dot_fwd.hip", "grad_sort.hip", "grad_update.hip"):
+        text = open(os.path.join(csrc, f)).read()
+        names = set(re.findall(r"\bvoid\s+(k_[a-z0-9_]+)\s*\(", text))  # kernels are void k_*
+        assert names, f
+        for k in names:
+            if k.startswith(("k_scan_", "k_seg_flags", "k_seg_emit", "k_seg_empty")):
+                continue  # the segment listing of emb_grad_sort: not on the timed path
+            assert k in bench.KERNEL_SOURCES, (f, k)
+            assert f"embedding_lookup_feature_amd/csrc/{f}" in bench.KERNEL_SOURCES[k], (f, k)
+
+
+def test_source_digest_ignores_comments_only():
+    a = bench.source_digest(["embedding_lookup_feature_amd/csrc/grad_update.hip"])
+    path = os.path.join(ROOT, "embedding_lookup_feature_amd", "csrc", "grad_update.hip")
+    text = open(path).read()
+    import hashlib
+    import re
+    stripped = re.sub(r"//[^\n]*", " ", re.sub(r"/\*.*?\*/", " ", text, flags=re.S))
+    assert a == hashlib.sha256(" ".join(stripped.split()).encode()).hexdigest()
+    assert a != hashlib.sha256(" ".join((stripped + " x").split()).encode()).hexdigest()

@@ -50,7 +50,48 @@ EMB_CASES = [
     ("bf16-d8-one-lane", (100,) * 4, 8, "bf16", "bf16", ("one",), "uniform", False, 65),
     ("f32-hash-hot1", (999, 7, 5000), 32, "f32", "f32", ("one",), "uniform", True, 400),
     ("bf16-hash-multihot", (999, 7, 5000), 64, "bf16", "bf16", ("poisson", 4.0, 0, 9), "zipf", True, 200),
+    # long bags (four lookups or more on average): one bag per lane group, at 128-, 512- and
+    # 4096-byte rows, with empty bags, rounds that end mid-way, and hashed indices
+    ("f32-bf16-d128-long-bags", (4000,) * 6, 128, "f32", "bf16", ("poisson", 9.0, 0, 40), "zipf", False, 400),
+    ("f16-d256-long-bags", (3000, 11, 900), 256, "f16", "f16", ("poisson", 6.0, 0, 17), "uniform", False, 300),
+    ("f32-d1024-long-bags-nvl4", (64,) * 2, 1024, "f32", "f32", ("poisson", 8.0, 0, 20), "uniform", False, 60),
+    ("bf16-hash-long-bags", (999, 7, 5000), 64, "bf16", "bf16", ("poisson", 12.0, 0, 33), "zipf", True, 250),
 ]
+
+
+def fp32_csr_sums(W, ro, idx, off, F, B, D, hsh):
+    """Pooled rows as the kernels sum them: fp32 additions in CSR order, starting from the
+    first row (-0.0 + x = x), an empty bag +0.  numpy float32, one entry position at a time."""
+    Wf = W.float().cpu().numpy()
+    ro_, idx_, off_ = to_np(ro).astype(np.int64), to_np(idx).astype(np.int64), to_np(off).astype(np.int64)
+    rows = ro_[1:] - ro_[:-1]
+    lens = off_[1:] - off_[:-1]
+    t_of = np.repeat(np.arange(F), B)
+    acc = np.full((F * B, D), -0.0, dtype=np.float32)
+    for j in range(int(lens.max()) if lens.size else 0):
+        sel = np.nonzero(lens > j)[0]
+        r = idx_[off_[sel] + j]
+        if hsh:
+            r = np.mod(r, rows[t_of[sel]])
+        acc[sel] += Wf[ro_[t_of[sel]] + r]
+    acc[lens == 0] = 0.0
+    return acc.reshape(F, B, D).transpose(1, 0, 2)
+
+
+@pytest.mark.parametrize("case", [c for c in EMB_CASES if c[5] != ("one",)],
+                         ids=[c[0] for c in EMB_CASES if c[5] != ("one",)])
+def test_emb_bag_fwd_multi_hot_sums_in_csr_order(case):
+    """Multi-hot bags bit for bit against fp32 sums in CSR order rounded once (the oracle's
+    converter): the kernels' association, whichever of them the shape takes."""
+    label, rows, D, tdt, odt, bag, dist, hsh, B = case
+    wl = base_wl(batch=B, rows=rows, dim=D, table_dtype=tdt, act_dtype=odt, index_dist=dist,
+                 zipf_alpha=1.05, bag=bag)
+    W, ro, idx, off = make_problem(wl, hash_spread=hsh)
+    out = torch.full((B, wl.num_tables, D), float("nan"), dtype=synth.torch_dtype(odt), device=DEV)
+    elf.emb_bag_fwd(elf.Tables(W, ro), elf.Bags(idx, off, B), out, hash_indices=hsh)
+    torch.cuda.synchronize()
+    ref = orc.round_from_f64(fp32_csr_sums(W, ro, idx, off, wl.num_tables, B, D, hsh).astype(np.float64), odt)
+    assert_bits(out, ref, label + " (fp32 CSR-order sums)")
 
 
 @pytest.mark.parametrize("case", EMB_CASES, ids=[c[0] for c in EMB_CASES])
