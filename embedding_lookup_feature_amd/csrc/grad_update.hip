@@ -418,6 +418,18 @@ el_status reduce_typed(const el_tables& tab, const el_bags& bags, const GradWork
   constexpr int EPL = 4;
   if (tab.dim % EPL != 0)
     return set_error(EL_ERR_UNSUPPORTED, "emb_grad_reduce_update: dim must be a multiple of 16 bytes of both row types");
+  // 16-bit gradient and table rows: 8 elements (16 bytes of each) per lane, so that a
+  // workgroup's lane groups cover twice the lookups with the same number of loads
+  if constexpr (sizeof(typename GT::S) == 2 && sizeof(typename WT::S) == 2) {
+    const int l8 = tab.dim / 8;
+    if (tab.dim % 8 == 0 && l8 >= 4 && l8 <= 64) {
+      if (l8 <= 4) return reduce_t<GT, WT, 4, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+      if (l8 <= 8) return reduce_t<GT, WT, 8, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+      if (l8 <= 16) return reduce_t<GT, WT, 16, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+      if (l8 <= 32) return reduce_t<GT, WT, 32, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+      return reduce_t<GT, WT, 64, 8>(tab, bags, ws, keys, vals, demb, lr, stream);
+    }
+  }
   const int lanes = tab.dim / EPL;
   if constexpr (EPL == 4) {  // rows of more than 64 vectors: 8 elements per lane
     if (lanes > 64 && tab.dim % 8 == 0 && tab.dim <= 512)

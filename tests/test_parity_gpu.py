@@ -546,6 +546,10 @@ def test_emb_grad_sort_degenerate():
 
 UPDATE_CASES = SORT_CASES + [
     ("one-row-per-table", (50, 50, 50), 16, "f32", "f32", ("one",), "uniform", False, 5000),
+    # 16-bit tables and gradients: 8 elements per lane (32-wide rows: 64 lane groups, ranges of
+    # 1024 lookups; 512-wide rows: 64 lanes per row)
+    ("f16-table-bf16-grad-d32", (3000, 40_000, 17), 32, "f16", "bf16", ("poisson", 6.0, 0, 30), "zipf", False, 700),
+    ("bf16-d512-long-rows", (2000,) * 3, 512, "bf16", "bf16", ("poisson", 3.0, 0, 9), "zipf", False, 300),
 ]
 
 
