@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
                       "embedding_lookup_feature_amd/csrc/el_mfma.hpp",
                       "embedding_lookup_feature_amd/csrc/emb_dot_fwd.hip"],
 }
+KERNEL_SOURCES["k_emb_bag_long"] = KERNEL_SOURCES["k_emb_bag_fwd"]
 KERNEL_SOURCES["k_dot_fwd_valu"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
 KERNEL_SOURCES["k_dot_fwd_wide"] = KERNEL_SOURCES["k_dot_fwd_mfma"]
 KERNEL_SOURCES["k_dot_bwd_valu"] = KERNEL_SOURCES["k_dot_bwd_mfma"]
@@ -60,6 +61,9 @@ def kernel_of(call, wl):
     gradient rows), the fp32 FMA kernels otherwise."""
     V, D = wl.num_tables + 1, wl.dim
     mfma = wl.act_dtype in ("bf16", "f16") and D % 16 == 0 and V <= 128
+    row_bytes = D * (4 if wl.table_dtype == "f32" else 2)
+    if call == "emb_bag_fwd" and wl.bag[0] == "poisson" and wl.bag[1] >= 4 and row_bytes >= 128:
+        return "k_emb_bag_long"  # long bags: one bag per lane group
     if call == "dot_interact_fwd" and not mfma:
         return "k_dot_fwd_valu"
     if call == "dot_interact_fwd" and V > 32:  # several 32-row tiles: four wavefronts per sample
@@ -526,7 +530,7 @@ def main():
         dom = max(single, key=lambda n: call_ms[n])
         kernel = kernel_of(dom, wl)
     else:  # a forward-only line whose one call runs the gather and the interaction in chunks
-        dom, kernel = names[0], "k_emb_bag_fwd + interaction forward"
+        dom, kernel = names[0], kernel_of("emb_bag_fwd", wl) + " + " + kernel_of("dot_interact_fwd", wl)
     def roofline_of(call, kernel, ms, nbytes, note=None, traffic_workload=None):
         a = nbytes / (ms * 1e-3) / 1e9
         r = {"bound": "hbm", "kernel": kernel, "call": call, "achieved": round(a, 1), "peak": HBM_PEAK_GBPS,

@@ -108,3 +108,8 @@ def test_source_digest_ignores_comments_only():
     stripped = re.sub(r"//[^\n]*", " ", re.sub(r"/\*.*?\*/", " ", text, flags=re.S))
     assert a == hashlib.sha256(" ".join(stripped.split()).encode()).hexdigest()
     assert a != hashlib.sha256(" ".join((stripped + " x").split()).encode()).hexdigest()
+
+
+def test_long_bag_gather_is_named():
+    assert bench.kernel_of("emb_bag_fwd", synth.WORKLOADS["multi_hot"]) == "k_emb_bag_long"
+    assert bench.kernel_of("emb_bag_fwd", synth.WORKLOADS["train_step"]) == "k_emb_bag_fwd"
