@@ -463,6 +463,18 @@ def main():
             call_samples["wait_for_sort"] = [e[ka].elapsed_time(w) for e, w in zip(evs, wevs)]
             call_samples["emb_grad_apply"] = [w.elapsed_time(e[ka + 1]) for e, w in zip(evs, wevs)]
     call_ms = {n: float(np.mean(v)) for n, v in call_samples.items()}
+    # the sort alone (nothing beside it), on the batches of the timed steps: what the side
+    # stream's figure above would be without the calls it overlaps
+    sort_alone = None
+    if overlap:
+        ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        torch.cuda.synchronize()
+        for i, (e0, e1) in enumerate(ea):
+            e0.record()
+            elf.emb_grad_prepare(tab, batches[i % len(batches)][0], ws)
+            e1.record()
+            torch.cuda.synchronize()
+        sort_alone = float(np.median([a.elapsed_time(b) for a, b in ea]))
 
     # the gather with no row reuse: emb_bag_fwd alone on the same shapes with every table's
     # lookups distinct rows (each row read once, so its algorithmic bytes all come from HBM)
@@ -515,6 +527,8 @@ def main():
         if n == "emb_grad_prepare":
             c["stream"] = "side (overlaps " + ("the forward and " if args.overlap_sort == "fwd" else "") + \
                           "the interaction backward)"
+            if sort_alone is not None:
+                c["alone_median_ms"] = round(sort_alone, 4)
         calls[n] = c
     if "wait_for_sort" in call_samples:
         v = call_samples["wait_for_sort"]

@@ -165,8 +165,8 @@ struct GradWorkspace {
   uint32_t* range_flags = nullptr;
 };
 
-constexpr int kRadixBits = 8;  // widest radix digit (wider digits measured slower)
-static_assert(kRadixBits <= 8, "the sort's histogram and scatter kernels take digits of at most 8 bits");
+constexpr int kRadixBits = 9;  // widest radix digit (wider digits measured slower)
+static_assert(kRadixBits <= 9, "the sort's histogram and scatter kernels take digits of at most 9 bits");
 constexpr int kSortTile = 4096;  // keys per radix tile: 4 waves x 16 steps x 64 lanes
 constexpr int kScanTile = 4096;  // elements per scan tile: 256 threads x 16
 constexpr int kChunk = 16;         // lookups per lane group in the reduce

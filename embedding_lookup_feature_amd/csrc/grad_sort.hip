@@ -14,7 +14,8 @@
 // that of all rows together, and adds the table's first row when it writes the last pass.
 //
 // Radix sort: least significant digit first, the fewest passes of at most kRadixBits-bit
-// digits that cover the local rows, with equal digit widths (20-bit rows: 3 x 7 bits).
+// digits that cover the local rows, with equal digit widths (20-bit rows: 3 x 7 bits;
+// 17-bit rows: 2 x 9 bits).
 // Tiles of 4096 keys never straddle two tables (a table's last tile may be short).  One
 // pass = tile histograms -> per digit, a scan over the tiles -> stable scatter; the scatter
 // takes its table's digit starts from the scanned counts at the table's first and last
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
                                                     int shift, uint32_t* __restrict__ hist, int nblocks) {
   constexpr int kRadix = 1 << RB;
   constexpr int kSteps = kSortTile / 256;
-  constexpr int kLaneGroups = 8;  // sub-histograms per wavefront
+  constexpr int kLaneGroups = RB <= 8 ? 8 : 2;  // sub-histograms per wavefront (LDS-bound)
   constexpr int kSub = 4 * kLaneGroups;
   // one pad word per sub-histogram: a digit's counters in the different sub-histograms
   // then fall in different LDS banks
@@ -561,6 +562,7 @@ el_status radix_pass(const el_tables& tab, const el_bags& bags, bool hash, const
     case 6: return radix_pass_t<6>(tab, bags, hash, ws, pass, kin, vin, kout, vout, stream);
     case 7: return radix_pass_t<7>(tab, bags, hash, ws, pass, kin, vin, kout, vout, stream);
     case 8: return radix_pass_t<8>(tab, bags, hash, ws, pass, kin, vin, kout, vout, stream);
+    case 9: return radix_pass_t<9>(tab, bags, hash, ws, pass, kin, vin, kout, vout, stream);
   }
   return set_error(EL_ERR_UNSUPPORTED, "radix digit width out of range");
 }
