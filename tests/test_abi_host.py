@@ -50,10 +50,11 @@ def test_workspace_bytes_is_host_pure_and_scales():
     assert big >= 6 * 4 * nnz
     assert L.emb_grad_workspace_bytes(ref(tables()), ref(bags(B=0, nnz=0))) == 0
     assert L.emb_grad_workspace_bytes(None, ref(bags())) == 0
-    # a declared largest table: the sort works on fewer bits (17 instead of 22 here), so
-    # no more workspace than without it; beyond the total it is refused
+    # a declared largest table: the sort works on fewer bits (17 instead of 22 here: 2
+    # passes of 9-bit digits instead of 3 of 8, so a larger digit histogram, still far
+    # below the key arrays); beyond the total it is refused
     declared = L.emb_grad_workspace_bytes(ref(tables(max_rows=100_000)), ref(bags()))
-    assert 0 < declared <= big
+    assert 6 * 4 * nnz <= declared <= big + 4 * (26 + nnz // 4096 + 1) * 512 * 2
     assert L.emb_grad_workspace_bytes(ref(tables(max_rows=26 * 100_000 + 1)), ref(bags())) == 0
     assert L.emb_grad_workspace_bytes(ref(tables(max_rows=-1)), ref(bags())) == 0
 
