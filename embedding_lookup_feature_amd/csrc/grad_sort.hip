@@ -258,7 +258,11 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
   __shared__ uint32_t gofs[kRadix];    // global position of tile-local position 0, per digit
   __shared__ uint32_t wsum[4];
   __shared__ uint32_t sk[kSortTile], sv[kSortTile];
-  const SortTile ti = tiles[blockIdx.x];
+  // each XCD takes one contiguous run of tiles: neighbouring tiles write neighbouring parts
+  // of every digit's run, whose partly written lines then meet in the same L2
+  const int j = xcd_remap(blockIdx.x, gridDim.x);  // the grid is a multiple of 8
+  if (j >= nblocks) return;
+  const SortTile ti = tiles[j];
   if (ti.count == 0) return;  // a tile past the last one (the whole block leaves)
   for (int i = threadIdx.x; i < 4 * kRadix; i += 256) (&cnt[0][0])[i] = 0;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
         const uint32_t sf = hist_scan[row + ti.first];
         const uint32_t se = ti.end < nblocks ? hist_scan[row + ti.end] : totals[d0 + x];
         tot[x] = se - sf;
-        tglob[x] = hist_scan[row + blockIdx.x] - sf;
+        tglob[x] = hist_scan[row + j] - sf;
       }
       sum += tot[x];
     }
@@ -538,12 +542,12 @@ el_status radix_pass_t(const el_tables& tab, const el_bags& bags, bool hash, con
                      static_cast<const uint32_t*>(ws.hist), ws.hist_scan, nb, ws.dtotal);
   if ((st = check_launch("radix_scan")) != EL_OK) return st;
   if (first)
-    hipLaunchKernelGGL((k_radix_scatter<RB, true>), dim3(nb), dim3(256), 0, stream, kin, bags.indices, vin,
+    hipLaunchKernelGGL((k_radix_scatter<RB, true>), dim3(round_up8(nb)), dim3(256), 0, stream, kin, bags.indices, vin,
                        static_cast<const SortTile*>(ws.tiles), tab.row_offset, hash ? 1 : 0, last, shift,
                        static_cast<const uint32_t*>(ws.hist_scan), static_cast<const uint32_t*>(ws.dtotal),
                        kout, vout, nb);
   else
-    hipLaunchKernelGGL((k_radix_scatter<RB, false>), dim3(nb), dim3(256), 0, stream, kin, bags.indices, vin,
+    hipLaunchKernelGGL((k_radix_scatter<RB, false>), dim3(round_up8(nb)), dim3(256), 0, stream, kin, bags.indices, vin,
                        static_cast<const SortTile*>(ws.tiles), tab.row_offset, hash ? 1 : 0, last, shift,
                        static_cast<const uint32_t*>(ws.hist_scan), static_cast<const uint32_t*>(ws.dtotal),
                        kout, vout, nb);

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
     const typename GT::S* __restrict__ demb, int32_t B, int32_t F, int32_t D,
     typename WT::S* __restrict__ W, float lr, float* __restrict__ rhead,
-    float* __restrict__ rtail, uint32_t* __restrict__ rflags) {
+    float* __restrict__ rtail, uint32_t* __restrict__ rflags, int64_t nranges) {
   constexpr int G = 256 / L;       // lane groups per workgroup
   constexpr int RANGE = G * CH;    // sorted lookups per workgroup
   constexpr int PITCH = L * EPL;   // floats per LDS slot (>= D)
@@ -155,7 +155,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
 
   const int tid = threadIdx.x;
   const int g = tid / L, gl = tid % L;
-  const int64_t w = blockIdx.x;
+  // each XCD takes one contiguous run of ranges, so that the gradient rows its lookups
+  // re-read (the bags of the few tables it is working on) stay in its L2
+  const int64_t w = xcd_remap(blockIdx.x, gridDim.x);
+  if (w >= nranges) return;  // the grid is rounded up to a multiple of 8 (whole workgroup)
   const int64_t p0 = w * RANGE;
   const int nloc = static_cast<int>(n - p0 < RANGE ? n - p0 : RANGE);  // lookups of the range, >= 1
 
@@ -381,10 +384,10 @@ el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspac
   constexpr int RANGE = (256 / L) * CH;
   static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
   const int64_t nr = (ws.n + RANGE - 1) / RANGE;
-  hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub>), dim3(static_cast<unsigned>(nr)), dim3(256), 0, stream,
-                     keys, vals, ws.n, static_cast<const typename GT::S*>(demb), bags.batch,
+  hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub>), dim3(static_cast<unsigned>(round_up8(nr))), dim3(256), 0,
+                     stream, keys, vals, ws.n, static_cast<const typename GT::S*>(demb), bags.batch,
                      tab.num_tables, tab.dim, static_cast<typename WT::S*>(tab.base), lr,
-                     ws.range_head, ws.range_tail, ws.range_flags);
+                     ws.range_head, ws.range_tail, ws.range_flags, nr);
   el_status st = check_launch("segment_reduce");
   if (st != EL_OK || nr < 2) return st;
   // fix-up: LF lanes x NV vectors of 4 fp32 per row
