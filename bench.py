@@ -835,9 +835,10 @@ def cpu_info():
 
 
 def cpu_baseline(wl, W, ro, batch, seconds):
-    """The CPU oracle over the first `n` samples of batch 0 (same tables), sized so that
-    the run takes about `seconds`; samples/s on one host core (the process is pinned to one
-    core while the oracle runs)."""
+    """The CPU oracle over batch 0 (same tables): the full batch when one run takes at most
+    `seconds`, else its first `n` samples sized for `seconds`; three repetitions (median) when
+    a run takes at most 10 s, else one.  samples/s on one host core (the process is pinned to
+    one core while the oracle runs)."""
     from oracle import oracle as orc
     from tests.helpers import compact_tables, sub_batch, to_np
 
@@ -868,17 +869,21 @@ def cpu_baseline(wl, W, ro, batch, seconds):
     model, nproc = cpu_info()
     old = os.sched_getaffinity(0)
     os.sched_setaffinity(0, {min(old)})
-    reps = 3
     try:
-        probe_n = 256
-        dt = run(probe_n)
-        per_sample = dt / probe_n
-        n = int(min(B, max(probe_n, (seconds / reps) / max(per_sample, 1e-9))))
+        # two probes separate the per-sample cost from the fixed one (the full-table SGD copy)
+        n1, n2 = min(256, B), min(1024, B)
+        t1 = run(n1)
+        t2 = run(n2) if n2 > n1 else t1
+        per_sample = max((t2 - t1) / max(n2 - n1, 1), t2 / max(n2, 1) * 0.5, 1e-9)
+        fixed = max(t1 - per_sample * n1, 0.0)
+        full_s = fixed + per_sample * B
+        n = B if full_s <= seconds else int(min(B, max(n2, (seconds - fixed) / per_sample)))
+        est = fixed + per_sample * n
+        reps = 3 if est <= 10.0 else 1
         dts = [run(n) for _ in range(reps)]
         dt = float(np.median(dts))
     finally:
         os.sched_setaffinity(0, old)
-    full_s = dt * B / n
     # the same oracle source built with OpenMP (bags / samples over all host threads; the
     # update stays serial), on the same sample
     from oracle import build as obuild
@@ -886,21 +891,23 @@ def cpu_baseline(wl, W, ro, batch, seconds):
     if os.path.exists(obuild.LIB_OMP):
         prev = orc.use_library(obuild.LIB_OMP)
         try:
-            dt_omp = float(np.median([run(n) for _ in range(reps)]))
+            dt_omp = float(np.median([run(n) for _ in range(3)]))
         finally:
             orc.restore_library(prev)
         threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(old)
         omp = {"value": round(n / dt_omp, 1), "unit": "samples/s", "cores": threads,
                "kind": "oracle, OpenMP build (forward and interaction backward threaded)",
-               "sample": f"the same {n} samples, median of {reps} repetitions of {dt_omp:.1f} s"}
+               "sample": f"the same {n} samples, median of 3 repetitions of {dt_omp:.1f} s"}
     tables = "full tables" + ("; full-table SGD copy" if wl.backward else "") if full_tables \
         else "only the looked-up rows of the tables"
-    why = "" if n == B else (f"; not the full batch: one full-batch repetition would take about "
-                             f"{full_s:.0f} s single-threaded, beyond the benchmark's few-minute budget")
+    why = "" if n == B else (f"; not the full batch: one full-batch run would take about "
+                             f"{full_s:.0f} s single-threaded, beyond the {seconds:.0f} s this leg is given")
+    what = f"all {B} samples" if n == B else f"first {n} of {B} samples"
+    runs = f"median of {reps} repetitions of {dt:.1f} s" if reps > 1 else \
+        f"one run of {dt:.1f} s (a run above 10 s is not repeated)"
     res = {"value": round(n / dt, 1), "unit": "samples/s", "cores": 1, "kind": "oracle",
-           "sample": f"first {n} of {B} samples of batch 0 (all {F} tables, {tables}), "
-                     f"single-threaded C oracle pinned to one core, median of {reps} repetitions "
-                     f"of {dt:.1f} s{why}",
+           "sample": f"{what} of batch 0 (all {F} tables, {tables}), "
+                     f"single-threaded C oracle pinned to one core, {runs}{why}",
            "host_cpu": model, "host_cpus_visible": nproc}
     return res, omp
 
