@@ -192,8 +192,11 @@ __global__ __launch_bounds__(256) void k_emb_bag_long(
 #pragma unroll
     for (int x = 0; x < E; ++x) acc[m][x] = -0.0f;
   const int src0 = grp * L;  // the group's first lane
-  int ri = s + (gl & (R - 1)) < e ? ld_stream(idx + s + (gl & (R - 1))) : 0;
-  if (hash) ri = floor_mod(ri, nt);
+  int ri = 0;
+  if (s + (gl & (R - 1)) < e) {  // (a table without rows has only empty bags)
+    ri = ld_stream(idx + s + (gl & (R - 1)));
+    if (hash) ri = floor_mod(ri, nt);
+  }
   for (int k = s; k < e; k += R) {  // group-uniform trip count
     // the next round's indices, in flight with this round's rows
     const int kn = k + R + (gl & (R - 1));

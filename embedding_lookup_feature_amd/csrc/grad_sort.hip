@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_tile_info(const int32_t* __restrict__ o
   SortTile ti{0, 0, 0, 0, 0, 0, 0, 0};
   if (lo < F) {
     const int32_t s = off[static_cast<int64_t>(lo) * B], e = off[static_cast<int64_t>(lo + 1) * B];
-    const int32_t start = s + (j - tile_prefix[lo]) * kSortTile;
+    const int32_t start = static_cast<int32_t>(s + static_cast<int64_t>(j - tile_prefix[lo]) * kSortTile);
     ti.t = lo;
     ti.start = start;
     ti.count = e - start < kSortTile ? e - start : kSortTile;
