@@ -593,6 +593,46 @@ def test_emb_grad_reduce_update_is_deterministic_and_lr0_is_identity():
     assert torch.equal(tab_w[2].view(torch.int32), W.view(torch.int32))
 
 
+def test_calls_are_bitwise_the_same_beside_other_work():
+    """The interaction kernels stride over samples with as many workgroups as fit at once, and
+    the update's ranges go to whichever workgroup starts; on a side stream while the default
+    stream keeps the GPU busy, fewer of them run at once and samples fall to other
+    workgroups: the bits must not change (each sample and each row has one fixed sum)."""
+    F, D, B = 26, 128, 3000
+    wl, x0, emb, stride = dot_inputs(F, D, "bf16", B, None)
+    dout = synth.make_dout(wl, DEV)
+    gwl, W, ro, idx, off = grad_problem(SORT_CASES[0])
+    demb_u = synth.make_demb(gwl, DEV, dtype="bf16")
+
+    def buffers():
+        Wc = W.clone()
+        tab, bags = elf.Tables(Wc, ro), elf.Bags(idx, off, gwl.batch)
+        return dict(out=torch.empty((B, stride), dtype=torch.bfloat16, device=DEV),
+                    dx0=torch.empty((B, D), dtype=torch.bfloat16, device=DEV),
+                    demb=torch.empty((B, F, D), dtype=torch.bfloat16, device=DEV),
+                    W=Wc, tab=tab, bags=bags, ws=elf.alloc_workspace(tab, bags))
+
+    def run(b, stream):
+        elf.dot_interact_fwd(x0, emb, b["out"], stream=stream)
+        elf.dot_interact_bwd(x0, emb, dout, b["dx0"], b["demb"], stream=stream)
+        elf.emb_grad_reduce_update(b["tab"], b["bags"], demb_u, gwl.lr, b["ws"], stream=stream)
+
+    quiet, busy = buffers(), buffers()
+    busy_buf = torch.ones(1 << 28, dtype=torch.float32, device=DEV)  # 1 GiB of elementwise work
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    run(quiet, None)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        busy_buf.mul_(1.0000001)  # the default stream stays busy while the side stream runs
+    run(busy, side)
+    for _ in range(3):
+        busy_buf.mul_(1.0000001)
+    torch.cuda.synchronize()
+    for name in ("out", "dx0", "demb", "W"):
+        assert torch.equal(quiet[name].view(torch.uint8), busy[name].view(torch.uint8)), name
+
+
 @pytest.mark.parametrize("case", [SORT_CASES[0], SORT_CASES[-1], UPDATE_CASES[-1]],
                          ids=[SORT_CASES[0][0], SORT_CASES[-1][0], UPDATE_CASES[-1][0]])
 def test_emb_grad_prepare_apply_equals_reduce_update(case):
