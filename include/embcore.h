@@ -207,11 +207,12 @@ EL_API size_t emb_grad_workspace_bytes(const el_tables* tab, const el_bags* bags
  * Sparse SGD update of the embedding rows (same page, §Command-line options, --lr: plain
  * SGD).  For every distinct row r looked up by the batch:
  *   W[r] <- round( W[r] - lr * sum_{lookups k of row r, in lookup order} demb[b_k][t_k] )
- * Rows that are not looked up are not written.  The lookups are sorted by global row with
- * a stable, deterministic LSD radix sort; equal rows form segments that are reduced in
- * fixed-size chunks (fp32) with an ordered fix-up for segments spanning chunks.  No
- * floating-point atomics (the sort's digit histograms count with integer LDS atomics, exact
- * in any order): the result is bitwise reproducible.
+ * Rows that are not looked up are not written.  The lookups are sorted by joint row with a
+ * stable, deterministic LSD radix sort (each table's lookups by local row, on the bits of
+ * tab->max_rows); equal rows form runs that are summed in sorted order (fp32) in ranges of
+ * consecutive lookups, with an ordered fix-up for runs spanning ranges.  No floating-point
+ * atomics (the sort's digit histograms count with integer LDS atomics, exact in any order):
+ * the result is bitwise reproducible, whatever the launch configuration.
  * demb: [B][F][D] of grad_dtype, 16-byte aligned.  workspace: >= emb_grad_workspace_bytes,
  * 256-byte aligned, contents on entry irrelevant.
  */
