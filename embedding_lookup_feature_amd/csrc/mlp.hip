@@ -80,7 +80,9 @@ __device__ inline u32x4 keep_if(const u32x4& v, uint32_t mask, int i) {
 // Global -> registers for one reduction-contiguous operand tile of ROWS rows x 64
 // reduction; NT threads, ROWS*8/NT vectors each (thread t: row t/8 + (NT/8) i, reduction
 // 8 (t%8) .. +8).
-template <int ROWS, int NT>
+// FULL: every vector of every stage lies inside the operand (the grid's tiles are whole and
+// the stage count is even), so no vector is masked.
+template <int ROWS, int NT, bool FULL>
 struct TileLoaderRC {
   static constexpr int N = ROWS * 8 / NT;
   u32x4 v[N];
@@ -92,15 +94,20 @@ struct TileLoaderRC {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int r = row0 + (sub >> 3) + (NT / 8) * i;
-      const bool in = r < nrows && kk < kend;
-      v[i] = ld16(base + static_cast<long>(r) * ld + kk, base, in);
-      ok |= static_cast<uint32_t>(in) << i;
+      if constexpr (FULL) {
+        v[i] = *reinterpret_cast<const u32x4*>(base + static_cast<long>(r) * ld + kk);
+      } else {
+        const bool in = r < nrows && kk < kend;
+        v[i] = ld16(base + static_cast<long>(r) * ld + kk, base, in);
+        ok |= static_cast<uint32_t>(in) << i;
+      }
     }
   }
   __device__ inline void store(uint16_t* lds, int sub) const {
 #pragma unroll
     for (int i = 0; i < N; ++i)
-      *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + (NT / 8) * i) * kPitch + (sub & 7) * 8) = keep_if(v[i], ok, i);
+      *reinterpret_cast<u32x4*>(lds + ((sub >> 3) + (NT / 8) * i) * kPitch + (sub & 7) * 8) =
+          FULL ? v[i] : keep_if(v[i], ok, i);
   }
 };
 
@@ -109,7 +116,7 @@ struct TileLoaderRC {
 // BR..BR+BC-1 the cols operand's, through one code path (operand chosen by per-thread
 // selects, no branch between the two sets of loads); each block is transposed in
 // registers on its way to LDS.
-template <int BR>
+template <int BR, bool FULL>
 struct PairLoaderOC {
   u32x4 v[8];
   uint32_t ok = 0;
@@ -131,16 +138,20 @@ struct PairLoaderOC {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int k = k0 + kb * 8 + i;
-      const bool in = r < nrows && k < kend;
-      v[i] = ld16(base + static_cast<long>(k) * ld + r, base, in);
-      ok |= static_cast<uint32_t>(in) << i;
+      if constexpr (FULL) {
+        v[i] = *reinterpret_cast<const u32x4*>(base + static_cast<long>(k) * ld + r);
+      } else {
+        const bool in = r < nrows && k < kend;
+        v[i] = ld16(base + static_cast<long>(k) * ld + r, base, in);
+        ok |= static_cast<uint32_t>(in) << i;
+      }
     }
   }
   __device__ inline void store(uint16_t* lds) const {
     const int kb = sub & 7, rb = sub >> 3;
     u32x4 z[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = keep_if(v[i], ok, i);
+    for (int i = 0; i < 8; ++i) z[i] = FULL ? v[i] : keep_if(v[i], ok, i);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int w = j >> 1;
@@ -189,7 +200,7 @@ __device__ __forceinline__ void gemm_stage(const uint16_t* P, const uint16_t* Q,
   }
 }
 
-template <class T, class C, bool P_RC, bool Q_RC, int EPI>
+template <class T, class C, bool P_RC, bool Q_RC, int EPI, bool FULL>
 __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sP[2][C::BR * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][C::BC * kPitch];
@@ -232,8 +243,8 @@ __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   const int nk2 = (nk + 1) & ~1;
   auto k_at = [&](int t) { return kbeg + t * kBK; };
   if constexpr (P_RC && Q_RC) {
-    TileLoaderRC<C::BR, C::NT> pA, pB;
-    TileLoaderRC<C::BC, C::NT> qA, qB;
+    TileLoaderRC<C::BR, C::NT, FULL> pA, pB;
+    TileLoaderRC<C::BC, C::NT, FULL> qA, qB;
     pA.load(a.P, a.ldp, row0, a.R, k_at(0), kend, tid);
     qA.load(a.Q, a.ldq, col0, a.C, k_at(0), kend, tid);
     pB.load(a.P, a.ldp, row0, a.R, k_at(1), kend, tid);
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   } else {
     static_assert(!P_RC && !Q_RC, "mixed operand layouts are not instantiated");
     static_assert(C::BR + C::BC == C::NT, "one 8 x 8 block per thread");
-    PairLoaderOC<C::BR> lA(a, tid, row0, col0), lB(a, tid, row0, col0);
+    PairLoaderOC<C::BR, FULL> lA(a, tid, row0, col0), lB(a, tid, row0, col0);
     uint16_t* dst0 = tid >= C::BR ? sQ[0] : sP[0];
     uint16_t* dst1 = tid >= C::BR ? sQ[1] : sP[1];
     lA.load(k_at(0), kend);
@@ -676,7 +687,15 @@ WgradPlan plan_wgrad(int M, int K, int N) {
 template <class T, class C, bool RC, int EPI>
 void launch_gemm(GemmArgs a, int splits, hipStream_t st) {
   fill_tiles<C>(a);
-  hipLaunchKernelGGL((k_gemm<T, C, RC, RC, EPI>), dim3(a.tiles * splits), dim3(C::NT), 0, st, a);
+  // whole tiles, and every split's stage count even: no stage reads outside the operands
+  const int per = a.red_per_split;
+  const int last = a.red - (splits - 1) * per;
+  const bool full = a.R % C::BR == 0 && a.C % C::BC == 0 && per % (2 * kBK) == 0 && last > 0 &&
+                    last % (2 * kBK) == 0;
+  if (full)
+    hipLaunchKernelGGL((k_gemm<T, C, RC, RC, EPI, true>), dim3(a.tiles * splits), dim3(C::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_gemm<T, C, RC, RC, EPI, false>), dim3(a.tiles * splits), dim3(C::NT), 0, st, a);
 }
 template <class T, bool RC, int EPI>
 void launch_gemm_auto(const GemmArgs& a, int splits, bool large, hipStream_t st) {
