@@ -50,31 +50,38 @@ __device__ inline uint64_t match_digit(uint32_t d, bool valid) {
 }
 
 // Bag id of every lookup position.  A block takes 256 consecutive bags: their CSR bounds go
-// to LDS, and the block's threads walk the bags' lookup positions (contiguous) with unit
-// stride, so loads and stores are coalesced whatever the bag lengths; each position finds
-// its bag in the bounds (one probe when the bags hold one lookup each, else a binary
-// search).
+// to LDS.  Bags of one lookup each (position k of the block holds bag k - first): every
+// position's bag is checked with one probe and written straight away.  Otherwise the
+// block's positions are covered in windows of kBagWin: each thread marks the positions of
+// its own bag that fall in the window with the bag's number in LDS, and after a barrier the
+// block writes the window out with unit stride, so stores are coalesced for any bag lengths.
+constexpr int kBagWin = 4096;
+
 __global__ __launch_bounds__(256) void k_build_vals(const int32_t* __restrict__ off, int32_t nbags,
                                                     uint32_t* __restrict__ vals) {
   __shared__ int32_t bound[257];
+  __shared__ uint8_t mark[kBagWin];  // bag of the window's positions, relative to the block
+  __shared__ int32_t one_each;
   const int g0 = blockIdx.x * 256;
   const int nb = nbags - g0 < 256 ? nbags - g0 : 256;  // bags of this block
   for (int i = threadIdx.x; i <= nb; i += 256) bound[i] = ld_stream(off + g0 + i);
+  if (threadIdx.x == 0) one_each = 1;
   __syncthreads();
   const int s = bound[0], e = bound[nb];
-  for (int k = s + static_cast<int>(threadIdx.x); k < e; k += 256) {
-    // the bag holding position k: the last i in [0, nb) with bound[i] <= k.  First guess:
-    // every bag holds one lookup; otherwise binary search.
-    int lo = k - s < nb - 1 ? k - s : nb - 1;
-    if (!(bound[lo] <= k && k < bound[lo + 1])) {
-      lo = 0;
-      int hi = nb - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (bound[mid] <= k) lo = mid; else hi = mid - 1;
-      }
-    }
-    vals[k] = static_cast<uint32_t>(g0 + lo);
+  const int t = threadIdx.x;
+  if (t < nb && bound[t + 1] - bound[t] != 1) one_each = 0;  // any thread may clear it
+  __syncthreads();
+  if (one_each) {  // block-uniform
+    for (int k = s + t; k < e; k += 256) vals[k] = static_cast<uint32_t>(g0 + (k - s));
+    return;
+  }
+  const int bs = t < nb ? bound[t] : 0, be = t < nb ? bound[t + 1] : 0;  // this thread's bag
+  for (int w0 = s; w0 < e; w0 += kBagWin) {  // block-uniform
+    const int w1 = e - w0 < kBagWin ? e : w0 + kBagWin;
+    for (int k = bs > w0 ? bs : w0; k < (be < w1 ? be : w1); ++k) mark[k - w0] = static_cast<uint8_t>(t);
+    __syncthreads();
+    for (int k = w0 + t; k < w1; k += 256) vals[k] = static_cast<uint32_t>(g0 + mark[k - w0]);
+    __syncthreads();  // the window's marks are read before the next window's are written
   }
 }
 
