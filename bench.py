@@ -190,7 +190,8 @@ def hbm_calibration(dev, gib=4, reps=5):
     table) and writing them contiguously (gather_*: reads + writes + indices), writing only
     their first half (gather_*_write_half: the mix of fp32 rows pooled into 16-bit outputs)
     or only reading them (gather_read_*).  Each figure is the median of `reps` launches timed with
-    HIP events after one warm-up launch."""
+    HIP events after one warm-up launch, and the best over the cache policies of the kernel's
+    loads and stores (plain or non-temporal; `policy` records which won)."""
     import embedding_lookup_feature_amd as elf
     from embedding_lookup_feature_amd import embcore as ec
     n = gib << 30
@@ -211,26 +212,37 @@ def hbm_calibration(dev, gib=4, reps=5):
             ts.append(e0.elapsed_time(e1))
         return float(np.median(ts))
 
-    res = {}
-    for name, mode in (("read", ec.EL_CALIB_READ), ("write", ec.EL_CALIB_WRITE), ("copy", ec.EL_CALIB_COPY),
-                       ("read3_write1", ec.EL_CALIB_READ3_WRITE1)):
-        res[name] = round(n / (median_ms(lambda: elf.hbm_calib(mode, a, b, n)) * 1e-3) / 1e9, 1)
+    NL, NS = ec.EL_CALIB_NT_LOADS, ec.EL_CALIB_NT_STORES
+    names = {0: "plain", NL: "nt loads", NS: "nt stores", NL | NS: "nt loads+stores"}
+    res, policy = {}, {}
+
+    def best(name, traffic, run, policies):
+        ms = {p: median_ms(lambda: run(p)) for p in policies}
+        p = min(ms, key=ms.get)
+        res[name] = round(traffic / (ms[p] * 1e-3) / 1e9, 1)
+        policy[name] = names[p]
+
+    both = (0, NL, NS, NL | NS)
+    for name, mode, pols in (("read", ec.EL_CALIB_READ, (0, NL)), ("write", ec.EL_CALIB_WRITE, (0, NS)),
+                             ("copy", ec.EL_CALIB_COPY, both), ("read3_write1", ec.EL_CALIB_READ3_WRITE1, both)):
+        best(name, n, lambda p: elf.hbm_calib(mode | p, a, b, n), pols)
     g = torch.Generator(device=dev)
     g.manual_seed(12345)
     for rb in (128, 256, 512):
         rows = n // rb
         nr = (n // 2) // rb  # distinct random rows, half the table's bytes, read once each
         idx = torch.randperm(rows, generator=g, device=dev)[:nr].to(torch.int32)
-        ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER, a, b, 0, idx=idx, row_bytes=rb))
-        res[f"gather_{rb}B"] = round((2 * nr * rb + 4 * nr) / (ms * 1e-3) / 1e9, 1)
-        ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER_READ, a, b, 0, idx=idx, row_bytes=rb))
-        res[f"gather_read_{rb}B"] = round((nr * rb + 4 * nr) / (ms * 1e-3) / 1e9, 1)
+        best(f"gather_{rb}B", 2 * nr * rb + 4 * nr,
+             lambda p: elf.hbm_calib(ec.EL_CALIB_GATHER | p, a, b, 0, idx=idx, row_bytes=rb), both)
+        best(f"gather_read_{rb}B", nr * rb + 4 * nr,
+             lambda p: elf.hbm_calib(ec.EL_CALIB_GATHER_READ | p, a, b, 0, idx=idx, row_bytes=rb), (0, NL))
         if rb >= 256:  # rows pooled into outputs of half their size (fp32 rows, 16-bit outputs)
-            ms = median_ms(lambda: elf.hbm_calib(ec.EL_CALIB_GATHER, a, b, rb // 2, idx=idx, row_bytes=rb))
-            res[f"gather_{rb}B_write_half"] = round((nr * rb * 3 // 2 + 4 * nr) / (ms * 1e-3) / 1e9, 1)
+            best(f"gather_{rb}B_write_half", nr * rb * 3 // 2 + 4 * nr,
+                 lambda p: elf.hbm_calib(ec.EL_CALIB_GATHER | p, a, b, rb // 2, idx=idx, row_bytes=rb), both)
         del idx
     del a, b
     torch.cuda.empty_cache()
+    res["policy"] = policy
     return res
 
 

@@ -381,7 +381,11 @@ el_status el_validate_bags(const el_tables* tab, const el_bags* bags, uint32_t f
 el_status el_hbm_calib(int32_t mode, const void* src, void* dst, size_t bytes, const int32_t* idx,
                        int64_t nrows, int32_t row_bytes, hipStream_t stream) {
   const char* fn = "el_hbm_calib";
-  if (mode < EL_CALIB_READ || mode > EL_CALIB_GATHER_READ) return bad(fn, "unknown mode");
+  const int32_t policy = mode & ~EL_CALIB_MODE_MASK;
+  const int32_t full = mode;
+  mode &= EL_CALIB_MODE_MASK;
+  if (mode > EL_CALIB_GATHER_READ || (policy & ~(EL_CALIB_NT_LOADS | EL_CALIB_NT_STORES)) != 0)
+    return bad(fn, "unknown mode");
   EL_TRY(check_dense(fn, dst, true, "dst"));
   if (mode == EL_CALIB_GATHER || mode == EL_CALIB_GATHER_READ) {
     EL_TRY(check_dense(fn, src, true, "src"));
@@ -397,7 +401,7 @@ el_status el_hbm_calib(int32_t mode, const void* src, void* dst, size_t bytes, c
     if (bytes % 64 != 0) return bad(fn, "bytes must be a multiple of 64");
     if (bytes == 0) return EL_OK;
   }
-  return launch_hbm_calib(mode, src, dst, bytes, idx, nrows, row_bytes, stream);
+  return launch_hbm_calib(full, src, dst, bytes, idx, nrows, row_bytes, stream);
 }
 
 const char* el_last_error(void) { return g_last_error.c_str(); }

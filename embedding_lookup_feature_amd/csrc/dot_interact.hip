@@ -7,7 +7,10 @@
 // matrix Z = V V^T, stored row-major: pair (i, j), i > j, at p(i,j) = i(i-1)/2 + j.
 //
 // 16-bit inputs (bf16 / fp16): one wavefront per sample.  The sample's V x D tile is
-// streamed from HBM with 16-byte loads into LDS (row pitch padded by 16 bytes so that the
+// streamed from HBM with 16-byte loads into LDS (non-temporal in the forward, whose
+// wavefronts each cover whole rows; the backward's lanes each take one chunk of many rows,
+// so a cache line feeds several of its load instructions and stays with the default
+// policy; row pitch padded by 16 bytes so that the
 // 32 rows read by one MFMA operand fall on distinct banks), then
 //   forward : the lower-triangular 32x32 tiles of Z are v_mfma_f32_32x32x16_{bf16,f16}
 //             products of the tile with itself, K = D in steps of 16 (fp32 accumulate);
@@ -81,7 +84,7 @@ __device__ inline void fetch_sample(const uint16_t* __restrict__ x0, const uint1
     } else {
       src = q < nv ? x0 + x0_base + q * 8 : emb + emb_base + q * 8;
     }
-    r[u] = *reinterpret_cast<const u32x4*>(src);
+    r[u] = ld_stream16(src);
   }
 }
 
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void k_dot_fwd_wide(const uint16_t* __restrict
       q = q < tile ? q : tile - 1;
       const int row = q / nv, c = q - row * nv;
       const uint16_t* src = row == 0 ? x0 + x0b + c * 8 : emb + eb + static_cast<int64_t>(row) * D + c * 8;
-      r[u] = *reinterpret_cast<const u32x4*>(src);
+      r[u] = ld_stream16(src);
     }
   };
   int b = blockIdx.x;
@@ -635,7 +638,9 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
     const int qd = tid < nd ? tid : nd - 1;  // threads past D/8 repeat the last chunk
     const u32x4 gdir = *reinterpret_cast<const u32x4*>(lds + goff + qd * 16);
     __syncthreads();
-    // rows 1.. -> demb[b] (contiguous), row 0 -> dx0[b] = G[0:D) + dV_0; 16-byte stores.
+    // rows 1.. -> demb[b] (contiguous, non-temporal: nothing reads them before the update,
+    // after the rest of the backward has passed through the caches), row 0 -> dx0[b] =
+    // G[0:D) + dV_0; 16-byte stores.
     // Every thread issues a fixed number of stores (threads past the end repeat the last
     // chunk with the same bytes), so that waiting for the next sample's loads never has to
     // wait for these stores as well.
@@ -647,8 +652,8 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
       int q = k * 256 + tid;
       q = q < nchunk ? q : nchunk - 1;
       const int row = q / nv + 1, c = q - (row - 1) * nv;
-      *reinterpret_cast<uint4*>(derow + static_cast<int64_t>(q) * 16) =
-          *reinterpret_cast<const uint4*>(lds + ooff + row * opitch + c * 16);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(lds + ooff + row * opitch + c * 16),
+                                  reinterpret_cast<u32x4*>(derow + static_cast<int64_t>(q) * 16));
     }
     {
       // dx0 chunk qd = G[0:D) chunk (registers) + dV_0 chunk (fp32 in LDS; its next writer

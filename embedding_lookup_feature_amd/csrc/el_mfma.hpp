@@ -12,6 +12,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Native 4 x 32-bit vector (kept in registers by the optimiser, unlike HIP's uint4 class).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Streaming 16-byte load (non-temporal): for rows that a kernel reads once and no later
+// kernel needs from the cache.
+__device__ inline u32x4 ld_stream16(const void* p) { return __builtin_nontemporal_load(static_cast<const u32x4*>(p)); }
+
 template <class IT>
 __device__ inline f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c);
 template <>

@@ -153,9 +153,11 @@ __global__ __launch_bounds__(256) void k_tile_info(const int32_t* __restrict__ o
   tiles[j] = ti;
 }
 
-// Local row of lookup p of table t (FIRST pass: straight from the indices).
+// Local row of lookup p of table t (FIRST pass: straight from the indices).  STREAM: a
+// non-temporal load (the scatter's, the sort's last read of the indices).
+template <bool STREAM = false>
 __device__ inline uint32_t local_row(const int32_t* __restrict__ idx, int64_t p, bool hash, int32_t rows) {
-  int32_t r = idx[p];
+  int32_t r = STREAM ? ld_stream(idx + p) : idx[p];
   if (hash) r = floor_mod(r, rows);
   return static_cast<uint32_t>(r);
 }
@@ -285,10 +287,10 @@ __global__ __launch_bounds__(256) void k_radix_scatter(const uint32_t* __restric
     const int p = base + st * 64 + lane;
     const bool valid = p < tn;
     if (FIRST)
-      kk[st] = valid ? local_row(idx, tile0 + p, hash, rows) : 0u;
+      kk[st] = valid ? local_row<true>(idx, tile0 + p, hash, rows) : 0u;
     else
-      kk[st] = valid ? keys_in[tile0 + p] : 0u;
-    vv[st] = valid ? vals_in[tile0 + p] : 0u;
+      kk[st] = valid ? ld_stream(keys_in + tile0 + p) : 0u;  // the pass's last read of them
+    vv[st] = valid ? ld_stream(vals_in + tile0 + p) : 0u;
   }
   // global start of each of this thread's digits (see above)
   const int d0 = threadIdx.x * DPT;

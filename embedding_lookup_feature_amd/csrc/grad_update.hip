@@ -63,9 +63,9 @@ __device__ inline Raw<T, N> load_raw(const typename T::S* p) {
   return r;
 }
 
-// The same from the table: non-temporal, since every table row the update touches is read
-// once and written once, and the cache space is better left to the gradient rows (a
-// multi-hot bag's gradient row is read once per lookup of the bag).
+// The same, non-temporal: every table row the update touches is read once and written
+// once; a gradient row too when bags hold one lookup (a multi-hot bag's gradient row is
+// read once per lookup of the bag, and is then left to the cache).
 typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
 
@@ -140,7 +140,7 @@ __device__ inline int first_of(const uint32_t* skey, uint32_t k, int hi) {
 
 // GT: gradient type, WT: table type; L lanes per row (a power of two), EPL elements per lane,
 // SUB lookups loaded at once.
-template <class GT, class WT, int L, int EPL, int SUB>
+template <class GT, class WT, int L, int EPL, int SUB, bool GNT>
 __global__ __launch_bounds__(256) void k_seg_reduce(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
     const typename GT::S* __restrict__ demb, int32_t B, int32_t F, int32_t D,
@@ -211,7 +211,9 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
         const uint32_t v = sval[c0 + qb + (q < hc ? q : hc - 1)];
         const uint32_t t = v / static_cast<uint32_t>(B);
         const uint32_t b = v - t * static_cast<uint32_t>(B);
-        gr[q] = load_raw<GT, EPL>(demb + (static_cast<int64_t>(b) * F + t) * D + e0);
+        const typename GT::S* gsrc = demb + (static_cast<int64_t>(b) * F + t) * D + e0;
+        if constexpr (GNT) gr[q] = load_raw_nt<GT, EPL>(gsrc);
+        else gr[q] = load_raw<GT, EPL>(gsrc);
       }
 #pragma unroll
       for (int q = 0; q < SUB; ++q) {
@@ -384,10 +386,21 @@ el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspac
   constexpr int RANGE = (256 / L) * CH;
   static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
   const int64_t nr = (ws.n + RANGE - 1) / RANGE;
-  hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub>), dim3(static_cast<unsigned>(round_up8(nr))), dim3(256), 0,
-                     stream, keys, vals, ws.n, static_cast<const typename GT::S*>(demb), bags.batch,
-                     tab.num_tables, tab.dim, static_cast<typename WT::S*>(tab.base), lr,
-                     ws.range_head, ws.range_tail, ws.range_flags, nr);
+  // at most one lookup per bag on average: every gradient row is read about once, so it is
+  // streamed (non-temporal) like the table rows; otherwise a bag's row is re-read once per
+  // lookup and is left to the cache
+  const bool once = ws.n <= static_cast<int64_t>(bags.batch) * tab.num_tables;
+  auto reduce = [&](auto gnt) {
+    hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub, decltype(gnt)::value>),
+                       dim3(static_cast<unsigned>(round_up8(nr))), dim3(256), 0, stream, keys, vals, ws.n,
+                       static_cast<const typename GT::S*>(demb), bags.batch, tab.num_tables, tab.dim,
+                       static_cast<typename WT::S*>(tab.base), lr, ws.range_head, ws.range_tail,
+                       ws.range_flags, nr);
+  };
+  if (once)
+    reduce(std::true_type{});
+  else
+    reduce(std::false_type{});
   el_status st = check_launch("segment_reduce");
   if (st != EL_OK || nr < 2) return st;
   // fix-up: LF lanes x NV vectors of 4 fp32 per row

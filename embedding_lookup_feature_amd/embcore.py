@@ -22,6 +22,7 @@ EL_ACT_NONE, EL_ACT_RELU = 0, 1
 EL_LINEAR_DX_RELU_MASK = 1
 EL_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/embcore.h
 EL_CALIB_READ, EL_CALIB_WRITE, EL_CALIB_COPY, EL_CALIB_READ3_WRITE1, EL_CALIB_GATHER, EL_CALIB_GATHER_READ = range(6)
+EL_CALIB_NT_LOADS, EL_CALIB_NT_STORES = 16, 32  # cache-policy bits OR-ed into the mode
 
 _DTYPE = {torch.float32: EL_F32, torch.float16: EL_F16, torch.bfloat16: EL_BF16}
 

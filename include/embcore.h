@@ -370,21 +370,26 @@ EL_API el_status el_sgd_dense(float* master, void* copy, el_dtype copy_dtype, co
  * bandwidth-bound, the bandwidth that plain streaming kernels reach on the same GPU is the
  * yardstick its kernels are compared with (beside the published peak).  One call runs one
  * kernel (k_copy_calib / k_gather_calib) that moves 16-byte vectors, 8 loads in flight per
- * thread, over the whole buffer.  `bytes` is the total traffic (reads + writes):
+ * thread, over the whole buffer (streams in workgroup chunks of 32 KiB).  `bytes` is the
+ * total traffic (reads + writes):
  *   EL_CALIB_READ          reads src[0, bytes); writes 8 MiB of per-thread xors to dst;
  *   EL_CALIB_WRITE         writes dst[0, bytes);
  *   EL_CALIB_COPY          copies src[0, bytes/2) to dst[0, bytes/2);
  *   EL_CALIB_READ3_WRITE1  reads src[0, 3*bytes/4) and writes dst[0, bytes/4), output
- *                          vector i the xor of input vectors 3i .. 3i+2 (a 3:1 read-heavy mix);
+ *                          vector i the xor of input vectors i, i + m and i + 2m (m = bytes/64
+ *                          output vectors: three read streams and one write stream);
  *   EL_CALIB_GATHER        reads the nrows rows idx[i] (row_bytes each, 16..1024, a multiple
  *                          of 16) of the row-major table at src and writes the first `bytes`
  *                          of each (0: the whole row) to dst[i * bytes] (traffic = nrows *
  *                          (row_bytes + bytes) plus the indices);
  *   EL_CALIB_GATHER_READ   the same rows, only read (8 MiB of per-thread xors to dst).
+ * OR-ing EL_CALIB_NT_LOADS / EL_CALIB_NT_STORES into the mode makes the kernel's data loads /
+ * stores non-temporal (the cache policy that is faster depends on the mix).
  * Pointers 16-byte aligned; bytes a multiple of 64.  Not part of the model's computation.
  * ------------------------------------------------------------------------------------ */
 enum { EL_CALIB_READ = 0, EL_CALIB_WRITE = 1, EL_CALIB_COPY = 2, EL_CALIB_READ3_WRITE1 = 3,
-       EL_CALIB_GATHER = 4, EL_CALIB_GATHER_READ = 5 };
+       EL_CALIB_GATHER = 4, EL_CALIB_GATHER_READ = 5,
+       EL_CALIB_MODE_MASK = 15, EL_CALIB_NT_LOADS = 16, EL_CALIB_NT_STORES = 32 };
 EL_API el_status el_hbm_calib(int32_t mode, const void* src, void* dst, size_t bytes,
                               const int32_t* idx, int64_t nrows, int32_t row_bytes,
                               hipStream_t stream);

@@ -189,7 +189,11 @@ def test_hbm_calib_rejects_on_the_host():
     assert L.el_hbm_calib(ec.EL_CALIB_GATHER, A, A, 0, A, 10, 24, None) == INVALID         # row size
     assert L.el_hbm_calib(ec.EL_CALIB_GATHER, A, A, 0, A, 10, 2048, None) == INVALID
     assert "el_hbm_calib" in ec.el_last_error()
+    assert L.el_hbm_calib(ec.EL_CALIB_READ | 64, A, A, 1 << 20, None, 0, 0, None) == INVALID  # unknown policy bit
+    assert L.el_hbm_calib(-1, A, A, 1 << 20, None, 0, 0, None) == INVALID
     assert L.el_hbm_calib(ec.EL_CALIB_WRITE, None, A, 0, None, 0, 0, None) == ec.EL_OK     # nothing to move
+    policy = ec.EL_CALIB_NT_LOADS | ec.EL_CALIB_NT_STORES
+    assert L.el_hbm_calib(ec.EL_CALIB_COPY | policy, A, A, 0, None, 0, 0, None) == ec.EL_OK
 
 
 def test_grad_calls_reject_small_or_missing_workspace():
