@@ -47,6 +47,12 @@ struct Raw {
   uint32_t w[NW];
 };
 
+// Element offset of row r of a row-major matrix of D-element rows (one 32 x 32 -> 64-bit
+// multiply: r and D are non-negative).
+__device__ inline uint64_t row_off(uint32_t r, int D) {
+  return static_cast<uint64_t>(r) * static_cast<uint32_t>(D);
+}
+
 template <class T, int N>
 __device__ inline Raw<T, N> load_raw(const typename T::S* p) {
   Raw<T, N> r;
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
   constexpr int RANGE = G * CH;    // sorted lookups per workgroup
   constexpr int PITCH = L * EPL;   // floats per LDS slot (>= D)
   __shared__ uint32_t skey[RANGE + 2];  // key before the range, the range's keys, key after
-  __shared__ uint32_t sval[RANGE];
+  __shared__ uint32_t sval[RANGE];      // gradient row (b * F + t) of each lookup's bag
   __shared__ float slot[G * PITCH];     // per group: the piece that continues past its lookups
 
   const int tid = threadIdx.x;
@@ -166,7 +172,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
   for (int i = tid; i < RANGE; i += 256) {
     const bool ok = i < nloc;
     skey[1 + i] = ok ? ld_stream(keys + p0 + i) : NONE;
-    sval[i] = ok ? ld_stream(vals + p0 + i) : 0u;
+    // bag g = t * B + b -> its row of demb, b * F + t (< F * B < 2^31), once per lookup here
+    // rather than in each lane that loads the row
+    const uint32_t g = ok ? ld_stream(vals + p0 + i) : 0u;
+    const uint32_t t = g / static_cast<uint32_t>(B);
+    sval[i] = (g - t * static_cast<uint32_t>(B)) * static_cast<uint32_t>(F) + t;
   }
   if (tid == 0) skey[0] = p0 > 0 ? keys[p0 - 1] : NONE;
   if (tid == 1) skey[RANGE + 1] = p0 + RANGE < n ? keys[p0 + RANGE] : NONE;
@@ -208,10 +218,8 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
       Raw<WT, EPL> wold[SUB];
 #pragma unroll
       for (int q = 0; q < SUB; ++q) {
-        const uint32_t v = sval[c0 + qb + (q < hc ? q : hc - 1)];
-        const uint32_t t = v / static_cast<uint32_t>(B);
-        const uint32_t b = v - t * static_cast<uint32_t>(B);
-        const typename GT::S* gsrc = demb + (static_cast<int64_t>(b) * F + t) * D + e0;
+        const uint32_t grow = sval[c0 + qb + (q < hc ? q : hc - 1)];
+        const typename GT::S* gsrc = demb + row_off(grow, D) + e0;
         if constexpr (GNT) gr[q] = load_raw_nt<GT, EPL>(gsrc);
         else gr[q] = load_raw<GT, EPL>(gsrc);
       }
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
       for (int q = 0; q < SUB; ++q) {
         const bool ends = q < hc && kq[q] != kq[q + 1];
         if (ends && kq[q] != kbefore) {
-          wold[q] = load_raw_nt<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0);
+          wold[q] = load_raw_nt<WT, EPL>(W + row_off(kq[q], D) + e0);
         } else {
 #pragma unroll
           for (int x = 0; x < Raw<WT, EPL>::NW; ++x) wold[q].w[x] = 0u;
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
               whead = wold[q];
               has_head = true;
             } else if (lane_on) {
-              sgd_store<WT, EPL>(W + static_cast<int64_t>(kq[q]) * D + e0, wold[q], acc, lr);
+              sgd_store<WT, EPL>(W + row_off(kq[q], D) + e0, wold[q], acc, lr);
             }
 #pragma unroll
             for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
