@@ -225,13 +225,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
       }
 #pragma unroll
       for (int q = 0; q < SUB; ++q) {
-        const bool ends = q < hc && kq[q] != kq[q + 1];
-        if (ends && kq[q] != kbefore) {
-          wold[q] = load_raw_nt<WT, EPL>(W + row_off(kq[q], D) + e0);
-        } else {
 #pragma unroll
-          for (int x = 0; x < Raw<WT, EPL>::NW; ++x) wold[q].w[x] = 0u;
-        }
+        for (int x = 0; x < Raw<WT, EPL>::NW; ++x) wold[q].w[x] = 0u;
+        // a run ends at lookup q (never at q >= hc: kq[hc..SUB] all hold the key after)
+        if (kq[q] != kq[q + 1] && kq[q] != kbefore) wold[q] = load_raw_nt<WT, EPL>(W + row_off(kq[q], D) + e0);
       }
 
       // (2) pieces in order: a run inside the group is finished here; the head piece waits
@@ -283,7 +280,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
       if (kh == kbefore)  // began before the range: its part in this range is the head partial
         store_n<F32T, EPL>(rhead + w * D + e0, tot);
       else
-        sgd_store<WT, EPL>(W + static_cast<int64_t>(kh) * D + e0, whead, tot, lr);
+        sgd_store<WT, EPL>(W + row_off(kh, D) + e0, whead, tot, lr);
     }
   }
   //     the run that continues past the range: its pieces here are the range's tail partial
