@@ -240,18 +240,16 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
           raw_to_f<GT, EPL>(gr[q], f);
 #pragma unroll
           for (int x = 0; x < EPL; ++x) acc[x] += f[x];
-          if (kq[q] != kq[q + 1]) {  // a piece ends here
-            if (head_cont && kq[q] == khead) {
+          const bool ends = kq[q] != kq[q + 1];           // a piece ends here
+          const bool head = ends && head_cont && kq[q] == khead;
+          if (ends && !head && lane_on) sgd_store<WT, EPL>(W + row_off(kq[q], D) + e0, wold[q], acc, lr);
 #pragma unroll
-              for (int x = 0; x < EPL; ++x) hacc[x] = acc[x];
-              whead = wold[q];
-              has_head = true;
-            } else if (lane_on) {
-              sgd_store<WT, EPL>(W + row_off(kq[q], D) + e0, wold[q], acc, lr);
-            }
+          for (int x = 0; x < EPL; ++x) hacc[x] = head ? acc[x] : hacc[x];
 #pragma unroll
-            for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
-          }
+          for (int x = 0; x < Raw<WT, EPL>::NW; ++x) whead.w[x] = head ? wold[q].w[x] : whead.w[x];
+          has_head = has_head || head;
+#pragma unroll
+          for (int x = 0; x < EPL; ++x) acc[x] = ends ? 0.0f : acc[x];
         }
       }
     }
