@@ -8,10 +8,10 @@
 // Skewed (Zipf) indices make some runs thousands of lookups long, so the work is cut by
 // sorted position, not by run:
 //   k_seg_reduce: a workgroup takes a range of G * 16 consecutive sorted lookups, each of
-//     its G lane groups (L lanes, EPL elements of a row per lane) 16 of them.  A group
-//     issues all 16 gradient-row loads, and the table-row loads of the runs that end in its
-//     16 lookups, before any store; it sums its lookups in order (fp32), one "piece" per run,
-//     and updates the rows of the runs that lie inside its 16 lookups.  A piece that
+//     its G lane groups (L lanes, EPL elements of a row per lane) 16 of them, in batches of
+//     SUB.  A group issues a batch's gradient-row loads, and the table-row loads of the runs
+//     that end in it, before any store; it sums its lookups in order (fp32), one "piece" per
+//     run, and updates the rows of the runs that lie inside its 16 lookups.  A piece that
 //     continues into the next group's lookups goes to an LDS slot.  After one barrier the
 //     group where such a run ends adds the earlier groups' slots in group order, then its
 //     own piece, and updates the row.  Only runs that cross an edge of the workgroup's range
@@ -34,7 +34,6 @@ namespace el {
 namespace {
 
 constexpr int CH = kChunk;              // lookups per lane group
-constexpr int kSub = 8;                 // of which loaded at once
 constexpr uint32_t NONE = 0xffffffffu;  // not a row: rows are < total_rows < 2^32 - 1
 constexpr uint32_t RANGE_THROUGH = 1u;  // one run covers the whole range
 constexpr uint32_t RANGE_OWNER = 2u;    // the range's last run continues into the next range
@@ -393,8 +392,16 @@ el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspac
   // streamed (non-temporal) like the table rows; otherwise a bag's row is re-read once per
   // lookup and is left to the cache
   const bool once = ws.n <= static_cast<int64_t>(bags.batch) * tab.num_tables;
+  // lookups loaded at once per lane group (measured on the training-step and multi-hot
+  // shapes with both table types): rows read once are bandwidth-bound and want bytes in
+  // flight (8: update 147-185 us, against 151-190 with 2 or 4 and 157-183 with 16); a
+  // multi-hot bag's rows come back from L2 and the table rows' latency is what remains, so
+  // more resident wavefronts with fewer loads each win (16-bit tables 2: 785 us against 923
+  // with 8; fp32 tables 4: 1100 us against 1227)
   auto reduce = [&](auto gnt) {
-    hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, kSub, decltype(gnt)::value>),
+    constexpr bool GNT = decltype(gnt)::value;
+    constexpr int SUB = GNT ? 8 : (sizeof(typename WT::S) == 2 ? 2 : 4);
+    hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, SUB, GNT>),
                        dim3(static_cast<unsigned>(round_up8(nr))), dim3(256), 0, stream, keys, vals, ws.n,
                        static_cast<const typename GT::S*>(demb), bags.batch, tab.num_tables, tab.dim,
                        static_cast<typename WT::S*>(tab.base), lr, ws.range_head, ws.range_tail,
