@@ -550,6 +550,10 @@ UPDATE_CASES = SORT_CASES + [
     # 1024 lookups; 512-wide rows: 64 lanes per row)
     ("f16-table-bf16-grad-d32", (3000, 40_000, 17), 32, "f16", "bf16", ("poisson", 6.0, 0, 30), "zipf", False, 700),
     ("bf16-d512-long-rows", (2000,) * 3, 512, "bf16", "bf16", ("poisson", 3.0, 0, 9), "zipf", False, 300),
+    # the lookups loaded per batch depend on whether bags hold one lookup and on the table
+    # type: one lookup per bag with 16-bit tables, and multi-hot bags with fp32 tables
+    ("hot1-bf16-table", (5000,) * 8, 64, "bf16", "bf16", ("one",), "zipf", False, 1000),
+    ("multihot-f32-d128", (20000,) * 6, 128, "f32", "bf16", ("poisson", 8.0, 1, 30), "zipf", False, 300),
 ]
 
 
@@ -633,8 +637,12 @@ def test_calls_are_bitwise_the_same_beside_other_work():
         assert torch.equal(quiet[name].view(torch.uint8), busy[name].view(torch.uint8)), name
 
 
-@pytest.mark.parametrize("case", [SORT_CASES[0], SORT_CASES[-1], UPDATE_CASES[-1]],
-                         ids=[SORT_CASES[0][0], SORT_CASES[-1][0], UPDATE_CASES[-1][0]])
+PREPARE_APPLY_CASES = [c for c in UPDATE_CASES
+                       if c[0] in ("hot1-zipf-26x5000", "27-bit-keys-three-passes", "bf16-d512-long-rows",
+                                   "multihot-f32-d128")]
+
+
+@pytest.mark.parametrize("case", PREPARE_APPLY_CASES, ids=[c[0] for c in PREPARE_APPLY_CASES])
 def test_emb_grad_prepare_apply_equals_reduce_update(case):
     """The two halves, on two streams ordered by an event, give the one-call result bit for
     bit (and both match the oracle through the one-call test above)."""
