@@ -7,11 +7,12 @@
 //
 // Skewed (Zipf) indices make some runs thousands of lookups long, so the work is cut by
 // sorted position, not by run:
-//   k_seg_reduce: a workgroup takes a range of G * 16 consecutive sorted lookups, each of
-//     its G lane groups (L lanes, EPL elements of a row per lane) 16 of them, in batches of
-//     SUB.  A group issues a batch's gradient-row loads, and the table-row loads of the runs
-//     that end in it, before any store; it sums its lookups in order (fp32), one "piece" per
-//     run, and updates the rows of the runs that lie inside its 16 lookups.  A piece that
+//   k_seg_reduce: a workgroup takes a range of G * CH consecutive sorted lookups, each of
+//     its G lane groups (L lanes, EPL elements of a row per lane) CH of them (16, or 32 for
+//     multi-hot bags), in batches of SUB.  A group issues a batch's gradient-row loads, and
+//     the table-row loads of the runs that end in it, before any store; it sums its lookups
+//     in order (fp32), one "piece" per run, and updates the rows of the runs that lie inside
+//     its CH lookups.  A piece that
 //     continues into the next group's lookups goes to an LDS slot.  After one barrier the
 //     group where such a run ends adds the earlier groups' slots in group order, then its
 //     own piece, and updates the row.  Only runs that cross an edge of the workgroup's range
@@ -33,7 +34,6 @@
 namespace el {
 namespace {
 
-constexpr int CH = kChunk;              // lookups per lane group
 constexpr uint32_t NONE = 0xffffffffu;  // not a row: rows are < total_rows < 2^32 - 1
 constexpr uint32_t RANGE_THROUGH = 1u;  // one run covers the whole range
 constexpr uint32_t RANGE_OWNER = 2u;    // the range's last run continues into the next range
@@ -144,8 +144,8 @@ __device__ inline int first_of(const uint32_t* skey, uint32_t k, int hi) {
 }
 
 // GT: gradient type, WT: table type; L lanes per row (a power of two), EPL elements per lane,
-// SUB lookups loaded at once.
-template <class GT, class WT, int L, int EPL, int SUB, bool GNT>
+// CH lookups per lane group, SUB of them loaded at once; GNT: gradient rows non-temporal.
+template <class GT, class WT, int L, int EPL, int CH, int SUB, bool GNT>
 __global__ __launch_bounds__(256) void k_seg_reduce(
     const uint32_t* __restrict__ keys, const uint32_t* __restrict__ vals, int64_t n,
     const typename GT::S* __restrict__ demb, int32_t B, int32_t F, int32_t D,
@@ -385,23 +385,27 @@ template <class GT, class WT, int L, int EPL>
 el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspace& ws,
                    const uint32_t* keys, const uint32_t* vals, const void* demb, float lr,
                    hipStream_t stream) {
-  constexpr int RANGE = (256 / L) * CH;
-  static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
-  const int64_t nr = (ws.n + RANGE - 1) / RANGE;
   // at most one lookup per bag on average: every gradient row is read about once, so it is
   // streamed (non-temporal) like the table rows; otherwise a bag's row is re-read once per
   // lookup and is left to the cache
   const bool once = ws.n <= static_cast<int64_t>(bags.batch) * tab.num_tables;
-  // lookups loaded at once per lane group (measured on the training-step and multi-hot
-  // shapes with both table types): rows read once are bandwidth-bound and want bytes in
-  // flight (8: update 147-185 us, against 151-190 with 2 or 4 and 157-183 with 16); a
-  // multi-hot bag's rows come back from L2 and the table rows' latency is what remains, so
-  // more resident wavefronts with fewer loads each win (16-bit tables 2: 785 us against 923
-  // with 8; fp32 tables 4: 1100 us against 1227)
+  // Lookups per lane group and per load batch, measured on the training-step and multi-hot
+  // shapes with both table types.  Rows read once are bandwidth-bound and want bytes in
+  // flight: 16 per group, 8 at once (update 147-185 us, against 151-190 with 2 or 4 at once,
+  // 157-183 with 16, and 153-190 with 32 per group).  A multi-hot bag's rows come back from
+  // L2 and the table rows' latency is what remains, so more resident wavefronts with fewer
+  // loads each win, and longer ranges leave fewer partials: 32 per group, 2 at once for
+  // 16-bit tables (752 us against 923 with 16 and 8) and 4 for fp32 (1071 against 1227).
+  int64_t nr = 0, range = 0;
   auto reduce = [&](auto gnt) {
     constexpr bool GNT = decltype(gnt)::value;
+    constexpr int CH = GNT ? kChunk : 2 * kChunk;
     constexpr int SUB = GNT ? 8 : (sizeof(typename WT::S) == 2 ? 2 : 4);
-    hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, SUB, GNT>),
+    constexpr int RANGE = (256 / L) * CH;
+    static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
+    range = RANGE;
+    nr = (ws.n + RANGE - 1) / RANGE;
+    hipLaunchKernelGGL((k_seg_reduce<GT, WT, L, EPL, CH, SUB, GNT>),
                        dim3(static_cast<unsigned>(round_up8(nr))), dim3(256), 0, stream, keys, vals, ws.n,
                        static_cast<const typename GT::S*>(demb), bags.batch, tab.num_tables, tab.dim,
                        static_cast<typename WT::S*>(tab.base), lr, ws.range_head, ws.range_tail,
@@ -418,7 +422,7 @@ el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspac
   auto fix = [&](auto lf, auto nv) {
     constexpr int LF = decltype(lf)::value, NV = decltype(nv)::value;
     hipLaunchKernelGGL((k_seg_fixup<WT, LF, NV>), dim3(blocks_for(nr, 256 / LF)), dim3(256), 0, stream,
-                       keys, ws.n, nr, RANGE, tab.dim, static_cast<typename WT::S*>(tab.base), lr,
+                       keys, ws.n, nr, static_cast<int>(range), tab.dim, static_cast<typename WT::S*>(tab.base), lr,
                        static_cast<const float*>(ws.range_head), static_cast<const float*>(ws.range_tail),
                        static_cast<const uint32_t*>(ws.range_flags));
     return check_launch("segment_fixup");
