@@ -80,8 +80,9 @@ __device__ inline u32x4 keep_if(const u32x4& v, uint32_t mask, int i) {
 // Global -> registers for one reduction-contiguous operand tile of ROWS rows x 64
 // reduction; NT threads, ROWS*8/NT vectors each (thread t: row t/8 + (NT/8) i, reduction
 // 8 (t%8) .. +8).
-// FULL: every vector of every stage lies inside the operand (the grid's tiles are whole and
-// the stage count is even), so no vector is masked.
+// FULL: every vector of every computed stage lies inside the operand (the grid's tiles are
+// whole and the stage count is even), so no vector is masked; the loads the pipeline issues
+// ahead for stages past the last are pointed at the last stage (see k_at in k_gemm).
 template <int ROWS, int NT, bool FULL>
 struct TileLoaderRC {
   static constexpr int N = ROWS * 8 / NT;
@@ -238,10 +239,12 @@ __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   // multiplies tile kt: every load has two stages of products to arrive.  The stage count is
   // rounded up to even; stages past the reduction load zeros (masked, from the operand's
   // base), so the loop body has no branch and the compiler waits for exactly the older set.
-  // Scheduling fences keep each stage's LDS writes after the previous barrier and its loads
-  // ahead of its products, so no wait for a newer set is pulled into a stage.
+  // The last two iterations also issue loads for up to three stages that are never
+  // multiplied: unmasked (FULL), those re-read the last stage, so that no load leaves the
+  // operand.  Scheduling fences keep each stage's LDS writes after the previous barrier and
+  // its loads ahead of its products, so no wait for a newer set is pulled into a stage.
   const int nk2 = (nk + 1) & ~1;
-  auto k_at = [&](int t) { return kbeg + t * kBK; };
+  auto k_at = [&](int t) { return kbeg + (FULL && t >= nk ? nk - 1 : t) * kBK; };
   if constexpr (P_RC && Q_RC) {
     TileLoaderRC<C::BR, C::NT, FULL> pA, pB;
     TileLoaderRC<C::BC, C::NT, FULL> qA, qB;
