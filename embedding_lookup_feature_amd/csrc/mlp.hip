@@ -246,31 +246,29 @@ __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   const int nk2 = (nk + 1) & ~1;
   auto k_at = [&](int t) { return kbeg + (FULL && t >= nk ? nk - 1 : t) * kBK; };
   if constexpr (P_RC && Q_RC) {
-    TileLoaderRC<C::BR, C::NT, FULL> pA, pB;
-    TileLoaderRC<C::BC, C::NT, FULL> qA, qB;
+    TileLoaderRC<C::BR, C::NT, FULL> pA;
+    TileLoaderRC<C::BC, C::NT, FULL> qA;
     pA.load(a.P, a.ldp, row0, a.R, k_at(0), kend, tid);
     qA.load(a.Q, a.ldq, col0, a.C, k_at(0), kend, tid);
-    pB.load(a.P, a.ldp, row0, a.R, k_at(1), kend, tid);
-    qB.load(a.Q, a.ldq, col0, a.C, k_at(1), kend, tid);
     pA.store(sP[0], tid);
     qA.store(sQ[0], tid);
-    pA.load(a.P, a.ldp, row0, a.R, k_at(2), kend, tid);
-    qA.load(a.Q, a.ldq, col0, a.C, k_at(2), kend, tid);
+    pA.load(a.P, a.ldp, row0, a.R, k_at(1), kend, tid);
+    qA.load(a.Q, a.ldq, col0, a.C, k_at(1), kend, tid);
     __syncthreads();
     for (int kt = 0; kt < nk2; kt += 2) {
       __builtin_amdgcn_sched_barrier(0);
-      pB.store(sP[1], tid);
-      qB.store(sQ[1], tid);
-      pB.load(a.P, a.ldp, row0, a.R, k_at(kt + 3), kend, tid);
-      qB.load(a.Q, a.ldq, col0, a.C, k_at(kt + 3), kend, tid);
+      pA.store(sP[1], tid);
+      qA.store(sQ[1], tid);
+      pA.load(a.P, a.ldp, row0, a.R, k_at(kt + 2), kend, tid);
+      qA.load(a.Q, a.ldq, col0, a.C, k_at(kt + 2), kend, tid);
       __builtin_amdgcn_sched_barrier(0);
       gemm_stage<T, C, false>(sP[0], sQ[0], wr, wc, half, l32, acc, false, tid, dbsum);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       pA.store(sP[0], tid);
       qA.store(sQ[0], tid);
-      pA.load(a.P, a.ldp, row0, a.R, k_at(kt + 4), kend, tid);
-      qA.load(a.Q, a.ldq, col0, a.C, k_at(kt + 4), kend, tid);
+      pA.load(a.P, a.ldp, row0, a.R, k_at(kt + 3), kend, tid);
+      qA.load(a.Q, a.ldq, col0, a.C, k_at(kt + 3), kend, tid);
       __builtin_amdgcn_sched_barrier(0);
       gemm_stage<T, C, false>(sP[1], sQ[1], wr, wc, half, l32, acc, false, tid, dbsum);
       __syncthreads();
