@@ -276,24 +276,23 @@ __global__ __launch_bounds__(C::NT, C::WPS) void k_gemm(GemmArgs a) {
   } else {
     static_assert(!P_RC && !Q_RC, "mixed operand layouts are not instantiated");
     static_assert(C::BR + C::BC == C::NT, "one 8 x 8 block per thread");
-    PairLoaderOC<C::BR, FULL> lA(a, tid, row0, col0), lB(a, tid, row0, col0);
+    PairLoaderOC<C::BR, FULL> lA(a, tid, row0, col0);
     uint16_t* dst0 = tid >= C::BR ? sQ[0] : sP[0];
     uint16_t* dst1 = tid >= C::BR ? sQ[1] : sP[1];
     lA.load(k_at(0), kend);
-    lB.load(k_at(1), kend);
     lA.store(dst0);
-    lA.load(k_at(2), kend);
+    lA.load(k_at(1), kend);
     __syncthreads();
     for (int kt = 0; kt < nk2; kt += 2) {
       __builtin_amdgcn_sched_barrier(0);
-      lB.store(dst1);
-      lB.load(k_at(kt + 3), kend);
+      lA.store(dst1);
+      lA.load(k_at(kt + 2), kend);
       __builtin_amdgcn_sched_barrier(0);
       gemm_stage<T, C, EPI == EPI_WGRAD>(sP[0], sQ[0], wr, wc, half, l32, acc, do_db, tid, dbsum);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
       lA.store(dst0);
-      lA.load(k_at(kt + 4), kend);
+      lA.load(k_at(kt + 3), kend);
       __builtin_amdgcn_sched_barrier(0);
       gemm_stage<T, C, EPI == EPI_WGRAD>(sP[1], sQ[1], wr, wc, half, l32, acc, do_db, tid, dbsum);
       __syncthreads();
