@@ -12,10 +12,10 @@
 //     multi-hot bags), in batches of SUB.  A group issues a batch's gradient-row loads, and
 //     the table-row loads of the runs that end in it, before any store; it sums its lookups
 //     in order (fp32), one "piece" per run, and updates the rows of the runs that lie inside
-//     its CH lookups.  A piece that
-//     continues into the next group's lookups goes to an LDS slot.  After one barrier the
-//     group where such a run ends adds the earlier groups' slots in group order, then its
-//     own piece, and updates the row.  Only runs that cross an edge of the workgroup's range
+//     its CH lookups.  A piece that continues into the next group's lookups goes to an LDS
+//     slot.  After one barrier the group where such a run ends adds the earlier groups'
+//     slots in group order, then its own piece, and updates the row.  Only runs that cross
+//     an edge of the workgroup's range
 //     leave an fp32 partial row in HBM: the run coming in from the previous range (its
 //     pieces in this range: the range's "head"; the whole range if one run covers it) and
 //     the run going out to the next range (the range's "tail").
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
   for (int i = tid; i < RANGE; i += 256) {
     const bool ok = i < nloc;
     skey[1 + i] = ok ? ld_stream(keys + p0 + i) : NONE;
-    // bag g = t * B + b -> its row of demb, b * F + t (< F * B < 2^31), once per lookup here
+    // bag t * B + b -> its row of demb, b * F + t (< F * B < 2^31), once per lookup here
     // rather than in each lane that loads the row
-    const uint32_t g = ok ? ld_stream(vals + p0 + i) : 0u;
-    const uint32_t t = g / static_cast<uint32_t>(B);
-    sval[i] = (g - t * static_cast<uint32_t>(B)) * static_cast<uint32_t>(F) + t;
+    const uint32_t bag = ok ? ld_stream(vals + p0 + i) : 0u;
+    const uint32_t t = bag / static_cast<uint32_t>(B);
+    sval[i] = (bag - t * static_cast<uint32_t>(B)) * static_cast<uint32_t>(F) + t;
   }
   if (tid == 0) skey[0] = p0 > 0 ? keys[p0 - 1] : NONE;
   if (tid == 1) skey[RANGE + 1] = p0 + RANGE < n ? keys[p0 + RANGE] : NONE;
@@ -201,16 +201,16 @@ __global__ __launch_bounds__(256) void k_seg_reduce(
     float acc[EPL];
 #pragma unroll
     for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
-    // the group's lookups in halves of SUB (fewer rows held in registers at once); the
-    // running piece carries over from one half to the next
+    // the group's lookups in batches of SUB (fewer rows held in registers at once); the
+    // running piece carries over from one batch to the next
 #pragma unroll 1
     for (int qb = 0; qb < cnt; qb += SUB) {
-      const int hc = cnt - qb < SUB ? cnt - qb : SUB;  // lookups of this half
+      const int hc = cnt - qb < SUB ? cnt - qb : SUB;  // lookups of this batch
       uint32_t kq[SUB + 1];
 #pragma unroll
       for (int q = 0; q <= SUB; ++q) kq[q] = skey[1 + c0 + qb + (q < hc ? q : hc)];  // kq[hc..]: key after
 
-      // (1) every load of the half: its gradient rows (positions past the end re-read the
+      // (1) every load of the batch: its gradient rows (positions past the end re-read the
       //     last one), and the table rows of the runs that end here and began inside the
       //     range (a run that began before the range is finished by the fix-up)
       Raw<GT, EPL> gr[SUB];
