@@ -394,13 +394,14 @@ el_status reduce_t(const el_tables& tab, const el_bags& bags, const GradWorkspac
   // flight: 16 per group, 8 at once (update 147-185 us, against 151-190 with 2 or 4 at once,
   // 157-183 with 16, and 153-190 with 32 per group).  A multi-hot bag's rows come back from
   // L2 and the table rows' latency is what remains, so more resident wavefronts with fewer
-  // loads each win, and longer ranges leave fewer partials: 32 per group, 2 at once for
-  // 16-bit tables (752 us against 923 with 16 and 8) and 4 for fp32 (1071 against 1227).
+  // loads each win, and longer ranges leave fewer partials: 32 per group, 1 at once for
+  // 16-bit tables (730 us against 757 with 2 and 923 with 8 of 16) and 4 for fp32 (1076
+  // against 1160 with 2 and 1227 with 8 of 16).
   int64_t nr = 0, range = 0;
   auto reduce = [&](auto gnt) {
     constexpr bool GNT = decltype(gnt)::value;
     constexpr int CH = GNT ? kChunk : 2 * kChunk;
-    constexpr int SUB = GNT ? 8 : (sizeof(typename WT::S) == 2 ? 2 : 4);
+    constexpr int SUB = GNT ? 8 : (sizeof(typename WT::S) == 2 ? 1 : 4);
     constexpr int RANGE = (256 / L) * CH;
     static_assert(RANGE >= kMinRange, "the workspace holds partials for ranges of >= kMinRange lookups");
     range = RANGE;
