@@ -281,9 +281,11 @@ def main():
                     help="time emb_bag_fwd + dot_interact_fwd instead of emb_dot_fwd (which, for "
                          "forward-only workloads, does not store the pooled vectors at all, and in "
                          "training runs the two kernels on cache-sized chunks of samples)")
-    ap.add_argument("--overlap-sort", choices=["auto", "none", "fwd", "bwd"], default="auto",
+    ap.add_argument("--overlap-sort", choices=["auto", "none", "fwd", "bwd", "next"], default="auto",
                     help="run the gradient sort (emb_grad_prepare) on a side stream, from the start of "
                          "the step (fwd) or from the end of the forward (bwd), then emb_grad_apply; "
+                         "next: the sort of the next batch (it needs only that batch's indices) "
+                         "starts beside this step's update, into the other of two workspaces; "
                          "auto: from the start when the sort's passes move more bytes than the "
                          "interaction backward, else from the end of the forward")
     ap.add_argument("--recompute-emb", action="store_true",
@@ -341,7 +343,14 @@ def main():
 
     if args.overlap_sort == "auto":
         args.overlap_sort = sort_start(wl, batches[0][3].numel()) if wl.backward else "none"
+    if args.overlap_sort == "next" and args.graph:
+        sys.exit("--overlap-sort next leaves the next batch's sort running past the step, which a "
+                 "graph of one step cannot hold")
     overlap = wl.backward and args.overlap_sort != "none"
+    nxt = overlap and args.overlap_sort == "next"
+    # next: two workspaces, batch i's in wss[i % 2] (the sort of batch i + 1 writes the other
+    # one while the update of batch i reads this one)
+    wss = ([ws, torch.empty_like(ws)] if nxt else [ws, ws]) if wl.backward else None
     fused_fwd = not args.separate_fwd
     # training: store the pooled vectors and read them back (the faster order here), or
     # with --recompute-emb rebuild them in the backward where the fused backward covers
@@ -360,21 +369,22 @@ def main():
         names = fwd_names + [bwd_name, "emb_grad_reduce_update"]
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else None  # default priority
-    prepared = torch.cuda.Event()
+    prepared = [torch.cuda.Event(), torch.cuda.Event()]  # sort of batch i done: prepared[i % 2]
     fwd_done = torch.cuda.Event()
     fork = torch.cuda.Event()
 
-    def start_sort(bags, side_ev):
-        # the workspace is free once the previous update is done: from the start of the step,
-        # fork from the step's stream (the update ran there before); from the end of the
-        # forward, the wait for the forward already implies it
-        if args.overlap_sort == "fwd":
+    def start_sort(i, side_ev):
+        # the workspace is free once the update that last read it is done: from the start of
+        # the step, fork from the step's stream (the update ran there before); from the end of
+        # the forward, the wait for the forward already implies it; next: the fork at the end
+        # of this step's backward comes after the previous update, the other workspace's
+        if args.overlap_sort in ("fwd", "next"):
             fork.record(torch.cuda.current_stream())
             side.wait_event(fork)
         if side_ev: side_ev[0].record(side)
-        elf.emb_grad_prepare(tab, bags, ws, stream=side)
+        elf.emb_grad_prepare(tab, batches[i % len(batches)][0], wss[i % 2], stream=side)
         if side_ev: side_ev[1].record(side)
-        prepared.record(side)
+        prepared[i % 2].record(side)
 
     def step(i, ev=None, side_ev=None, wait_ev=None):
         """One pass of the path over batch i.  With overlap, the sort of the lookups (it needs
@@ -382,7 +392,7 @@ def main():
         backward run; the update waits for it."""
         bags, x0, G = batches[i % len(batches)][:3]
         if overlap and args.overlap_sort == "fwd":
-            start_sort(bags, side_ev)
+            start_sort(i, side_ev)
         if ev: ev[0].record()
         k = 1
         if fused_fwd:  # pooled vectors stored only when the backward reads them back
@@ -399,7 +409,7 @@ def main():
         if overlap and args.overlap_sort == "bwd":
             fwd_done.record(torch.cuda.current_stream())
             side.wait_event(fwd_done)
-            start_sort(bags, side_ev)
+            start_sort(i, side_ev)
         if recompute:
             elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb)
         else:
@@ -407,10 +417,12 @@ def main():
         if ev: ev[k].record()
         k += 1
         if overlap:
-            torch.cuda.current_stream().wait_event(prepared)
+            if nxt:  # the next batch's sort, beside this update and what follows it
+                start_sort(i + 1, side_ev)
+            torch.cuda.current_stream().wait_event(prepared[i % 2])
             if wait_ev is not None:  # the update's own time starts once the sort is done
                 wait_ev.record()
-            elf.emb_grad_apply(tab, bags, demb, wl.lr, ws)
+            elf.emb_grad_apply(tab, bags, demb, wl.lr, wss[i % 2])
         else:
             elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
         if ev: ev[k].record()
@@ -424,6 +436,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def prime():
+        """next: the sort of the first step's batch, before the steps (each step sorts the
+        batch after it, so a run of K steps still sorts K batches)."""
+        if nxt:
+            elf.emb_grad_prepare(tab, batches[0][0], wss[0], stream=side)
+            prepared[0].record(side)
+            torch.cuda.synchronize()
+
+    prime()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -444,6 +465,7 @@ def main():
 
     # timed region: K whole steps, no per-call events (nothing but the path in the stream)
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prime()
     torch.cuda.synchronize()
     t0.record()
     if side is not None:
@@ -453,6 +475,8 @@ def main():
             graphs[i % len(graphs)].replay()
         else:
             step(i)
+    if nxt:  # the sort of the batch after the last step is part of the K steps' work
+        main_stream.wait_event(prepared[args.steps % 2])
     t1.record()  # the last update waited for the last sort, so all work is before t1
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
@@ -463,6 +487,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     sevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     wevs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    prime()
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i], sevs[i] if overlap else None, wevs[i] if overlap else None)
