@@ -20,6 +20,8 @@
 // numbers past the end are clamped), every store count is fixed and each trip issues its
 // loads before its stores, so waiting for a load never waits for a store (loads and stores
 // share one in-order completion counter).
+#include <algorithm>
+
 #include "el_internal.hpp"
 #include "el_mfma.hpp"
 
@@ -241,7 +243,14 @@ el_status launch_t(const el_tables& tab, const el_bags& bags, uint32_t flags, co
                    void* out, int out_stride, size_t lds, hipStream_t stream) {
   auto kern = k_emb_dot_fwd<TT, IT, NU, SPL>;
   const int B = bags.batch;
-  hipLaunchKernelGGL(kern, dim3(resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64)),
+  // twice the workgroups that fit at once when each still loops over 16 samples or more:
+  // late or slow ones hand their samples to the dispatcher instead of holding up the end
+  // (fwd_core 174 -> 170 us, large_table 551 -> 496 us at B = 262144; with fewer samples
+  // per workgroup the extra ones cost more than they balance: B = 4096 16 -> 18 us, and four
+  // times the grid lost at B = 1048576, 2.29 -> 2.57 ms)
+  const int64_t resident = resident_grid(reinterpret_cast<const void*>(kern), B, lds, 64);
+  const int64_t grid = B >= 32 * resident ? 2 * resident : resident;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)),
                      dim3(64), lds, stream, static_cast<const typename TT::S*>(tab.base),
                      tab.row_offset, bags.indices, static_cast<int32_t>(bags.nnz), bags.offsets, B,
                      tab.num_tables, tab.dim, (flags & EL_FLAG_HASH_INDICES) ? 1u : 0u,
