@@ -650,7 +650,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def dlrm_bench(args, dev):
     """The whole DLRM training step on the train_step shapes: bottom MLP 13-512-256-128,
-    emb-bag + dot interaction, top MLP 479-1024-1024-512-256-1, logistic loss, backward of
+    emb-bag + dot interaction, top MLP 479-1024-1024-512-256-1 (its input zero-padded to 512
+    columns), logistic loss, backward of
     every stage, SGD (lr 0.01) on the dense parameters and the embedding rows; the sort of
     the lookups on a side stream from the start of the step.  Reports samples/s, per-stage
     HIP-event times, and each dense layer's forward / backward timed on its own (TFLOP/s vs
@@ -788,7 +789,7 @@ def dlrm_cpu_baseline(wl, W, ro, step, batch, seconds):
         for w, b in zip(bw, bb):
             hs.append(orc.linear_fwd(hs[-1], dt, w, dt, b, True, dt))
         emb = orc.emb_bag_fwd(W_h, wl.table_dtype, ro_h, si, so, nb, D, dt)
-        ts = [orc.dot_interact_fwd(hs[-1], emb, dt, dt, wl.out_stride)]
+        ts = [orc.dot_interact_fwd(hs[-1], emb, dt, dt, step.inter.shape[1])]
         for j, (w, b) in enumerate(zip(tw, tb)):
             ts.append(orc.linear_fwd(ts[-1], dt, w, dt, b, j < len(tw) - 1, dt))
         _, dz = orc.bce_logits(ts[-1], dt, lab_h[:n], dt)

@@ -13,9 +13,10 @@ Layout choices:
     by the products, fp32 gradient), so one SGD launch updates them all; weights are
     w[n][k] ([N][K] row-major), biases stay fp32;
   * the 13 dense features are zero-padded to 16 columns (and the first layer's weights get
-    zero columns), the interaction output keeps its zero-padded width (e.g. 480) as the top
-    MLP's input width: padded inputs are always zero, so the layers compute what the
-    unpadded ones would.
+    zero columns), the interaction output keeps a zero-padded width as the top MLP's input
+    width (479 -> 512: a multiple of 128 once it is 256 or wider, so that the top MLP's
+    first products have no partial reduction stage and take the GEMM's unmasked instance):
+    padded inputs are always zero, so the layers compute what the unpadded ones would.
 """
 from typing import Sequence
 
@@ -27,6 +28,13 @@ from . import synth
 
 def _pad8(n: int) -> int:
     return (n + 7) // 8 * 8
+
+
+def inter_stride(wl: synth.Workload) -> int:
+    """Row width of the interaction output as the top MLP's input: the workload's padded
+    width, rounded up to a multiple of 128 once it is 256 or wider."""
+    w = wl.out_stride
+    return (w + 127) // 128 * 128 if w >= 256 else w
 
 
 class DenseMLP:
@@ -72,18 +80,19 @@ class DLRMStep:
         self.k_pad = k_pad
         self.bottom = DenseMLP(synth.make_mlp_params(wl, "bottom", wl.bottom_mlp, k_pad, device), dt, device)
         self.top_sizes = (wl.out_width,) + tuple(top)
-        self.top = DenseMLP(synth.make_mlp_params(wl, "top", self.top_sizes, wl.out_stride, device), dt, device)
+        self.istride = inter_stride(wl)
+        self.top = DenseMLP(synth.make_mlp_params(wl, "top", self.top_sizes, self.istride, device), dt, device)
         e = lambda *s: torch.empty(s, dtype=dt, device=device)  # noqa: E731
         # forward activations (kept for the backward)
         self.h_bot = [e(B, n) for n in wl.bottom_mlp[1:]]       # ..., x0 = h_bot[-1]
         self.emb = e(B, F, D)
-        self.inter = e(B, wl.out_stride)
+        self.inter = e(B, self.istride)
         self.h_top = [e(B, n) for n in top]                      # ..., logits = h_top[-1]
         # backward buffers
-        widest = max(max(top[:-1]), max(wl.bottom_mlp[1:]), wl.out_stride)
+        widest = max(max(top[:-1]), max(wl.bottom_mlp[1:]), self.istride)
         self.gbuf = [torch.empty(B * widest, dtype=dt, device=device) for _ in range(2)]
         self.dlogit = e(B, 1)
-        self.dout = e(B, wl.out_stride)
+        self.dout = e(B, self.istride)
         self.dx0 = e(B, D)
         self.demb = e(B, F, D)
         self.loss = torch.zeros(1, dtype=torch.float32, device=device)

@@ -209,7 +209,7 @@ def test_dlrm_step_stage_by_stage_matches_oracle():
         h = step.h_bot[i]
     r_emb = orc.emb_bag_fwd(W0, wl.table_dtype, to_np(ro), to_np(idx), to_np(off), B, D, dt)
     assert_bits(step.emb, r_emb, "pooled embeddings")
-    r_out = orc.dot_interact_fwd(to_np(step.h_bot[-1]), r_emb, dt, dt, wl.out_stride)
+    r_out = orc.dot_interact_fwd(to_np(step.h_bot[-1]), r_emb, dt, dt, step.inter.shape[1])
     assert_close(step.inter, r_out, dt, "interaction")
     h = step.inter
     for i in range(len(top_w)):
@@ -265,7 +265,7 @@ def test_dlrm_step_stage_by_stage_matches_oracle():
     h = to_np(dense)
     for i in range(n_bot):
         h = orc.linear_fwd(h, dt, bot_w[i], dt, bot_b[i], True, dt)
-    out = orc.dot_interact_fwd(h, r_emb, dt, dt, wl.out_stride)
+    out = orc.dot_interact_fwd(h, r_emb, dt, dt, step.inter.shape[1])
     for i in range(len(top_w)):
         out = orc.linear_fwd(out, dt, top_w[i], dt, top_b[i], i < len(top_w) - 1, dt)
     e2e_loss, _ = orc.bce_logits(out, dt, to_np(labels), dt)
