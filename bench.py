@@ -299,6 +299,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of HIP graphs, one per index batch, each capturing one whole "
                          "step (both streams); per-call times still come from eager calls")
+    ap.add_argument("--hash-indices", action="store_true",
+                    help="pass the floor-modulo index hashing flag to every call that reads the indices "
+                         "(the generated indices are already in range, so results are unchanged; the "
+                         "line then shows what the hashing costs)")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip the HBM calibration kernels (4 GiB each) that measure the bandwidth "
                          "streaming kernels reach on this GPU")
@@ -367,6 +371,7 @@ def main():
         names = fwd_names + [bwd_name, "emb_grad_apply"]
     else:
         names = fwd_names + [bwd_name, "emb_grad_reduce_update"]
+    hx = args.hash_indices
     main_stream = torch.cuda.current_stream()
     side = torch.cuda.Stream() if overlap else None  # default priority
     prepared = [torch.cuda.Event(), torch.cuda.Event()]  # sort of batch i done: prepared[i % 2]
@@ -382,7 +387,7 @@ def main():
             fork.record(torch.cuda.current_stream())
             side.wait_event(fork)
         if side_ev: side_ev[0].record(side)
-        elf.emb_grad_prepare(tab, batches[i % len(batches)][0], wss[i % 2], stream=side)
+        elf.emb_grad_prepare(tab, batches[i % len(batches)][0], wss[i % 2], hash_indices=hx, stream=side)
         if side_ev: side_ev[1].record(side)
         prepared[i % 2].record(side)
 
@@ -396,9 +401,9 @@ def main():
         if ev: ev[0].record()
         k = 1
         if fused_fwd:  # pooled vectors stored only when the backward reads them back
-            elf.emb_dot_fwd(tab, bags, x0, out, emb if store_emb else None)
+            elf.emb_dot_fwd(tab, bags, x0, out, emb if store_emb else None, hash_indices=hx)
         else:
-            elf.emb_bag_fwd(tab, bags, emb)
+            elf.emb_bag_fwd(tab, bags, emb, hash_indices=hx)
             if ev: ev[k].record()
             k += 1
             elf.dot_interact_fwd(x0, emb, out)
@@ -411,7 +416,7 @@ def main():
             side.wait_event(fwd_done)
             start_sort(i, side_ev)
         if recompute:
-            elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb)
+            elf.emb_dot_bwd(tab, bags, x0, G, dx0, demb, hash_indices=hx)
         else:
             elf.dot_interact_bwd(x0, emb, G, dx0, demb)
         if ev: ev[k].record()
@@ -422,9 +427,9 @@ def main():
             torch.cuda.current_stream().wait_event(prepared[i % 2])
             if wait_ev is not None:  # the update's own time starts once the sort is done
                 wait_ev.record()
-            elf.emb_grad_apply(tab, bags, demb, wl.lr, wss[i % 2])
+            elf.emb_grad_apply(tab, bags, demb, wl.lr, wss[i % 2], hash_indices=hx)
         else:
-            elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws)
+            elf.emb_grad_reduce_update(tab, bags, demb, wl.lr, ws, hash_indices=hx)
         if ev: ev[k].record()
 
     if args.copy_calib_mib:
@@ -440,7 +445,7 @@ def main():
         """next: the sort of the first step's batch, before the steps (each step sorts the
         batch after it, so a run of K steps still sorts K batches)."""
         if nxt:
-            elf.emb_grad_prepare(tab, batches[0][0], wss[0], stream=side)
+            elf.emb_grad_prepare(tab, batches[0][0], wss[0], hash_indices=hx, stream=side)
             prepared[0].record(side)
             torch.cuda.synchronize()
 
@@ -508,7 +513,7 @@ def main():
         torch.cuda.synchronize()
         for i, (e0, e1) in enumerate(ea):
             e0.record()
-            elf.emb_grad_prepare(tab, batches[i % len(batches)][0], ws)
+            elf.emb_grad_prepare(tab, batches[i % len(batches)][0], ws, hash_indices=hx)
             e1.record()
             torch.cuda.synchronize()
         sort_alone = float(np.median([a.elapsed_time(b) for a, b in ea]))
@@ -609,6 +614,8 @@ def main():
                                      "counters of the distinct-row workload of the same shapes (another seed "
                                      "of the same draw)", traffic_workload=distinct_twin(wl)))
 
+    sort_where = {"fwd": "from the start of the step", "bwd": "from the end of the forward",
+                  "next": "for the next batch, beside this step's update"}.get(args.overlap_sort)
     result = {
         "metric": metric_name(wl),
         "value": round(B / (ms_per_step * 1e-3), 1),
@@ -628,9 +635,9 @@ def main():
                    "table_dtype": wl.table_dtype, "act_dtype": wl.act_dtype, "nnz": int(nnz),
                    "unique_rows": U, "parallelism": "single-gpu",
                    "launch": "HIP graph replay, one graph per step" if args.graph else "eager",
-                   "calls": " -> ".join(names) + (f" (emb_grad_prepare on a side stream from the "
-                                                  f"{'start of the step' if args.overlap_sort == 'fwd' else 'end of the forward'})"
-                                                  if overlap else "")},
+                   "calls": " -> ".join(names) + (f" (emb_grad_prepare on a side stream {sort_where})"
+                                                  if overlap else ""),
+                   "hash_indices": bool(hx)},
         "hbm_gbps_algorithmic": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "calls": calls,
         "roofline": roofline,

@@ -24,6 +24,8 @@ VARIANTS = [
     ("tiny-next", ["--workload", "tiny", "--overlap-sort", "next"]),
     ("tiny-graph", ["--workload", "tiny", "--graph"]),
     ("tiny-separate", ["--workload", "tiny", "--separate-fwd", "--overlap-sort", "none"]),
+    ("tiny-hash", ["--workload", "tiny", "--hash-indices"]),
+    ("small-tables-hash-next", ["--workload", "train_small_tables", "--hash-indices", "--overlap-sort", "next"]),
     ("small-tables", ["--workload", "train_small_tables"]),
     ("forward-only", ["--workload", "fwd_core"]),
 ]
@@ -47,6 +49,7 @@ def test_bench_variant_prints_one_result_line(args):
     assert d["roofline"]["bound"] in ("hbm", "mfma", "alu")
     for c in d.get("calls", {}).values():
         assert c["ms"] >= 0
+    assert d["config"]["hash_indices"] is ("--hash-indices" in args)
 
 
 def test_bench_refuses_graph_with_the_next_batch_sort():
