@@ -595,6 +595,13 @@ def main():
         ck, cg = ceiling_of(call, wl, calib)
         if cg:
             r.update({"ceiling": ck, "ceiling_gbps": cg, "frac_of_ceiling": round(a / cg, 4)})
+        if r["traffic"] is not None:  # the HBM rate by the counters' bytes
+            tg = r["traffic"] / (ms * 1e-3) / 1e9
+            r.update({"traffic_gbps": round(tg, 1), "traffic_frac": round(tg / HBM_PEAK_GBPS, 4)})
+        if a > HBM_PEAK_GBPS:
+            reuse = ("the algorithmic bytes count every lookup's rows, and caches serve the rows that "
+                     "lookups share, so they exceed what HBM alone could deliver in this time")
+            note = f"{note}; {reuse}" if note else reuse
         if note:
             r["note"] = note
         return r

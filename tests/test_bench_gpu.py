@@ -50,6 +50,9 @@ def test_bench_variant_prints_one_result_line(args):
     for c in d.get("calls", {}).values():
         assert c["ms"] >= 0
     assert d["config"]["hash_indices"] is ("--hash-indices" in args)
+    for r in d.get("rooflines", [d["roofline"]]):
+        assert (r["traffic"] is None) == ("traffic_gbps" not in r)
+        assert r["frac"] <= 1 or "caches serve" in r.get("note", "")
 
 
 def test_bench_refuses_graph_with_the_next_batch_sort():
