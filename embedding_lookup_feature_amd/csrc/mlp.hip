@@ -653,7 +653,9 @@ void fill_tiles(GemmArgs& a) {
 
 // Splits of the weight-gradient reduction over the batch: enough workgroups to fill every
 // CU's workgroup slots once (output tiles x splits >= 512 small or 256 large tiles), each
-// split at least 4 LDS stages long.
+// split at least 8 LDS stages long (with 4, the 256 -> 128 layer's 256 splits of 256 rows
+// spent more on partials and pipeline fill than they gained: its backward 62 -> 56 us at
+// B = 65536 with 8).
 // Large tiles once the output holds at least 8 of them (one workgroup per CU, so more
 // splits; with fewer tiles the split partials outweigh what the larger tile saves).
 WgradPlan plan_wgrad(int M, int K, int N) {
@@ -671,7 +673,7 @@ WgradPlan plan_wgrad(int M, int K, int N) {
   const int tiles = ((N + br - 1) / br) * ((K + bc - 1) / bc);
   const int target = p.large ? 256 : 512;  // workgroups: two per CU (small tiles), one (large)
   int s = std::max(1, (target + tiles - 1) / tiles);
-  const int max_s = std::max(1, M / (4 * kBK));
+  const int max_s = std::max(1, M / (8 * kBK));
   s = std::min(std::min(s, max_s), 256);
   int per = (M + s - 1) / s;
   per = (per + kBK - 1) / kBK * kBK;
