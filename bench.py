@@ -311,7 +311,7 @@ def main():
                          "with every table's lookups distinct rows, so that no row comes from cache)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import embedding_lookup_feature_amd as elf

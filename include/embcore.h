@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
   EL_OK = 0,
   EL_ERR_INVALID_ARG = 1, /* null / misaligned pointer, bad size, inconsistent shape */
-  EL_ERR_UNSUPPORTED = 2, /* valid request this build does not implement (e.g. row size) */
+  EL_ERR_UNSUPPORTED = 2, /* valid request the library does not implement (e.g. row size) */
   EL_ERR_WORKSPACE = 3,   /* workspace smaller than emb_grad_workspace_bytes() */
   EL_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } el_status;
