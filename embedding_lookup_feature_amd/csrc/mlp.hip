@@ -371,15 +371,16 @@ __global__ __launch_bounds__(256) void k_transpose16(const uint16_t* w, uint16_t
 }
 
 // Ordered sum of the split partials: out[c] = sum_s part[s][c] (c < n; VEC consecutive
-// columns per thread, n % VEC == 0).  Each workgroup covers 16 column vectors with 16
-// split groups: group g adds splits g, g+16, g+32, ... in order (loads issued 8 at a time),
-// then the 16 group sums are added in group order.  Bitwise reproducible.
+// columns per thread, n % VEC == 0), for workgroup `blk` of the array.  Each workgroup
+// covers 16 column vectors with 16 split groups: group g adds splits g, g+16, g+32, ... in
+// order (loads issued 8 at a time), then the 16 group sums are added in group order.
+// Bitwise reproducible.
 template <int VEC>
-__global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, int splits, float* out) {
+__device__ inline void split_sum_block(const float* part, long n, int splits, float* out, long blk) {
   constexpr int SG = 16, CV = 256 / SG;
   __shared__ float red[SG][CV * VEC];
   const int t = threadIdx.x, cv = t % CV, sg = t / CV;
-  const long c = (static_cast<long>(blockIdx.x) * CV + cv) * VEC;
+  const long c = (blk * CV + cv) * VEC;
   float s[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s[e] = 0.f;
@@ -424,12 +425,22 @@ __global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, in
   }
 }
 
+// The weight partials (4 columns per thread) in the first b4 workgroups, the bias partials
+// (one per thread) in the rest: one launch for both sums of a layer's gradient.
+__global__ __launch_bounds__(256) void k_split_sum(const float* part, long n, float* out, const float* dbp,
+                                                   long nb, float* db, int splits, long b4) {
+  if (blockIdx.x < b4)  // block-uniform
+    split_sum_block<4>(part, n, splits, out, blockIdx.x);
+  else
+    split_sum_block<1>(dbp, nb, splits, db, blockIdx.x - b4);
+}
+
 void launch_split_sum(const float* part, long n, int splits, float* out, const float* dbp, long nb, float* db,
                       hipStream_t st) {
   const long b4 = (n / 4 + 15) / 16;
-  hipLaunchKernelGGL(k_split_sum<4>, dim3(static_cast<unsigned>(b4)), dim3(256), 0, st, part, n, splits, out);
   const long b1 = (nb + 15) / 16;
-  hipLaunchKernelGGL(k_split_sum<1>, dim3(static_cast<unsigned>(b1)), dim3(256), 0, st, dbp, nb, splits, db);
+  hipLaunchKernelGGL(k_split_sum, dim3(static_cast<unsigned>(b4 + b1)), dim3(256), 0, st, part, n, out, dbp, nb, db,
+                     splits, b4);
 }
 
 // ---------------------------------------------------------------------------------------
