@@ -378,8 +378,10 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
       for (int m = 0; m < 2; ++m) {
         const int tt = row_table(uu, m);
         const int gbag = (tt < 0 ? 0 : tt) * B + jc;
-        bnd_s[Q][uu][m] = ld_stream(gs.off + gbag);
-        bnd_e[Q][uu][m] = ld_stream(gs.off + gbag + 1);
+        // plain loads: 32 neighbouring samples' bounds (and first indices) share a cache
+        // line that as many wavefronts read (streamed, the call took 553 instead of 409 us)
+        bnd_s[Q][uu][m] = gs.off[gbag];
+        bnd_e[Q][uu][m] = gs.off[gbag + 1];
       }
   };
   // stage B: first index of the bags whose bounds are in parity Q's registers (the bag's
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(256, (bwd_wg_per_cu<UPT, GPT, GATHER>())) void k_do
         int p = bnd_s[Q][uu][m];
         ibag_n[Q][uu][m] = bnd_e[Q][uu][m] - p;
         p = p < 0 ? 0 : (p < gs.nnz ? p : gs.nnz - 1);
-        gix[Q][uu][m] = ld_stream(gs.idx + p);
+        gix[Q][uu][m] = gs.idx[p];
       }
   };
   // joint-table row of a bag's first index (row 0 for an empty bag: read, never used)

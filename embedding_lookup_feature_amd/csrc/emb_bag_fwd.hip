@@ -9,7 +9,7 @@
 // consecutive bags in one pass and exits: the wave is cut into NG groups of L lanes
 // (L = row bytes / 16, rounded up to a power of two; a group covers one row with 16-byte
 // loads) and every group pools U bags.
-//   1. lane i < NB streams in the CSR bounds of bag i and the first row of its table
+//   1. lane i < NB loads the CSR bounds of bag i and the first row of its table
 //      (independent loads, one round trip), then the bag's first index;
 //   2. every group issues the first-row loads of its U bags back to back, so U row loads
 //      per lane are in flight (for hotness-1 bags this is the whole gather); later entries
@@ -70,13 +70,14 @@ __global__ __launch_bounds__(256) void k_emb_bag_fwd(
     t = gc / Bc;
     b = b0 + (gc - t * Bc);
     const int g = t * B + b;
-    s = ld_stream(off + g);
-    e = ld_stream(off + g + 1);
+    // plain loads: neighbouring wavefronts read the same lines of bounds and indices
+    s = off[g];
+    e = off[g + 1];
     base = row_off[t];
     if (hash) nt = static_cast<int32_t>(row_off[t + 1] - base);
   }
   if (e > s) {
-    r0 = ld_stream(idx + s);
+    r0 = idx[s];
     if (hash) r0 = floor_mod(r0, nt);
   }
 
@@ -181,8 +182,9 @@ __global__ __launch_bounds__(256) void k_emb_bag_long(
     t = static_cast<int>(gc / Bc);
     b = b0 + static_cast<int>(gc - static_cast<int64_t>(t) * Bc);
     const int64_t g = static_cast<int64_t>(t) * B + b;
-    s = ld_stream(off + g);
-    e = ld_stream(off + g + 1);
+    // plain loads: neighbouring wavefronts read the same lines of bounds and indices
+    s = off[g];
+    e = off[g + 1];
     base = row_off[t];
     if (hash) nt = static_cast<int32_t>(row_off[t + 1] - base);
   }
@@ -194,13 +196,13 @@ __global__ __launch_bounds__(256) void k_emb_bag_long(
   const int src0 = grp * L;  // the group's first lane
   int ri = 0;
   if (s + (gl & (R - 1)) < e) {  // (a table without rows has only empty bags)
-    ri = ld_stream(idx + s + (gl & (R - 1)));
+    ri = idx[s + (gl & (R - 1))];
     if (hash) ri = floor_mod(ri, nt);
   }
   for (int k = s; k < e; k += R) {  // group-uniform trip count
     // the next round's indices, in flight with this round's rows
     const int kn = k + R + (gl & (R - 1));
-    int rn = kn < e ? ld_stream(idx + kn) : 0;
+    int rn = kn < e ? idx[kn] : 0;
     uint4 w[R][NVL];
 #pragma unroll
     for (int q = 0; q < R; ++q) {
