@@ -268,6 +268,7 @@ el_status with_type(el_dtype d, F&& f) {
     case EL_F32: return f(F32T{});
     case EL_F16: return f(F16T{});
     case EL_BF16: return f(BF16T{});
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "unknown dtype");
 }

@@ -295,6 +295,7 @@ el_status dispatch_out(const el_tables& tab, const el_bags& bags, uint32_t flags
     case EL_F32: return dispatch_shape<TT, F32T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
     case EL_F16: return dispatch_shape<TT, F16T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
     case EL_BF16: return dispatch_shape<TT, BF16T>(tab, bags, flags, out, ostride, ocol, b0, Bc, stream);
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown output dtype");
 }
@@ -310,6 +311,7 @@ el_status launch_emb_bag_fwd(const el_tables& tab, const el_bags& bags, uint32_t
     case EL_F32: return dispatch_out<F32T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
     case EL_F16: return dispatch_out<F16T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
     case EL_BF16: return dispatch_out<BF16T>(tab, bags, flags, out, out_dtype, ostride, ocol, b0, Bc, stream);
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_bag_fwd: unknown table dtype");
 }

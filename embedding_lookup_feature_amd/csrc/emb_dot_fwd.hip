@@ -336,6 +336,7 @@ el_status launch_emb_dot_fwd(const el_tables& tab, const el_bags& bags, uint32_t
     case EL_F32: return launch_act<F32T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
     case EL_F16: return launch_act<F16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
     case EL_BF16: return launch_act<BF16T>(tab, bags, flags, x0, act_dtype, out, out_stride, lds, stream);
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "emb_dot_fwd: unknown table dtype");
 }

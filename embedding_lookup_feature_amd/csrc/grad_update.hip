@@ -484,6 +484,7 @@ el_status reduce_w(const el_tables& tab, const el_bags& bags, const GradWorkspac
     case EL_F32: return reduce_typed<GT, F32T>(tab, bags, ws, keys, vals, demb, lr, stream);
     case EL_F16: return reduce_typed<GT, F16T>(tab, bags, ws, keys, vals, demb, lr, stream);
     case EL_BF16: return reduce_typed<GT, BF16T>(tab, bags, ws, keys, vals, demb, lr, stream);
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "unknown table dtype");
 }
@@ -497,6 +498,7 @@ el_status launch_reduce_update(const el_tables& tab, const el_bags& bags, const 
     case EL_F32: return reduce_w<F32T>(tab, bags, ws, sorted_keys, sorted_vals, demb, lr, stream);
     case EL_F16: return reduce_w<F16T>(tab, bags, ws, sorted_keys, sorted_vals, demb, lr, stream);
     case EL_BF16: return reduce_w<BF16T>(tab, bags, ws, sorted_keys, sorted_vals, demb, lr, stream);
+    default: break;
   }
   return set_error(EL_ERR_INVALID_ARG, "unknown gradient dtype");
 }

@@ -673,23 +673,25 @@ WgradPlan plan_wgrad(int M, int K, int N) {
   WgradPlan p;
   if (M <= 0) return p;
   if (N == 1) {
-    const int per = std::max(256, (M + 1023) / 1024);
-    p.splits = (M + per - 1) / per;
-    p.per = per;
-    p.bytes = static_cast<size_t>(p.splits) * (K + 1) * sizeof(float);
+    const int64_t per = std::max<int64_t>(256, (static_cast<int64_t>(M) + 1023) / 1024);
+    p.splits = static_cast<int>((M + per - 1) / per);
+    p.per = static_cast<int>(per);
+    p.bytes = static_cast<size_t>(p.splits) * (static_cast<size_t>(K) + 1) * sizeof(float);
     return p;
   }
-  p.large = static_cast<long>((N + CfgL::BR - 1) / CfgL::BR) * ((K + CfgL::BC - 1) / CfgL::BC) >= 8;
-  const int br = p.large ? CfgL::BR : CfgS::BR, bc = p.large ? CfgL::BC : CfgS::BC;
-  const int tiles = ((N + br - 1) / br) * ((K + bc - 1) / bc);
-  const int target = p.large ? 256 : 512;  // workgroups: two per CU (small tiles), one (large)
-  int s = std::max(1, (target + tiles - 1) / tiles);
-  const int max_s = std::max(1, M / (8 * kBK));
-  s = std::min(std::min(s, max_s), 256);
-  int per = (M + s - 1) / s;
-  per = (per + kBK - 1) / kBK * kBK;
-  p.splits = (M + per - 1) / per;
-  p.per = per;
+  // 64-bit arithmetic: the sizes may be anything up to 2^31 - 1 here
+  const int64_t M64 = M, N64 = N, K64 = K;
+  p.large = ((N64 + CfgL::BR - 1) / CfgL::BR) * ((K64 + CfgL::BC - 1) / CfgL::BC) >= 8;
+  const int64_t br = p.large ? CfgL::BR : CfgS::BR, bc = p.large ? CfgL::BC : CfgS::BC;
+  const int64_t tiles = ((N64 + br - 1) / br) * ((K64 + bc - 1) / bc);
+  const int64_t target = p.large ? 256 : 512;  // workgroups: two per CU (small tiles), one (large)
+  int64_t s = std::max<int64_t>(1, (target + tiles - 1) / tiles);
+  const int64_t max_s = std::max<int64_t>(1, M64 / (8 * kBK));
+  s = std::min<int64_t>(std::min(s, max_s), 256);
+  int64_t per = (M64 + s - 1) / s;
+  per = std::min<int64_t>((per + kBK - 1) / kBK * kBK, INT32_MAX / kBK * kBK);
+  p.splits = static_cast<int>((M64 + per - 1) / per);
+  p.per = static_cast<int>(per);
   p.wt_bytes = (static_cast<size_t>(N) * K * 2 + 255) / 256 * 256;
   p.bytes = p.wt_bytes +
             (p.splits > 1 ? static_cast<size_t>(p.splits) * (static_cast<size_t>(N) * K + N) * sizeof(float) : 0);
@@ -895,7 +897,7 @@ EL_API el_status el_relu_bwd(const void* dy, const void* y, void* dz, int32_t M,
 
 EL_API size_t el_bce_workspace_bytes(int32_t M) {
   if (M < 1) return 0;
-  return static_cast<size_t>((M + kBceBlock - 1) / kBceBlock) * sizeof(double);
+  return static_cast<size_t>((static_cast<int64_t>(M) + kBceBlock - 1) / kBceBlock) * sizeof(double);
 }
 
 EL_API el_status el_bce_logits(const void* z, int32_t ldz, const float* labels, int32_t M,

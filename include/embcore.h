@@ -49,7 +49,16 @@ typedef enum {
   EL_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 } el_status;
 
-typedef enum { EL_F32 = 0, EL_F16 = 1, EL_BF16 = 2 } el_dtype;
+typedef enum {
+  EL_F32 = 0,
+  EL_F16 = 1,
+  EL_BF16 = 2,
+  /* Not dtypes.  With these two bounds every int32 is a value of the type, so an unknown
+   * code that a caller passes (from C, Python, ...) reaches the checks, which refuse it,
+   * instead of being an out-of-range enum value in the library's C++. */
+  EL_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  EL_DTYPE_RANGE_MAX_ = 2147483647
+} el_dtype;
 
 /* --hash_indices (page "DLRM For PyTorch", §Command-line options): replace every index by
  * index mod table size, with the floor-modulo sign convention (a negative index maps into
